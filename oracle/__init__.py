@@ -1,0 +1,11 @@
+"""fp64 CPU oracle of the sink-routed decode path (test infrastructure only).
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg import this
+package; the HIP library never does.  Parity-pinned functions are listed in
+``sinkrouter``'s module docstring; none is unpinned.
+"""
+from .sinkrouter import (  # noqa: F401
+    attend_group, cosine, default_scale, dense_decode, group_mask, merge_partials,
+    record_sink, route, route_scores, routed_decode, routed_decode_items,
+    split_k_decode, split_partials, work_list,
+)

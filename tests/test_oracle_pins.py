@@ -1,0 +1,344 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+Each test names the pin it checks: brute force on tiny inputs, a library
+routine (torch's scaled_dot_product_attention in fp64, scipy's cosine
+distance, Python's stable sort), closed forms (T = 1, q = 0, the fixed-point
+bound of Eq. (1)), invariants (split count, permutation of positions 1..T-1,
+GQA = repeated-KV MHA) and hand-built routing cases with closed-form cosines
+(tests/golden/route_cases.json).  The last block plants plausible mistakes in
+copies of the oracle and checks that some pin catches each one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import sinkrouter as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_layer(seed, B, Hq, Hkv, T, d, k0_norm=None):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, d))
+    k = rng.standard_normal((B, Hkv, T, d))
+    v = rng.standard_normal((B, Hkv, T, d))
+    if k0_norm is not None:
+        k[:, :, 0] *= k0_norm / np.linalg.norm(k[:, :, 0], axis=-1, keepdims=True)
+    return q, k, v
+
+
+# --- p1: brute force ---------------------------------------------------------
+def brute_force(q, k, v, scale):
+    """Triple loop with math.exp and math.fsum, one head at a time."""
+    B, Hq, d = q.shape
+    Hkv, T = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, d))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            z = [scale * math.fsum(q[b, h, i] * k[b, g, t, i] for i in range(d)) for t in range(T)]
+            zm = max(z)
+            w = [math.exp(x - zm) for x in z]
+            den = math.fsum(w)
+            for i in range(d):
+                out[b, h, i] = math.fsum(w[t] * v[b, g, t, i] for t in range(T)) / den
+    return out
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,d", [(1, 2, 2, 1, 4), (2, 4, 2, 17, 8), (1, 8, 2, 64, 8),
+                                          (1, 4, 1, 33, 5)])
+def test_p1_dense_equals_brute_force(B, Hq, Hkv, T, d):
+    q, k, v = rand_layer(1 + T, B, Hq, Hkv, T, d)
+    s = 0.37
+    np.testing.assert_allclose(oracle.dense_decode(q, k, v, s), brute_force(q, k, v, s),
+                               rtol=0, atol=1e-12)
+
+
+# --- p2: library routine -----------------------------------------------------
+@pytest.mark.parametrize("B,Hq,Hkv,T,d", [(2, 8, 2, 300, 64), (1, 32, 8, 129, 128), (3, 4, 4, 50, 16)])
+def test_p2_dense_equals_torch_sdpa_fp64(B, Hq, Hkv, T, d):
+    q, k, v = rand_layer(7 + d, B, Hq, Hkv, T, d, k0_norm=30.0)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, :, None, :], torch.from_numpy(k), torch.from_numpy(v),
+        enable_gqa=True).squeeze(2).numpy()
+    np.testing.assert_allclose(oracle.dense_decode(q, k, v), ref, rtol=0, atol=1e-12)
+
+
+# --- p3: GQA equals MHA with repeated KV heads ------------------------------
+def test_p3_gqa_equals_repeated_kv_mha():
+    q, k, v = rand_layer(3, 2, 8, 2, 77, 16)
+    G = 4
+    k_rep = np.repeat(k, G, axis=1)
+    v_rep = np.repeat(v, G, axis=1)
+    np.testing.assert_allclose(oracle.dense_decode(q, k, v),
+                               oracle.dense_decode(q, k_rep, v_rep), rtol=0, atol=1e-14)
+
+
+# --- p4: routed sink rows are v0 exactly ------------------------------------
+def test_p4_sink_rows_are_v0_bit_exact():
+    q, k, v = rand_layer(4, 2, 8, 4, 40, 16)
+    k0, v0 = oracle.record_sink(k, v)
+    mask = np.array([[1, 0, 1, 0], [0, 1, 1, 1]], dtype=np.uint8)
+    out = oracle.routed_decode(q, k, v, v0, mask)
+    dense = oracle.dense_decode(q, k, v)
+    for b in range(2):
+        for g in range(4):
+            rows = out[b, 2 * g:2 * g + 2]
+            if mask[b, g]:
+                assert np.array_equal(rows, np.stack([v[b, g, 0]] * 2))
+            else:
+                assert np.array_equal(rows, dense[b, 2 * g:2 * g + 2])
+
+
+# --- p5: fixed point of Eq. (1) ---------------------------------------------
+def test_p5_fixed_point_bound():
+    d, T = 64, 4096
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((1, 1, T, d))
+    v = rng.standard_normal((1, 1, T, d))
+    k[0, 0, 0] *= 400.0 / np.linalg.norm(k[0, 0, 0])
+    q = (k[0, 0, 0] / np.linalg.norm(k[0, 0, 0]))[None, None, :]
+    out = oracle.dense_decode(q, k, v)[0, 0]
+    z = (k[0, 0] @ q[0, 0]) / 8.0
+    delta = z[0] - z[1:].max()
+    assert delta > 45.0
+    spread = np.abs(v[0, 0, 1:] - v[0, 0, 0]).max()
+    bound = (T - 1) * math.exp(-delta) * spread
+    err = np.abs(out - v[0, 0, 0]).max()
+    assert err <= bound + 1e-15
+    # general form: |u - v0| <= (1 - alpha_0) max_t |v_t - v0|
+    w = np.exp(z - z.max())
+    alpha0 = w[0] / w.sum()
+    assert err <= (1 - alpha0) * spread * (1 + 1e-9) + 1e-15
+
+
+def test_p5_general_bound_moderate_dominance():
+    d, T = 16, 500
+    rng = np.random.default_rng(55)
+    k = rng.standard_normal((1, 1, T, d))
+    v = rng.standard_normal((1, 1, T, d))
+    k[0, 0, 0] *= 12.0 / np.linalg.norm(k[0, 0, 0])
+    q = (k[0, 0, 0] / np.linalg.norm(k[0, 0, 0]))[None, None, :] * 2.0
+    out = oracle.dense_decode(q, k, v)[0, 0]
+    z = (k[0, 0] @ q[0, 0]) / 4.0
+    w = np.exp(z - z.max())
+    alpha0 = w[0] / w.sum()
+    assert 0.0 < alpha0 < 1.0
+    dev = v[0, 0, 1:] - v[0, 0, 0]
+    lhs = np.linalg.norm(out - v[0, 0, 0])
+    assert lhs <= (1 - alpha0) * np.linalg.norm(dev, axis=1).max() * (1 + 1e-12)
+
+
+# --- p6: T = 1 ----------------------------------------------------------------
+def test_p6_single_position_returns_v0_exactly():
+    q, k, v = rand_layer(6, 2, 6, 3, 1, 32)
+    out = oracle.dense_decode(q, k, v)
+    assert np.array_equal(out, np.repeat(v[:, :, 0], 2, axis=1))
+
+
+# --- p7: q = 0 ----------------------------------------------------------------
+def test_p7_zero_query_is_uniform_average_and_active():
+    q, k, v = rand_layer(7, 1, 4, 2, 123, 16)
+    q[:] = 0.0
+    out = oracle.dense_decode(q, k, v)
+    np.testing.assert_allclose(out, np.repeat(v.mean(axis=2), 2, axis=1), rtol=0, atol=1e-14)
+    scores, mask, wl, n_active = oracle.route(q, k[:, :, 0], 0.5)
+    assert np.array_equal(scores, np.zeros_like(scores))
+    assert mask.sum() == 0 and n_active == 2
+
+
+# --- p8: split-K invariance ---------------------------------------------------
+@pytest.mark.parametrize("S", [1, 2, 3, 7, 64, 100, 105])
+def test_p8_split_count_invariance(S):
+    q, k, v = rand_layer(8, 1, 8, 2, 100, 16, k0_norm=30.0)
+    ref = oracle.dense_decode(q, k, v)
+    got = oracle.split_k_decode(q, k, v, S)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_p8_per_token_partials_are_exact_softmax_terms():
+    # S = T: each split holds one position, so m = z_t, l = 1, acc = v_t
+    q, k, v = rand_layer(88, 1, 2, 1, 9, 4)
+    parts = oracle.split_partials(q[0], k[0, 0], v[0, 0], 0.5, 9)
+    for t, (m, l, acc) in enumerate(parts):
+        np.testing.assert_allclose(m, 0.5 * (q[0] @ k[0, 0, t]), rtol=0, atol=1e-15)
+        assert np.array_equal(l, np.ones(2))
+        assert np.array_equal(acc, np.stack([v[0, 0, t]] * 2))
+
+
+# --- p9: permutation invariance ----------------------------------------------
+def test_p9_permuting_positions_after_0():
+    q, k, v = rand_layer(9, 2, 8, 2, 200, 32, k0_norm=30.0)
+    perm = np.concatenate([[0], 1 + np.random.default_rng(0).permutation(199)])
+    np.testing.assert_allclose(oracle.dense_decode(q, k[:, :, perm], v[:, :, perm]),
+                               oracle.dense_decode(q, k, v), rtol=0, atol=1e-13)
+    r1 = oracle.route(q, k[:, :, 0], 0.5)
+    r2 = oracle.route(q, k[:, :, perm][:, :, 0], 0.5)
+    assert np.array_equal(r1[1], r2[1])
+
+
+# --- p10: cosine closed forms and a library routine --------------------------
+def test_p10_cosine_identities():
+    import scipy.spatial.distance as ssd
+    rng = np.random.default_rng(10)
+    for _ in range(20):
+        a, b = rng.standard_normal(64), rng.standard_normal(64)
+        c = oracle.cosine(a, b)
+        assert abs(c - (1.0 - ssd.cosine(a, b))) < 1e-14
+        assert abs(oracle.cosine(3.5 * a, 0.25 * b) - c) < 1e-14
+        assert abs(oracle.cosine(a, a) - 1.0) < 1e-15
+        assert abs(oracle.cosine(-a, a) + 1.0) < 1e-15
+    assert oracle.cosine(np.zeros(8), np.ones(8)) == 0.0
+    e = np.eye(4)
+    assert oracle.cosine(e[0], e[1]) == 0.0
+
+
+def test_p10_route_scores_per_head_group_map():
+    # head h of a group of G reads k0 of group h // G
+    rng = np.random.default_rng(11)
+    k0 = rng.standard_normal((2, 3, 16))
+    q = np.zeros((2, 6, 16))
+    for b in range(2):
+        for h in range(6):
+            q[b, h] = k0[b, h // 2] * (h + 1)
+    scores = oracle.route_scores(q, k0)
+    np.testing.assert_allclose(scores, np.ones((2, 6)), rtol=0, atol=1e-14)
+
+
+# --- routing golden cases (closed-form cosines) ------------------------------
+def _golden_cases():
+    with open(os.path.join(GOLDEN, "route_cases.json")) as f:
+        return json.load(f)["cases"]
+
+
+def build_golden(case):
+    B, Hq, Hkv, d = case["batch"], case["num_q_heads"], case["num_kv_heads"], case["head_dim"]
+    k0 = np.zeros((B, Hkv, d))
+    q = np.zeros((B, Hq, d))
+    for b in range(B):
+        for g in range(Hkv):
+            k0[b, g, 0] = case["k0_scale"][b][g]
+        for h in range(Hq):
+            a, c = case["q_ab"][b][h]
+            q[b, h, 0], q[b, h, 1] = a, c
+    return q, k0
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_route_golden_cases(case):
+    q, k0 = build_golden(case)
+    scores, mask, wl, n_active = oracle.route(q, k0, case["tau"])
+    np.testing.assert_allclose(scores, np.array(case["expect_scores"]), rtol=0, atol=1e-15)
+    assert mask.tolist() == case["expect_mask"]
+    assert wl.tolist() == case["expect_work_list"]
+    assert n_active == case["expect_n_active"]
+
+
+def test_work_list_is_python_stable_sort_by_sink_flag():
+    rng = np.random.default_rng(12)
+    for _ in range(50):
+        mask = (rng.random((3, 8)) < rng.random()).astype(np.uint8)
+        wl, n_active = oracle.work_list(mask)
+        flat = mask.reshape(-1).tolist()
+        assert wl.tolist() == sorted(range(len(flat)), key=lambda j: flat[j])
+        assert n_active == flat.count(0)
+
+
+def test_record_sink_takes_position_zero():
+    q, k, v = rand_layer(13, 2, 4, 2, 10, 8)
+    k0, v0 = oracle.record_sink(k, v)
+    assert np.array_equal(k0, k[:, :, 0]) and np.array_equal(v0, v[:, :, 0])
+
+
+def test_rope_at_position_zero_is_identity():
+    # The recorded key is the same before and after rotary embedding: every
+    # rotation angle at position 0 is 0 (reading of the README's pre/post-RoPE
+    # wording; the routing score does not depend on which one is kept).
+    d = 128
+    x = np.random.default_rng(14).standard_normal(d)
+    inv_freq = 500000.0 ** (-np.arange(0, d, 2) / d)
+    ang = 0 * inv_freq
+    cos, sin = np.cos(np.concatenate([ang, ang])), np.sin(np.concatenate([ang, ang]))
+    rot = np.concatenate([-x[d // 2:], x[:d // 2]])
+    assert np.array_equal(x * cos + rot * sin, x)
+
+
+# --- planted mistakes: each one must trip a pin -----------------------------
+def _mut_wrong_group_map(q, k, v, scale):
+    B, Hq, d = q.shape
+    Hkv = k.shape[1]
+    out = np.zeros((B, Hq, d))
+    for b in range(B):
+        for h in range(Hq):
+            g = h % Hkv  # wrong: interleaved head->group map
+            out[b, h] = orc.attend_group(q[b, h:h + 1], k[b, g], v[b, g], scale)[0]
+    return out
+
+
+def _mut_no_scale(q, k, v, scale):
+    return oracle.dense_decode(q, k, v, 1.0)
+
+
+def _mut_transposed(q, k, v, scale):
+    return oracle.dense_decode(q, v, k, scale)  # K and V swapped
+
+
+def _mut_skip_position0(q, k, v, scale):
+    return oracle.dense_decode(q, k[:, :, 1:], v[:, :, 1:], scale)
+
+
+def _mut_no_normalise(q, k, v, scale):
+    out = np.zeros(q.shape)
+    B, Hq, d = q.shape
+    G = Hq // k.shape[1]
+    for b in range(B):
+        for h in range(Hq):
+            z = scale * (k[b, h // G] @ q[b, h])
+            out[b, h] = np.exp(z - z.max()) @ v[b, h // G]
+    return out
+
+
+@pytest.mark.parametrize("mutant", [_mut_wrong_group_map, _mut_no_scale, _mut_transposed,
+                                    _mut_skip_position0, _mut_no_normalise])
+def test_planted_attention_mistakes_fail_sdpa_pin(mutant):
+    q, k, v = rand_layer(21, 1, 8, 2, 60, 16, k0_norm=30.0)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, :, None, :], torch.from_numpy(k), torch.from_numpy(v),
+        enable_gqa=True).squeeze(2).numpy()
+    assert np.abs(mutant(q, k, v, 0.25) - ref).max() > 1e-6
+
+
+def test_planted_routing_mistakes_fail_golden():
+    cases = _golden_cases()
+
+    def any_rule(scores, Hkv, tau):  # "any head" instead of "every head"
+        B, Hq = scores.shape
+        G = Hq // Hkv
+        return np.array([[int(any(scores[b, g * G + i] >= tau for i in range(G)))
+                          for g in range(Hkv)] for b in range(B)], dtype=np.uint8)
+
+    caught = {"any": False, "unstable": False}
+    for case in cases:
+        q, k0 = build_golden(case)
+        sc = oracle.route_scores(q, k0)
+        if any_rule(sc, k0.shape[1], case["tau"]).tolist() != case["expect_mask"]:
+            caught["any"] = True
+        mask = np.array(case["expect_mask"], dtype=np.uint8)
+        reversed_sinks = [j for j in range(mask.size) if not mask.flat[j]] + \
+            [j for j in reversed(range(mask.size)) if mask.flat[j]]
+        if reversed_sinks != case["expect_work_list"]:
+            caught["unstable"] = True
+    assert all(caught.values()), caught
+
+
+def test_threshold_tie_counts_as_sink():
+    # Reading: "cosine >= tau" (ties route to the sink side).  Generated
+    # layers keep every score at least 0.05 away from tau, so ties never occur.
+    assert orc.group_mask(np.array([[0.5, 0.5]]), 1, 0.5).tolist() == [[1]]
+    assert orc.group_mask(np.array([[0.5, np.nextafter(0.5, 0.0)]]), 1, 0.5).tolist() == [[0]]
