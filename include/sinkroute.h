@@ -1,0 +1,176 @@
+/*
+ * libsinkroute: sink-aware routed GQA decode attention for MI355X (gfx950).
+ *
+ * One decode step of one attention layer, single query token per sequence:
+ *
+ *   sr_record_sink   prefill side: keep the key and value at position 0.
+ *   sr_route         score every query head against the position-0 key,
+ *                    decide per KV group (sink / active) and emit a compacted
+ *                    work list, all on the device.
+ *   sr_decode_attn   sink groups write the position-0 value; active groups run
+ *                    split-K flash-decode with an fp32 online softmax, merged
+ *                    in-kernel by the last workgroup to finish an item.
+ *   sr_dense_decode  the same kernel with routing off (every group active).
+ *
+ * The method is SinkRouter as described by its GitHub README
+ * (github.com/streamer-AP/SinkRouter, the list of decode-time steps and the
+ * routing-controls section) and by the pith.science rendering of the paper
+ * (arXiv 2604.16883: Eq. (1) in the Figure 1 caption, the Figure 4 workflow,
+ * the Figure 10 KV-group cosine proxy).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  B  batch, Hq query heads, Hkv KV heads, G = Hq / Hkv, d head dim,
+ *  T  cached positions 0..T-1 (all of them are attended; the caller has
+ *     already appended the current token's key and value).
+ *  Item j = b * Hkv + g is one (sequence, KV group) pair; query head h belongs
+ *  to group h / G (Hugging Face repeat_kv layout).
+ *
+ *  Caches k_cache / v_cache: element (b, g, t, i) lives at
+ *     base + b*stride_b + g*stride_h + t*stride_t + i        (in elements)
+ *  so d is contiguous and T_max >= T is allowed.  Element type is bf16 or
+ *  fp32 (kv_dtype).  Every row start must be 16-byte aligned.
+ *  q, out: fp32 [B][Hq][d] contiguous.  k0, v0: fp32 [B][Hkv][d] contiguous.
+ *
+ *  Pointers: every data pointer is a device pointer owned by the caller; the
+ *  library never allocates, frees or keeps them.  `stream` is a hipStream_t
+ *  (NULL = the default stream).  Calls only enqueue work: none of them waits
+ *  for the device, so results are ready once the stream is synchronised.
+ *  The only state the library keeps is the CU count of each device it meets.
+ *
+ *  Errors: arguments are checked on the host before anything is enqueued, so
+ *  a call that returns an error has done nothing.  SR_ERR_UNSUPPORTED means
+ *  the shape is outside the envelope below (the caller should use its
+ *  standard attention path, as the README's routing-controls section does
+ *  for shapes its kernel does not cover).  SR_ERR_HIP reports a failed launch.
+ *
+ *  Envelope: 1 <= G <= 16, d in {64, 128}, T >= 1, B*Hkv <= 2^20,
+ *  T <= 2^31 - 1.
+ */
+#ifndef SINKROUTE_H
+#define SINKROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SR_OK = 0,
+    SR_ERR_INVALID_ARG = 1,  /* null pointer, bad stride/alignment, small workspace */
+    SR_ERR_UNSUPPORTED = 2,  /* shape outside the envelope */
+    SR_ERR_HIP = 3           /* a HIP call or kernel launch failed */
+} sr_status;
+
+typedef enum { SR_KV_BF16 = 0, SR_KV_F32 = 1 } sr_kv_dtype;
+
+/* Which decode kernel runs the active groups. */
+typedef enum {
+    SR_KERNEL_AUTO = 0,  /* MFMA for bf16 caches, VALU for fp32 caches */
+    SR_KERNEL_VALU = 1,  /* vector-ALU dot products for QK and PV */
+    SR_KERNEL_MFMA = 2   /* bf16 matrix cores for QK (bf16 caches only) */
+} sr_kernel;
+
+typedef struct {
+    int32_t batch;         /* B   >= 1 */
+    int32_t num_q_heads;   /* Hq  >= 1, multiple of Hkv */
+    int32_t num_kv_heads;  /* Hkv >= 1 */
+    int32_t head_dim;      /* d: 64 or 128 */
+    int64_t seq_len;       /* T >= 1 */
+    int64_t stride_b;      /* cache strides in elements (d is contiguous) */
+    int64_t stride_h;
+    int64_t stride_t;      /* >= d */
+    int32_t kv_dtype;      /* sr_kv_dtype */
+    int32_t reserved;      /* must be 0 */
+} sr_shape;
+
+/* Launch policy for the decode kernels.  A NULL pointer means all zeros. */
+typedef struct {
+    /* > 0: every item is split into exactly this many contiguous ranges of
+     *      ceil(T / num_splits) positions (ranges past T are empty).
+     *   0: adaptive: the grid is a fixed number of workgroups sized from the
+     *      device's CU count, and the kernel splits each active item into
+     *      (grid / n_active) ranges, read from the device-side n_active, so
+     *      the GPU stays full at any sink fraction without a host sync. */
+    int32_t num_splits;
+    int32_t kernel;        /* sr_kernel */
+    int32_t wgs_per_cu;    /* adaptive grid size in workgroups per CU (0 = 2) */
+    int32_t reserved;      /* must be 0 */
+} sr_launch;
+
+/* Prefill side (README decode-time steps: the prefill path keeps the key at
+ * position 0).  k0[b][g][:] = K[b][g][0][:], v0[b][g][:] = V[b][g][0][:],
+ * widened exactly to fp32.  Idempotent. */
+sr_status sr_record_sink(const sr_shape* shape, const void* k_cache, const void* v_cache,
+                         float* k0, float* v0, void* stream);
+
+/* Routing (README decode-time steps and routing controls; pith.science
+ * Figure 10: cos(q, K_BOS) at the KV-group level).
+ *   q       fp32 [B][Hq][d], post-RoPE queries.
+ *   k0      fp32 [B][Hkv][d] from sr_record_sink.
+ *   tau     cosine threshold; a group is a sink iff every one of its G heads
+ *           has cos >= tau.  tau > 1 routes nothing (every group active).
+ *   scores  out fp32 [B][Hq]: cos(q[b,h], k0[b,h/G]); 0 if either norm is 0.
+ *   mask    out u8 [B][Hkv]: 1 = sink.
+ *   work_list out i32 [B*Hkv]: active items ascending, then sinks ascending.
+ *   n_active  out i32 [1]: number of active items (stays on the device).
+ * Runs as one workgroup; B*Hq heads of 3*d multiply-adds each. */
+sr_status sr_route(const sr_shape* shape, const float* q, const float* k0, float tau,
+                   float* scores, uint8_t* mask, int32_t* work_list, int32_t* n_active,
+                   void* stream);
+
+/* Bytes of scratch the decode calls need for this shape and launch policy:
+ * per-workgroup split partials (m, l and acc, fp32) plus one ticket per item.
+ * Depends on the current device's CU count in adaptive mode. Returns 0 on an
+ * invalid or unsupported shape. */
+size_t sr_workspace_bytes(const sr_shape* shape, const sr_launch* launch);
+
+/* Zero a new workspace once (the tickets).  Every decode call leaves the
+ * tickets it used back at zero, so a workspace is reusable as is.  Two
+ * calls that may run at the same time must not share a workspace. */
+sr_status sr_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Routed decode (README decode-time steps; paper Eq. (1)).
+ *   work_list, n_active: device outputs of sr_route.  Items at positions
+ *   [n_active, B*Hkv) of the list are sinks: their G output rows get v0
+ *   (bit-exact) and their caches are never read.  Items before are active:
+ *     out[b,h,:] = sum_t softmax_t(sm_scale * <q[b,h], K[b,g,t]>) V[b,g,t,:]
+ *   over t = 0..T-1, fp32 accumulation, split over the context and merged in
+ *   ascending split order (bitwise reproducible for a given launch policy).
+ *   sm_scale <= 0 means 1/sqrt(d).
+ *   For bf16 caches the MFMA kernel splits each scaled query into a sum of
+ *   bf16 terms; products with the stored bf16 keys are exact and the logits
+ *   carry ~2^-16 relative error in the query, far below the tolerance.
+ *   ws: at least sr_workspace_bytes(shape, launch) bytes, initialised once
+ *   by sr_workspace_init. */
+sr_status sr_decode_attn(const sr_shape* shape, const sr_launch* launch, const float* q,
+                         const void* k_cache, const void* v_cache, const float* v0,
+                         const int32_t* work_list, const int32_t* n_active, float sm_scale,
+                         void* ws, size_t ws_bytes, float* out, void* stream);
+
+/* Dense baseline: the decode kernel of sr_decode_attn with routing off
+ * (identity work list, every item active).  sr_decode_attn with a work list
+ * routed at tau > 1 gives the same bits for the same launch policy. */
+sr_status sr_dense_decode(const sr_shape* shape, const sr_launch* launch, const float* q,
+                          const void* k_cache, const void* v_cache, float sm_scale,
+                          void* ws, size_t ws_bytes, float* out, void* stream);
+
+/* Number of splits per active item the decode kernel will use for a given
+ * n_active under this policy (what the adaptive mode derives on the device). */
+int32_t sr_splits_for(const sr_shape* shape, const sr_launch* launch, int32_t n_active);
+
+/* Workgroups the decode kernel launches under this policy. */
+int32_t sr_grid_size(const sr_shape* shape, const sr_launch* launch);
+
+const char* sr_status_string(sr_status status);
+
+/* Library version, e.g. 100 for 0.1.0. */
+int32_t sr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SINKROUTE_H */

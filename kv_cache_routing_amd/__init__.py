@@ -1,0 +1,163 @@
+"""Python binding of libsinkroute (sink-routed GQA decode attention, gfx950).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+library.  torch supplies device memory and the current stream.
+
+    k0, v0 = record_sink(k, v)                   # prefill side
+    r = route(q, k0, tau=0.5)                    # scores, mask, work_list, n_active
+    out = decode_attn(q, k, v, v0, r.work_list, r.n_active)
+    ref = dense_decode(q, k, v)                  # routing off
+
+Shapes: q [B][Hq][d] fp32; caches [B][Hkv][T][d] (bf16 or fp32, d contiguous,
+any T_max >= T via a narrowed view); k0, v0 [B][Hkv][d] fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _native as N
+from ._native import (SR_KERNEL_AUTO, SR_KERNEL_MFMA, SR_KERNEL_VALU,  # noqa: F401
+                      SinkRouteError)
+
+__all__ = ["record_sink", "route", "decode_attn", "dense_decode", "Workspace", "make_shape",
+           "make_launch", "splits_for", "grid_size", "SinkRouteError", "Routing",
+           "SR_KERNEL_AUTO", "SR_KERNEL_VALU", "SR_KERNEL_MFMA"]
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("libsinkroute takes device tensors")
+
+
+def make_shape(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None = None) -> N.SrShape:
+    """sr_shape from q [B][Hq][d] and a cache view [B][Hkv][T][d]."""
+    if k.dim() != 4:
+        raise ValueError("cache must be [B][Hkv][T][d]")
+    if v is not None and (v.shape != k.shape or v.stride() != k.stride() or v.dtype != k.dtype):
+        raise ValueError("K and V caches must share shape, strides and dtype")
+    if k.stride(3) != 1:
+        raise ValueError("head_dim must be contiguous")
+    if k.dtype == torch.bfloat16:
+        dt = N.SR_KV_BF16
+    elif k.dtype == torch.float32:
+        dt = N.SR_KV_F32
+    else:
+        raise ValueError(f"unsupported cache dtype {k.dtype}")
+    B, Hkv, T, d = k.shape
+    Hq = q.shape[1] if q is not None else Hkv
+    return N.SrShape(B, Hq, Hkv, d, T, k.stride(0), k.stride(1), k.stride(2), dt, 0)
+
+
+def make_launch(num_splits: int = 0, kernel: int = SR_KERNEL_AUTO, wgs_per_cu: int = 0):
+    return N.SrLaunch(num_splits, kernel, wgs_per_cu, 0)
+
+
+def splits_for(shape: N.SrShape, launch: N.SrLaunch | None, n_active: int) -> int:
+    return N.lib.sr_splits_for(ctypes.byref(shape), _lp(launch), n_active)
+
+
+def grid_size(shape: N.SrShape, launch: N.SrLaunch | None) -> int:
+    return N.lib.sr_grid_size(ctypes.byref(shape), _lp(launch))
+
+
+def _lp(launch):
+    return None if launch is None else ctypes.byref(launch)
+
+
+class Workspace:
+    """Scratch for the decode calls (split partials + tickets), zeroed once."""
+
+    def __init__(self, shape: N.SrShape, launch: N.SrLaunch | None, device):
+        self.nbytes = int(N.lib.sr_workspace_bytes(ctypes.byref(shape), _lp(launch)))
+        if self.nbytes == 0:
+            raise SinkRouteError(N.SR_ERR_UNSUPPORTED, "sr_workspace_bytes")
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        N.check(N.lib.sr_workspace_init(_ptr(self.buf), self.nbytes, _stream()),
+                "sr_workspace_init")
+
+    def fits(self, shape, launch) -> bool:
+        return int(N.lib.sr_workspace_bytes(ctypes.byref(shape), _lp(launch))) <= self.nbytes
+
+
+def record_sink(k: torch.Tensor, v: torch.Tensor, q_heads: int | None = None):
+    _need_cuda(k, v)
+    shape = make_shape(None, k, v)
+    B, Hkv, _, d = k.shape
+    k0 = torch.empty((B, Hkv, d), dtype=torch.float32, device=k.device)
+    v0 = torch.empty_like(k0)
+    N.check(N.lib.sr_record_sink(ctypes.byref(shape), _ptr(k), _ptr(v), _ptr(k0), _ptr(v0),
+                                 _stream()), "sr_record_sink")
+    return k0, v0
+
+
+@dataclass
+class Routing:
+    scores: torch.Tensor     # [B][Hq] fp32
+    mask: torch.Tensor       # [B][Hkv] uint8, 1 = sink
+    work_list: torch.Tensor  # [B*Hkv] int32
+    n_active: torch.Tensor   # [1] int32 (device)
+
+
+def route(q: torch.Tensor, k0: torch.Tensor, tau: float = 0.5, out: Routing | None = None):
+    _need_cuda(q, k0)
+    B, Hkv, d = k0.shape
+    Hq = q.shape[1]
+    if q.dtype != torch.float32 or k0.dtype != torch.float32:
+        raise ValueError("q and k0 are fp32")
+    q = q.contiguous()
+    k0 = k0.contiguous()
+    shape = N.SrShape(B, Hq, Hkv, d, 1, Hkv * d, d, d, N.SR_KV_F32, 0)
+    if out is None:
+        dev = q.device
+        out = Routing(torch.empty((B, Hq), dtype=torch.float32, device=dev),
+                      torch.empty((B, Hkv), dtype=torch.uint8, device=dev),
+                      torch.empty((B * Hkv,), dtype=torch.int32, device=dev),
+                      torch.empty((1,), dtype=torch.int32, device=dev))
+    N.check(N.lib.sr_route(ctypes.byref(shape), _ptr(q), _ptr(k0), ctypes.c_float(tau),
+                           _ptr(out.scores), _ptr(out.mask), _ptr(out.work_list),
+                           _ptr(out.n_active), _stream()), "sr_route")
+    return out
+
+
+def _prep(q, k, v, launch, ws, out):
+    _need_cuda(q, k, v)
+    if q.dtype != torch.float32 or not q.is_contiguous():
+        raise ValueError("q must be contiguous fp32 [B][Hq][d]")
+    shape = make_shape(q, k, v)
+    if ws is None or not ws.fits(shape, launch):
+        ws = Workspace(shape, launch, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    return shape, ws, out
+
+
+def decode_attn(q, k, v, v0, work_list, n_active, sm_scale: float = 0.0,
+                launch: N.SrLaunch | None = None, ws: Workspace | None = None,
+                out: torch.Tensor | None = None):
+    shape, ws, out = _prep(q, k, v, launch, ws, out)
+    N.check(N.lib.sr_decode_attn(ctypes.byref(shape), _lp(launch), _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(v0), _ptr(work_list), _ptr(n_active),
+                                 ctypes.c_float(sm_scale), _ptr(ws.buf), ws.nbytes, _ptr(out),
+                                 _stream()), "sr_decode_attn")
+    return out
+
+
+def dense_decode(q, k, v, sm_scale: float = 0.0, launch: N.SrLaunch | None = None,
+                 ws: Workspace | None = None, out: torch.Tensor | None = None):
+    shape, ws, out = _prep(q, k, v, launch, ws, out)
+    N.check(N.lib.sr_dense_decode(ctypes.byref(shape), _lp(launch), _ptr(q), _ptr(k), _ptr(v),
+                                  ctypes.c_float(sm_scale), _ptr(ws.buf), ws.nbytes, _ptr(out),
+                                  _stream()), "sr_dense_decode")
+    return out

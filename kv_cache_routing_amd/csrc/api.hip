@@ -1,0 +1,237 @@
+// C ABI of libsinkroute: argument checks, launch sizing and dispatch.
+// Declarations and the contract of every call are in include/sinkroute.h.
+#include <math.h>
+
+#include <atomic>
+
+#include "sr_internal.h"
+
+namespace sr {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not yet queried
+
+int cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int n = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+        n = 256;
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+constexpr int32_t kMaxItems = 32768;  // route kernel keeps one flag per item in LDS
+
+size_t elem_size(const sr_shape& s) { return s.kv_dtype == SR_KV_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+sr_status check_shape(const sr_shape* s) {
+    if (!s) return SR_ERR_INVALID_ARG;
+    if (s->reserved != 0) return SR_ERR_INVALID_ARG;
+    if (s->batch < 1 || s->num_kv_heads < 1 || s->num_q_heads < 1) return SR_ERR_INVALID_ARG;
+    if (s->num_q_heads % s->num_kv_heads != 0) return SR_ERR_INVALID_ARG;
+    if (s->seq_len < 1) return SR_ERR_INVALID_ARG;
+    if (s->kv_dtype != SR_KV_BF16 && s->kv_dtype != SR_KV_F32) return SR_ERR_INVALID_ARG;
+    const int32_t G = s->num_q_heads / s->num_kv_heads;
+    if (G > 16) return SR_ERR_UNSUPPORTED;
+    if (s->head_dim != 64 && s->head_dim != 128) return SR_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(s->batch) * s->num_kv_heads > kMaxItems) return SR_ERR_UNSUPPORTED;
+    if (s->seq_len > INT32_MAX) return SR_ERR_UNSUPPORTED;
+    if (s->stride_t < s->head_dim || s->stride_h < 0 || s->stride_b < 0) return SR_ERR_INVALID_ARG;
+    const int64_t es = static_cast<int64_t>(elem_size(*s));
+    if ((s->stride_t * es) % 16 || (s->stride_h * es) % 16 || (s->stride_b * es) % 16)
+        return SR_ERR_INVALID_ARG;
+    return SR_OK;
+}
+
+sr_status check_caches(const sr_shape& s, const void* k, const void* v) {
+    if (!k || !v || !aligned16(k) || !aligned16(v)) return SR_ERR_INVALID_ARG;
+    return SR_OK;
+}
+
+struct Plan {
+    int32_t fixed_splits, grid, split_cap, gp, kernel;
+};
+
+sr_status make_plan(const sr_shape& s, const sr_launch* launch, Plan& p) {
+    sr_launch l{};
+    if (launch) l = *launch;
+    if (l.reserved != 0 || l.num_splits < 0 || l.wgs_per_cu < 0) return SR_ERR_INVALID_ARG;
+    if (l.kernel < SR_KERNEL_AUTO || l.kernel > SR_KERNEL_MFMA) return SR_ERR_INVALID_ARG;
+    p.kernel = l.kernel == SR_KERNEL_AUTO ? SR_KERNEL_VALU : l.kernel;
+    if (p.kernel == SR_KERNEL_MFMA && s.kv_dtype != SR_KV_BF16) return SR_ERR_UNSUPPORTED;
+    const int64_t n_items = static_cast<int64_t>(s.batch) * s.num_kv_heads;
+    p.gp = pad_group(s.num_q_heads / s.num_kv_heads);
+    const int64_t cap = (s.seq_len + kMinSplitLen - 1) / kMinSplitLen;
+    if (l.num_splits > 0) {
+        const int64_t grid = n_items * l.num_splits;
+        if (grid > INT32_MAX) return SR_ERR_UNSUPPORTED;
+        p.fixed_splits = l.num_splits;
+        p.grid = static_cast<int32_t>(grid);
+        p.split_cap = l.num_splits;
+    } else {
+        const int32_t per_cu = l.wgs_per_cu > 0 ? l.wgs_per_cu : 2;
+        int64_t grid = static_cast<int64_t>(per_cu) * cu_count();
+        if (grid < n_items) grid = n_items;
+        if (grid > INT32_MAX) return SR_ERR_UNSUPPORTED;
+        p.fixed_splits = 0;
+        p.grid = static_cast<int32_t>(grid);
+        p.split_cap = static_cast<int32_t>(cap < 1 ? 1 : cap);
+    }
+    return SR_OK;
+}
+
+constexpr size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct WsLayout {
+    size_t tickets, ml, acc, total;
+};
+
+WsLayout ws_layout(const sr_shape& s, const Plan& p) {
+    const size_t n_items = static_cast<size_t>(s.batch) * s.num_kv_heads;
+    WsLayout w;
+    w.tickets = 0;
+    w.ml = align256(n_items * sizeof(uint32_t));
+    w.acc = w.ml + align256(static_cast<size_t>(p.grid) * 2 * p.gp * sizeof(float));
+    w.total = w.acc + align256(static_cast<size_t>(p.grid) * p.gp * s.head_dim * sizeof(float));
+    return w;
+}
+
+sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float* q,
+                     const void* k, const void* v, const float* v0, const int32_t* work_list,
+                     const int32_t* n_active, float sm_scale, void* ws, size_t ws_bytes,
+                     float* out, void* stream, bool routed) {
+    sr_status st = check_shape(shape);
+    if (st != SR_OK) return st;
+    const sr_shape& s = *shape;
+    if ((st = check_caches(s, k, v)) != SR_OK) return st;
+    if (!q || !out || !ws || !aligned16(q) || !aligned16(out) || !aligned16(ws))
+        return SR_ERR_INVALID_ARG;
+    if (routed && (!v0 || !work_list || !n_active)) return SR_ERR_INVALID_ARG;
+    Plan p;
+    if ((st = make_plan(s, launch, p)) != SR_OK) return st;
+    const WsLayout w = ws_layout(s, p);
+    if (ws_bytes < w.total) return SR_ERR_INVALID_ARG;
+
+    DecodeArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.v0 = v0;
+    a.work_list = work_list;
+    a.n_active = n_active;
+    a.out = out;
+    char* base = static_cast<char*>(ws);
+    a.tickets = reinterpret_cast<uint32_t*>(base + w.tickets);
+    a.part_ml = reinterpret_cast<float*>(base + w.ml);
+    a.part_acc = reinterpret_cast<float*>(base + w.acc);
+    a.stride_b = s.stride_b;
+    a.stride_h = s.stride_h;
+    a.stride_t = s.stride_t;
+    a.seq_len = s.seq_len;
+    a.batch = s.batch;
+    a.num_q_heads = s.num_q_heads;
+    a.num_kv_heads = s.num_kv_heads;
+    a.group = s.num_q_heads / s.num_kv_heads;
+    const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf(static_cast<float>(s.head_dim));
+    a.qscale = scale * 1.4426950408889634f;
+    a.fixed_splits = p.fixed_splits;
+    a.grid = p.grid;
+    a.split_cap = p.split_cap;
+    a.routed = routed ? 1 : 0;
+
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e = p.kernel == SR_KERNEL_MFMA ? launch_decode_mfma(s, a, p.gp, hs)
+                                               : launch_decode_valu(s, a, p.gp, hs);
+    return e == hipSuccess ? SR_OK : SR_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace sr
+
+using namespace sr;
+
+extern "C" {
+
+sr_status sr_record_sink(const sr_shape* shape, const void* k_cache, const void* v_cache,
+                         float* k0, float* v0, void* stream) {
+    sr_status st = check_shape(shape);
+    if (st != SR_OK) return st;
+    if ((st = check_caches(*shape, k_cache, v_cache)) != SR_OK) return st;
+    if (!k0 || !v0) return SR_ERR_INVALID_ARG;
+    hipError_t e = launch_record(*shape, k_cache, v_cache, k0, v0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SR_OK : SR_ERR_HIP;
+}
+
+sr_status sr_route(const sr_shape* shape, const float* q, const float* k0, float tau,
+                   float* scores, uint8_t* mask, int32_t* work_list, int32_t* n_active,
+                   void* stream) {
+    sr_status st = check_shape(shape);
+    if (st != SR_OK) return st;
+    if (!q || !k0 || !scores || !mask || !work_list || !n_active) return SR_ERR_INVALID_ARG;
+    if (isnan(tau)) return SR_ERR_INVALID_ARG;
+    hipError_t e = launch_route(*shape, q, k0, tau, scores, mask, work_list, n_active,
+                                static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SR_OK : SR_ERR_HIP;
+}
+
+size_t sr_workspace_bytes(const sr_shape* shape, const sr_launch* launch) {
+    if (check_shape(shape) != SR_OK) return 0;
+    Plan p;
+    if (make_plan(*shape, launch, p) != SR_OK) return 0;
+    return ws_layout(*shape, p).total;
+}
+
+sr_status sr_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+    if (!ws || !aligned16(ws)) return SR_ERR_INVALID_ARG;
+    hipError_t e = launch_zero(ws, ws_bytes, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SR_OK : SR_ERR_HIP;
+}
+
+sr_status sr_decode_attn(const sr_shape* shape, const sr_launch* launch, const float* q,
+                         const void* k_cache, const void* v_cache, const float* v0,
+                         const int32_t* work_list, const int32_t* n_active, float sm_scale,
+                         void* ws, size_t ws_bytes, float* out, void* stream) {
+    return run_decode(shape, launch, q, k_cache, v_cache, v0, work_list, n_active, sm_scale, ws,
+                      ws_bytes, out, stream, true);
+}
+
+sr_status sr_dense_decode(const sr_shape* shape, const sr_launch* launch, const float* q,
+                          const void* k_cache, const void* v_cache, float sm_scale, void* ws,
+                          size_t ws_bytes, float* out, void* stream) {
+    return run_decode(shape, launch, q, k_cache, v_cache, nullptr, nullptr, nullptr, sm_scale, ws,
+                      ws_bytes, out, stream, false);
+}
+
+int32_t sr_splits_for(const sr_shape* shape, const sr_launch* launch, int32_t n_active) {
+    if (check_shape(shape) != SR_OK) return 0;
+    Plan p;
+    if (make_plan(*shape, launch, p) != SR_OK) return 0;
+    return splits_for(p.fixed_splits, p.grid, p.split_cap, n_active);
+}
+
+int32_t sr_grid_size(const sr_shape* shape, const sr_launch* launch) {
+    if (check_shape(shape) != SR_OK) return 0;
+    Plan p;
+    if (make_plan(*shape, launch, p) != SR_OK) return 0;
+    return p.grid;
+}
+
+const char* sr_status_string(sr_status status) {
+    switch (status) {
+        case SR_OK: return "ok";
+        case SR_ERR_INVALID_ARG: return "invalid argument";
+        case SR_ERR_UNSUPPORTED: return "unsupported shape (use the standard attention path)";
+        case SR_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+int32_t sr_version(void) { return 100; }
+
+}  // extern "C"

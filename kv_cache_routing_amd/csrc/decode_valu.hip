@@ -1,0 +1,213 @@
+// Split-K flash-decode of the active groups with vector-ALU dot products.
+// Handles fp32 and bf16 caches, d in {64, 128}, any group size up to 16.
+//
+// Layout: a wave reads a tile of whole cache rows.  Each lane owns 8
+// consecutive elements of one row (16 B of bf16, 32 B of fp32), so a row is
+// spread over d/8 lanes (a "lane group") and one wave-wide load instruction
+// covers 64/(d/8) consecutive rows: fully coalesced.  QK is an 8-term dot
+// product per lane followed by a DPP all-reduce inside the lane group; PV
+// accumulates p * V for the lane's 8 elements.  Every lane group keeps its own
+// running maximum, sum and accumulator (online softmax in base 2, rescaled
+// only when a tile raises the maximum); the groups of a wave, then the waves
+// of the workgroup, are merged at the end of the split.
+//
+// Method: SinkRouter README (github.com/streamer-AP/SinkRouter), decode-time
+// steps (tiled QK/PV with an online softmax, Split-K, in-kernel merge).
+#include "decode_common.h"
+
+namespace sr {
+namespace {
+
+template <typename KV>
+struct Row8;
+
+template <>
+struct Row8<uint16_t> {  // bf16 bits
+    __device__ static inline void load(const uint16_t* p, float (&x)[8]) {
+        const uint4 r = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+};
+
+template <>
+struct Row8<float> {
+    __device__ static inline void load(const float* p, float (&x)[8]) {
+        const float4 a = *reinterpret_cast<const float4*>(p);
+        const float4 b = *reinterpret_cast<const float4*>(p + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+};
+
+template <typename KV, int D, int GP, int NW, int U>
+__global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
+    constexpr int E = 8, LPT = D / E, TPI = 64 / LPT, TILE = TPI * U;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = lane / LPT, chunk = lane % LPT;
+
+    __shared__ float s_m[NW][GP], s_l[NW][GP];
+    __shared__ float s_acc[NW][GP][D];
+
+    WorkUnit u;
+    if (!map_work<D, NW * 64>(a, u)) return;
+    const int32_t G = a.group;
+
+    float qs[GP][E];
+    {
+        const float* qb = a.q + (static_cast<int64_t>(u.b) * a.num_q_heads +
+                                 static_cast<int64_t>(u.g) * G) * D + chunk * E;
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+            if (h < G) {
+                const float4 x0 = *reinterpret_cast<const float4*>(qb + h * D);
+                const float4 x1 = *reinterpret_cast<const float4*>(qb + h * D + 4);
+                qs[h][0] = x0.x * a.qscale; qs[h][1] = x0.y * a.qscale;
+                qs[h][2] = x0.z * a.qscale; qs[h][3] = x0.w * a.qscale;
+                qs[h][4] = x1.x * a.qscale; qs[h][5] = x1.y * a.qscale;
+                qs[h][6] = x1.z * a.qscale; qs[h][7] = x1.w * a.qscale;
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) qs[h][e] = 0.f;
+            }
+        }
+    }
+
+    const KV* kb = static_cast<const KV*>(a.k) + u.b * a.stride_b + u.g * a.stride_h + chunk * E;
+    const KV* vb = static_cast<const KV*>(a.v) + u.b * a.stride_b + u.g * a.stride_h + chunk * E;
+    const int64_t st = a.stride_t;
+
+    float m[GP], l[GP], acc[GP][E];
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+        m[h] = kNegInf;
+        l[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+    }
+
+    const int64_t last = u.t1 - 1;
+    for (int64_t tile = u.t0 + static_cast<int64_t>(wave) * TILE; tile < u.t1;
+         tile += static_cast<int64_t>(NW) * TILE) {
+        float kf[U][E], vf[U][E];
+        bool valid[U];
+#pragma unroll
+        for (int v = 0; v < U; ++v) {
+            const int64_t t = tile + v * TPI + row;
+            valid[v] = t < u.t1;
+            const int64_t tl = valid[v] ? t : last;  // clamped: always a real row
+            Row8<KV>::load(kb + tl * st, kf[v]);
+            Row8<KV>::load(vb + tl * st, vf[v]);
+        }
+        float z[U][GP];
+#pragma unroll
+        for (int v = 0; v < U; ++v) {
+#pragma unroll
+            for (int h = 0; h < GP; ++h) {
+                float s = 0.f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) s += qs[h][e] * kf[v][e];
+                s = group_allreduce_sum<LPT>(s);
+                z[v][h] = valid[v] ? s : kNegInf;
+            }
+        }
+        bool up = false;
+        float zm[GP];
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+            zm[h] = z[0][h];
+#pragma unroll
+            for (int v = 1; v < U; ++v) zm[h] = fmaxf(zm[h], z[v][h]);
+            up = up || (zm[h] > m[h]);
+        }
+        if (__any(up)) {
+#pragma unroll
+            for (int h = 0; h < GP; ++h) {
+                const float mn = fmaxf(m[h], zm[h]);
+                const float al = mn > m[h] ? fast_exp2(m[h] - mn) : 1.f;
+                m[h] = mn;
+                l[h] *= al;
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[h][e] *= al;
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < U; ++v) {
+#pragma unroll
+            for (int h = 0; h < GP; ++h) {
+                const float p = valid[v] ? fast_exp2(z[v][h] - m[h]) : 0.f;
+                l[h] += p;
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[h][e] += p * vf[v][e];
+            }
+        }
+    }
+
+    // merge the lane groups of this wave (lanes with the same chunk)
+#pragma unroll
+    for (int o = LPT; o < 64; o <<= 1) {
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+            const float mo = __shfl_xor(m[h], o);
+            const float lo = __shfl_xor(l[h], o);
+            const float M = fmaxf(m[h], mo);
+            const float wa = merge_weight(m[h], M), wb = merge_weight(mo, M);
+            l[h] = l[h] * wa + lo * wb;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float ao = __shfl_xor(acc[h][e], o);
+                acc[h][e] = acc[h][e] * wa + ao * wb;
+            }
+            m[h] = M;
+        }
+    }
+    if (row == 0) {
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) s_acc[wave][h][chunk * E + e] = acc[h][e];
+            if (chunk == 0) {
+                s_m[wave][h] = m[h];
+                s_l[wave][h] = l[h];
+            }
+        }
+    }
+    __syncthreads();
+    finish_split<D, GP, NW>(a, u, s_m, s_l, s_acc);
+}
+
+template <typename KV, int D, int GP>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
+    constexpr int NW = kDecodeThreads / 64;
+    constexpr int U = GP >= 16 ? 1 : (GP >= 8 ? 2 : 4);
+    hipLaunchKernelGGL((k_decode_valu<KV, D, GP, NW, U>), dim3(a.grid), dim3(NW * 64), 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename KV, int D>
+hipError_t launch_g(const DecodeArgs& a, int gp, hipStream_t st) {
+    switch (gp) {
+        case 1: return launch_t<KV, D, 1>(a, st);
+        case 2: return launch_t<KV, D, 2>(a, st);
+        case 4: return launch_t<KV, D, 4>(a, st);
+        case 8: return launch_t<KV, D, 8>(a, st);
+        case 16: return launch_t<KV, D, 16>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_valu(const sr_shape& s, const DecodeArgs& a, int gp, hipStream_t st) {
+    if (s.kv_dtype == SR_KV_BF16) {
+        return s.head_dim == 128 ? launch_g<uint16_t, 128>(a, gp, st)
+                                 : launch_g<uint16_t, 64>(a, gp, st);
+    }
+    return s.head_dim == 128 ? launch_g<float, 128>(a, gp, st) : launch_g<float, 64>(a, gp, st);
+}
+
+}  // namespace sr

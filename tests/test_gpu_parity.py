@@ -1,0 +1,271 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every test draws its layer from the seeded generator, runs record -> route ->
+decode on cuda:0 and checks: routing mask and work list bit-exact, sink rows
+bit-exact v0, active rows within max-abs 1e-2 / mean-abs 1e-3 / per-row
+rel-L2 1e-3 of the oracle (plus a tighter 2e-4 precision check).
+Small layers are checked in full; the full-size layers on sampled items.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import (assert_outputs, assert_route, log, oracle_inputs, sink_rows_exact,
+                    ticket_region, upload)
+from workloads import (CONFIGS, L70B_128K_B8, L8B_128K, L8B_256K_B4, L8B_512K, SINK_FRACTIONS,
+                       TINY, Workload, as_numpy, make_caches, make_layer, make_queries, sweep)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import kv_cache_routing_amd as sr
+else:  # collected on CPU only to be deselected by -m "not gpu"
+    sr = None
+
+BF16_KERNELS = ["valu"]
+KERNEL_ID = {"valu": 1, "mfma": 2, "auto": 0}
+
+
+def launch(kernel="auto", splits=0, per_cu=0):
+    return sr.make_launch(splits, KERNEL_ID[kernel], per_cu)
+
+
+def run_routed(q, k, v, tau, lau):
+    k0, v0 = sr.record_sink(k, v)
+    r = sr.route(q, k0, tau)
+    out = sr.decode_attn(q, k, v, v0, r.work_list, r.n_active, launch=lau)
+    return k0, v0, r, out
+
+
+def full_check(layer, lau, tau=None, check_dense=True):
+    wl = layer.wl
+    tau = wl.tau if tau is None else tau
+    G = wl.group_size
+    q_np, k_np, v_np = oracle_inputs(layer)
+    q, k, v = upload(layer)
+    k0, v0, r, out = run_routed(q, k, v, tau, lau)
+    torch.cuda.synchronize()
+    k0_ref, v0_ref = oracle.record_sink(k_np, v_np)
+    assert np.array_equal(k0.cpu().numpy(), k0_ref) and np.array_equal(v0.cpu().numpy(), v0_ref)
+    mask, n_active = assert_route(r, q_np, k0_ref, tau)
+    got = out.cpu().numpy()
+    ref = oracle.routed_decode(q_np, k_np, v_np, v0_ref, mask)
+    n_sink = sink_rows_exact(got, v0_ref, mask, G)
+    log(f"{wl.name} T={wl.seq_len} G={G} n_active={n_active} sink_rows={n_sink}")
+    if n_active:
+        act = np.repeat(mask == 0, G, axis=1)
+        assert_outputs(got[act], ref[act], "routed active rows")
+    if check_dense:
+        dense = sr.dense_decode(q, k, v, launch=lau).cpu().numpy()
+        assert_outputs(dense, oracle.dense_decode(q_np, k_np, v_np), "dense")
+    return got
+
+
+def test_tiny_layer_full_parity():
+    log("tiny")
+    full_check(make_layer(TINY), launch("valu"))
+
+
+REDUCED = [
+    Workload("8b-ragged", 1, 32, 8, 128, 12345, "bf16", seed=11, sink_plan=("count", 4)),
+    Workload("70b-shape", 2, 64, 8, 128, 6000, "bf16", seed=12, sink_plan=("bernoulli", 0.5)),
+    Workload("d64-g2", 2, 8, 4, 64, 3001, "bf16", seed=13, sink_plan=("count", 2)),
+    Workload("g3-nonpow2", 1, 12, 4, 128, 2100, "bf16", seed=14, sink_plan=("count", 1)),
+    Workload("mha-g1", 1, 8, 8, 128, 5000, "bf16", seed=15, sink_plan=("count", 3)),
+    Workload("g16-d64", 1, 32, 2, 64, 2000, "bf16", seed=16, sink_plan=("count", 1)),
+    Workload("g6-d64", 3, 12, 2, 64, 999, "bf16", seed=17, sink_plan=("bernoulli", 0.5)),
+    Workload("f32-d128-g4", 1, 16, 4, 128, 3333, "f32", seed=18, sink_plan=("count", 2)),
+    Workload("f32-g8-d64", 2, 16, 2, 64, 700, "f32", seed=19, sink_plan=("count", 1)),
+]
+
+
+@pytest.mark.parametrize("wl", REDUCED, ids=lambda w: w.name)
+@pytest.mark.parametrize("kernel", ["auto"] + BF16_KERNELS)
+def test_reduced_layers(wl, kernel):
+    if wl.kv_dtype == "f32" and kernel == "mfma":
+        pytest.skip("matrix-core kernel takes bf16 caches")
+    log(f"reduced {wl.name} kernel={kernel}")
+    full_check(make_layer(wl), launch(kernel))
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_split_count_sweep(kernel):
+    wl = Workload("8b-splits", 1, 32, 8, 128, 8192 + 77, "bf16", seed=21, sink_plan=("count", 4))
+    layer = make_layer(wl)
+    q_np, k_np, v_np = oracle_inputs(layer)
+    ref = oracle.dense_decode(q_np, k_np, v_np)
+    q, k, v = upload(layer)
+    for S in (1, 2, 3, 7, 64, 129, 300):
+        got = sr.dense_decode(q, k, v, launch=launch(kernel, splits=S)).cpu().numpy()
+        assert_outputs(got, ref, f"dense S={S}")
+    for per_cu in (1, 2, 4, 8):
+        got = sr.dense_decode(q, k, v, launch=launch(kernel, per_cu=per_cu)).cpu().numpy()
+        assert_outputs(got, ref, f"dense adaptive {per_cu}/CU")
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_more_splits_than_positions(kernel):
+    wl = Workload("short", 1, 8, 2, 128, 200, "bf16", seed=22)
+    layer = make_layer(wl)
+    q, k, v = upload(layer)
+    ref = oracle.dense_decode(*oracle_inputs(layer))
+    got = sr.dense_decode(q, k, v, launch=launch(kernel, splits=205)).cpu().numpy()
+    assert_outputs(got, ref, "S = T + 5")
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_tau_above_one_matches_dense_bitwise_and_repeats(kernel):
+    wl = L8B_128K.with_(seq_len=20000, name="8b-20k")
+    layer = make_layer(wl)
+    q, k, v = upload(layer)
+    for lau in (launch(kernel), launch(kernel, splits=17)):
+        k0, v0, r, out = run_routed(q, k, v, 2.0, lau)
+        assert int(r.n_active.cpu()[0]) == 8
+        dense = sr.dense_decode(q, k, v, launch=lau)
+        assert torch.equal(out, dense)
+    # repeated calls on one workspace: bitwise identical, tickets back to zero
+    lau = launch(kernel)
+    shape = sr.make_shape(q, k, v)
+    ws = sr.Workspace(shape, lau, q.device)
+    k0, v0 = sr.record_sink(k, v)
+    r = sr.route(q, k0, wl.tau)
+    first = sr.decode_attn(q, k, v, v0, r.work_list, r.n_active, launch=lau, ws=ws).clone()
+    for _ in range(200):
+        again = sr.decode_attn(q, k, v, v0, r.work_list, r.n_active, launch=lau, ws=ws)
+        assert torch.equal(again, first)
+    torch.cuda.synchronize()
+    assert int(ticket_region(ws, 8).abs().sum()) == 0
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_fixed_splits_routed_rows_equal_dense_rows(kernel):
+    wl = L8B_128K.with_(seq_len=9000, name="8b-9k")
+    layer = make_layer(wl)
+    q, k, v = upload(layer)
+    lau = launch(kernel, splits=11)
+    k0, v0, r, out = run_routed(q, k, v, wl.tau, lau)
+    dense = sr.dense_decode(q, k, v, launch=lau)
+    act = (r.mask == 0).repeat_interleave(4, dim=1)
+    assert torch.equal(out[act], dense[act])
+
+
+def test_special_cases_single_position_zero_query_fixed_point():
+    # T = 1: the output is v0 exactly (one weight of 1)
+    wl = Workload("t1", 2, 8, 2, 128, 1, "bf16", seed=31)
+    layer = make_layer(wl)
+    q, k, v = upload(layer)
+    for kernel in BF16_KERNELS:
+        out = sr.dense_decode(q, k, v, launch=launch(kernel)).cpu()
+        assert torch.equal(out, layer.v[:, :, 0].float().repeat_interleave(4, dim=1))
+    # q = 0: uniform weights, output is the mean of V; every score is 0 -> active
+    wl = Workload("q0", 1, 8, 2, 64, 3000, "bf16", seed=32)
+    layer = make_layer(wl)
+    q, k, v = upload(layer)
+    q.zero_()
+    k0, v0, r, out = run_routed(q, k, v, 0.5, launch("auto"))
+    assert int(r.n_active.cpu()[0]) == 2 and float(r.scores.abs().max()) == 0.0
+    ref = np.repeat(as_numpy(layer.v).astype(np.float64).mean(axis=2), 4, axis=1)
+    assert_outputs(out.cpu().numpy(), ref, "q=0 mean of V")
+    # fixed point: all softmax mass at position 0 -> the output is v0
+    d, T = 64, 4096
+    gen = torch.Generator().manual_seed(33)
+    kk = torch.randn((1, 1, T, d), generator=gen)
+    vv = torch.randn((1, 1, T, d), generator=gen)
+    kk[0, 0, 0] *= 400.0 / kk[0, 0, 0].norm()
+    qq = (kk[0, 0, 0] / kk[0, 0, 0].norm()).reshape(1, 1, d).contiguous()
+    out = sr.dense_decode(qq.cuda(), kk.cuda(), vv.cuda()).cpu()[0, 0]
+    err = (out - vv[0, 0, 0]).abs().max().item()
+    log(f"  fixed point: |dense - v0|_inf = {err:.3e}")
+    assert err <= 1e-5
+
+
+def test_all_sinks_and_no_sinks():
+    wl = Workload("edges", 2, 16, 4, 128, 4000, "bf16", seed=41, sink_plan=("count", 2))
+    layer = make_layer(wl)
+    q, k, v = upload(layer)
+    k0, v0, r, out = run_routed(q, k, v, -2.0, launch("auto"))   # every cosine >= -2
+    assert int(r.n_active.cpu()[0]) == 0
+    assert torch.equal(out, v0.repeat_interleave(4, dim=1))
+    q_np, k_np, v_np = oracle_inputs(layer)
+    k0, v0, r, out = run_routed(q, k, v, 1.5, launch("auto"))    # nothing reaches 1.5
+    assert int(r.n_active.cpu()[0]) == 8
+    assert_outputs(out.cpu().numpy(), oracle.dense_decode(q_np, k_np, v_np), "tau 1.5")
+
+
+def test_strided_cache_views():
+    wl = Workload("strided", 2, 16, 4, 128, 3000, "bf16", seed=51, sink_plan=("count", 2))
+    layer = make_layer(wl)
+    B, Hkv, T, d = layer.k.shape
+    big_k = torch.zeros((B, Hkv, T + 333, d), dtype=layer.k.dtype)
+    big_v = torch.zeros_like(big_k)
+    big_k[:, :, :T] = layer.k
+    big_v[:, :, :T] = layer.v
+    big_k[:, :, T:] = 1e4   # poison: must never be read
+    big_v[:, :, T:] = float("nan")
+    k = big_k.cuda()[:, :, :T]
+    v = big_v.cuda()[:, :, :T]
+    q = layer.q.cuda()
+    k0, v0, r, out = run_routed(q, k, v, wl.tau, launch("auto"))
+    q_np, k_np, v_np = oracle_inputs(layer)
+    mask = r.mask.cpu().numpy()
+    ref = oracle.routed_decode(q_np, k_np, v_np, as_numpy(layer.v[:, :, 0]), mask)
+    assert_outputs(out.cpu().numpy(), ref, "strided routed")
+
+
+# --- full-size layers, sampled outputs ----------------------------------------
+def sampled_check(layer, q, k, v, lau, n_samples=2, seed=0):
+    wl = layer.wl
+    G = wl.group_size
+    k0, v0, r, out = run_routed(q, k, v, wl.tau, lau)
+    torch.cuda.synchronize()
+    q_np = as_numpy(layer.q)
+    k0_ref = as_numpy(layer.k[:, :, 0])
+    v0_ref = as_numpy(layer.v[:, :, 0])
+    mask, n_active = assert_route(r, q_np, k0_ref, wl.tau)
+    got = out.cpu().numpy()
+    n_sink = sink_rows_exact(got, v0_ref, mask, G)
+    act = [j for j in r.work_list.cpu().numpy()[:n_active]]
+    rng = np.random.default_rng(seed)
+    picks = sorted(set([act[0], act[-1]] + list(rng.choice(act, size=min(n_samples, len(act)),
+                                                           replace=False)))) if act else []
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    log(f"{wl.name}: n_active={n_active} sink_rows={n_sink} sampled items={picks}")
+    for j in picks:
+        b, g = divmod(int(j), wl.num_kv_heads)
+        ref = oracle.attend_group(q_np[b, g * G:(g + 1) * G], as_numpy(layer.k[b, g]),
+                                  as_numpy(layer.v[b, g]), scale)
+        assert_outputs(got[b, g * G:(g + 1) * G], ref, f"item {j}")
+    return r
+
+
+@pytest.mark.parametrize("wl", [L8B_128K, L8B_512K, L70B_128K_B8], ids=lambda w: w.name)
+@pytest.mark.parametrize("kernel", ["auto"])
+def test_full_size_layers_sampled(wl, kernel):
+    log(f"full-size {wl.name}")
+    layer = make_layer(wl)
+    q, k, v = upload(layer)
+    sampled_check(layer, q, k, v, launch(kernel))
+    # dense path on one sampled item
+    dense = sr.dense_decode(q, k, v, launch=launch(kernel)).cpu().numpy()
+    G = wl.group_size
+    b, g = wl.batch - 1, wl.num_kv_heads - 1
+    ref = oracle.attend_group(as_numpy(layer.q)[b, g * G:(g + 1) * G], as_numpy(layer.k[b, g]),
+                              as_numpy(layer.v[b, g]), 1.0 / math.sqrt(wl.head_dim))
+    assert_outputs(dense[b, g * G:(g + 1) * G], ref, "dense last item")
+
+
+def test_full_size_256k_b4_sink_fraction_sweep():
+    base = L8B_256K_B4
+    log(f"full-size {base.name} sweep")
+    k_cpu, v_cpu = make_caches(base)
+    k, v = k_cpu.cuda(), v_cpu.cuda()
+    for f in SINK_FRACTIONS:
+        wl = sweep(base, f)
+        q_cpu, planted = make_queries(wl)
+        from workloads import Layer
+        layer = Layer(wl, q_cpu, k_cpu, v_cpu, planted)
+        r = sampled_check(layer, q_cpu.cuda(), k, v, launch("auto"), n_samples=1, seed=int(f * 4))
+        assert int(r.n_active.cpu()[0]) == round((1 - f) * 8) * 4
