@@ -8,7 +8,8 @@ the in-kernel merge).  The default workload is the Llama-3.1-8B decode layer
 at 524288 cached positions (B=1, 32 query / 8 KV heads, d=128, bf16 K/V,
 4 of 8 KV groups planted as sinks), the shape the SinkRouter pages quote
 their 512K speedup on.  Two copies of the layer are rotated so nothing of a
-step's working set is still in the 256 MB Infinity Cache from the step before.
+step's working set is still in the 256 MB Infinity Cache from the step before
+(in general enough copies to rotate over at least 4 GiB).
 
 Prints ONE JSON line (the metric: effective HBM GB/s of the routed
 layer-step, with us per layer-step, the dense baseline and the speedup), plus
@@ -64,6 +65,57 @@ def traffic_record(kernel_name: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+COPY_BYTES = 256 << 20
+
+
+def _pmc_rows(path, counter):
+    """{dispatch id: (kernel name, value)} from a rocprofv3 counter_collection csv."""
+    import csv
+    rows = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            rows[int(r["Dispatch_Id"])] = (r["Kernel_Name"], float(r["Counter_Value"]))
+    return rows
+
+
+def summarize_counters(fetch_csv, write_csv):
+    """HBM bytes per decode launch = counter (KiB) x 1024 x (COPY_BYTES / the
+    same counter's reading on the plain COPY_BYTES copy that `--calibrate-copy`
+    runs first).  Both runs execute the same program, so dispatch ids match;
+    the calibration copy is the copy kernel writing COPY_BYTES."""
+    out = {}
+    fetch, write = _pmc_rows(fetch_csv, "FETCH_SIZE"), _pmc_rows(write_csv, "WRITE_SIZE")
+    target = COPY_BYTES / 1024.0
+    cal = min((d for d, (k, v) in write.items() if "copy" in k.lower()),
+              key=lambda d: abs(write[d][1] - target))
+    assert abs(write[cal][1] - target) < 0.01 * target, "calibration copy not found"
+    for counter, rows in (("FETCH_SIZE", fetch), ("WRITE_SIZE", write)):
+        copy_kib = rows[cal][1]
+        scale = COPY_BYTES / (copy_kib * 1024.0)
+        for kname in ("k_decode_valu", "k_decode_mfma", "k_route"):
+            vals = [v for k, v in rows.values() if kname in k]
+            if vals:
+                rec = out.setdefault(kname, {})
+                rec[counter] = {"kib_per_dispatch": sum(vals) / len(vals), "dispatches": len(vals),
+                                "copy_kib": copy_kib, "scale": scale,
+                                "bytes_per_dispatch": sum(vals) / len(vals) * 1024.0 * scale}
+    recs = {}
+    from workloads import L8B_512K
+    for kname, rec in out.items():
+        if "FETCH_SIZE" in rec and "WRITE_SIZE" in rec:
+            recs[f"{kname}@{L8B_512K.name}"] = {
+                "sources": decode_sources_digest(),
+                "hbm_bytes_per_launch": round(rec["FETCH_SIZE"]["bytes_per_dispatch"]
+                                              + rec["WRITE_SIZE"]["bytes_per_dispatch"]),
+                "fetch": rec["FETCH_SIZE"], "write": rec["WRITE_SIZE"]}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(recs, f, indent=1, sort_keys=True)
+    print(json.dumps(recs, indent=1))
+
+
 def algorithmic_bytes(wl, n_active: int) -> int:
     """KV bytes of the active groups + q/out + k0/v0 (per layer-step)."""
     es = 2 if wl.kv_dtype == "bf16" else 4
@@ -71,6 +123,51 @@ def algorithmic_bytes(wl, n_active: int) -> int:
     io = wl.batch * wl.num_q_heads * wl.head_dim * 4 * 2
     sink = wl.batch * wl.num_kv_heads * wl.head_dim * 4 * 2
     return kv + io + sink
+
+
+def time_launches(fn, steps, stream):
+    """Average duration of one launch: an event pair around every launch, so
+    the gaps between launches are not counted (comparable with a profiler's
+    per-kernel duration)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / steps  # ms
+
+
+def read_ceiling(tensors, stream, grids=(256, 512, 1024), unrolls=(4, 8)):
+    """Best read bandwidth of the library's streaming probe over the given
+    device tensors (16-byte loads per lane, the decode kernels' access width),
+    grid-strided and per-workgroup-blocked."""
+    import ctypes
+
+    import torch
+
+    from kv_cache_routing_amd import _native as N
+    sink = torch.zeros(max(grids), dtype=torch.int32, device=tensors[0].device)
+    total = sum(t.numel() * t.element_size() for t in tensors)
+    best, rows = 0.0, []
+    for blocked in (0, 1):
+        for grid in grids:
+            for un in unrolls:
+                def f(i):
+                    for t in tensors:
+                        N.check(N.lib.sr_stream_read(
+                            ctypes.c_void_p(t.data_ptr()), t.numel() * t.element_size(), grid, un,
+                            blocked, ctypes.c_void_p(sink.data_ptr()),
+                            ctypes.c_void_p(stream.cuda_stream)), "sr_stream_read")
+                f(0)
+                ms = time_loop(f, 5, stream)
+                gbs = total / (ms * 1e-3) / 1e9
+                rows.append({"blocked": blocked, "grid": grid, "unroll": un, "gbs": round(gbs, 1)})
+                best = max(best, gbs)
+    return best, rows
 
 
 def time_loop(fn, steps, stream):
@@ -102,28 +199,30 @@ def cpu_baseline(layer, n_active_items, budget_s=12.0):
     G = wl.group_size
     q = as_numpy(layer.q)
     scale = 1.0 / math.sqrt(wl.head_dim)
-    done, t_total, bytes_total = 0, 0.0, 0
+    slabs = {}
     for j in n_active_items:
         b, g = divmod(int(j), wl.num_kv_heads)
-        ks, vs = as_numpy(layer.k[b, g]), as_numpy(layer.v[b, g])
-        t0 = time.perf_counter()
-        oracle.attend_group(q[b, g * G:(g + 1) * G], ks, vs, scale)
-        t_total += time.perf_counter() - t0
-        bytes_total += 2 * wl.seq_len * wl.head_dim * 2
-        done += 1
-        if t_total >= budget_s:
-            break
+        slabs[j] = (q[b, g * G:(g + 1) * G], as_numpy(layer.k[b, g]), as_numpy(layer.v[b, g]))
+    done, t_total, bytes_total, passes = 0, 0.0, 0, 0
+    while t_total < budget_s:
+        for j in n_active_items:
+            t0 = time.perf_counter()
+            oracle.attend_group(*slabs[j], scale)
+            t_total += time.perf_counter() - t0
+            bytes_total += 2 * wl.seq_len * wl.head_dim * 2
+            done += 1
+        passes += 1
     t0 = time.perf_counter()
     oracle.route(q, as_numpy(layer.k[:, :, 0]), wl.tau)
     t_route = time.perf_counter() - t0
-    per_item = t_total / done
-    step_s = per_item * len(n_active_items) + t_route
+    step_s = t_total / passes + t_route
     return {
         "value": round(bytes_total / t_total / 1e9, 4), "unit": "GB/s", "cores": int(cores),
         "kind": "oracle",
-        "sample": (f"{done} of {len(n_active_items)} active KV groups of one "
-                   f"{wl.name} layer-step (fp64 numpy, {wl.seq_len} positions, G={G}), "
-                   f"{t_total:.1f} s; routed layer-step extrapolates to {step_s * 1e3:.0f} ms"),
+        "sample": (f"{passes} passes over the {len(n_active_items)} active KV groups of one "
+                   f"{wl.name} layer-step ({done} group attentions, fp64 numpy, "
+                   f"{wl.seq_len} positions, G={G}) in {t_total:.1f} s; one routed "
+                   f"layer-step takes {step_s * 1e3:.0f} ms"),
         "us_per_layer_step": round(step_s * 1e6, 1),
         "seconds": round(t_total, 2),
     }
@@ -133,12 +232,31 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--rotate", type=int, default=2, help="layer caches rotated over steps")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama8b-512k",
+                    help="llama8b-512k (default), llama8b-128k, llama8b-256k-b4-sink{0,25,50,75,100}, "
+                         "llama70b-128k-b8, tiny-4k-f32")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="layer copies rotated over steps (0 = enough for >= 4 GiB)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the sink-fraction sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip timing the decode kernel under each kernel variant")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="print the HBM read-probe sweep over the layer caches and exit")
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="only the routed decode launches of the roofline measurement "
+                         "(the command the committed rocprofv3 summaries profile)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help=f"run one plain {COPY_BYTES >> 20} MiB device copy first (counter scale)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --calibrate-copy` into profiles/traffic.json and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the decode path has no multi-GPU mode "
@@ -148,9 +266,19 @@ def main():
     import torch
 
     import kv_cache_routing_amd as sr
-    from workloads import L8B_512K, SINK_FRACTIONS, make_caches, make_queries, sweep
+    from workloads import (CONFIGS, L8B_256K_B4, SINK_FRACTIONS, make_caches, make_queries,
+                           sweep)
 
-    wl = L8B_512K
+    names = {w.name: w for w in CONFIGS}
+    names.update({sweep(L8B_256K_B4, f).name: sweep(L8B_256K_B4, f) for f in SINK_FRACTIONS})
+    if args.workload not in names:
+        print(f"unknown workload {args.workload}; choose from {sorted(names)}", flush=True)
+        return 2
+    wl = names[args.workload]
+    es = 2 if wl.kv_dtype == "bf16" else 4
+    layer_bytes = 2 * wl.batch * wl.num_kv_heads * wl.seq_len * wl.head_dim * es
+    if args.rotate <= 0:
+        args.rotate = max(1, min(8, -(-(4 << 30) // layer_bytes)))
     tau = float(os.environ.get("SR_TAU", wl.tau))
     kernel = os.environ.get("SR_KERNEL", "auto")
     lau = sr.make_launch(int(os.environ.get("SR_SPLITS", "0")), KERNEL_IDS[kernel],
@@ -158,6 +286,12 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
 
+    if args.calibrate_copy:  # a plain copy of known size, for the traffic counters
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     t0 = time.time()
     k_cpu, v_cpu = make_caches(wl)
     q_cpu, planted = make_queries(wl)
@@ -193,21 +327,61 @@ def main():
         k, v, _, _ = caches[i % R]
         sr.dense_decode(q, k, v, launch=lau, ws=ws, out=out)
 
+    kname = "k_decode_mfma" if (kernel == "mfma" or (kernel == "auto" and wl.group_size > 4)
+                                and wl.kv_dtype == "bf16") else "k_decode_valu"
+    alg = algorithmic_bytes(wl, n_active)
+    if args.read_ceiling:
+        best, rows = read_ceiling([t for c in caches for t in c[:2]], stream)
+        print(json.dumps({"read_ceiling_gbs": round(best, 1), "bytes": sum(
+            t.numel() * t.element_size() for c in caches for t in c[:2]), "sweep": rows}),
+            flush=True)
+        return 0
+    if args.roofline_only:
+        for i in range(args.warmup):
+            decode_only(i)
+        ms_decode = time_launches(decode_only, args.steps, stream)
+        dec_gbs = alg / (ms_decode * 1e-3) / 1e9
+        print(json.dumps({"roofline_only": True, "kernel": kname, "decode_kernel_us":
+                          round(ms_decode * 1e3, 2), "achieved_gbs": round(dec_gbs, 1),
+                          "algorithmic_bytes_per_launch": alg, "launches": args.steps}),
+              flush=True)
+        return 0
     for i in range(args.warmup):
         routed_step(i)
         dense_step(i)
     ms_routed = time_loop(routed_step, args.steps, stream)
-    ms_decode = time_loop(decode_only, args.steps, stream)
+    ms_decode = time_launches(decode_only, args.steps, stream)
     ms_dense = time_loop(dense_step, args.steps, stream)
 
-    alg = algorithmic_bytes(wl, n_active)
+    compare = {}
+    if not args.no_compare:
+        for name in ("valu", "mfma"):
+            lk = sr.make_launch(lau.num_splits, KERNEL_IDS[name], lau.wgs_per_cu)
+            wsk = sr.Workspace(shape, lk, dev)
+
+            def dk(i, lk=lk, wsk=wsk):
+                k, v, k0, v0 = caches[i % R]
+                r = routes[i % R]
+                sr.decode_attn(q, k, v, v0, r.work_list, r.n_active, launch=lk, ws=wsk, out=out)
+
+            def dd(i, lk=lk, wsk=wsk):
+                k, v, _, _ = caches[i % R]
+                sr.dense_decode(q, k, v, launch=lk, ws=wsk, out=out)
+            for i in range(args.warmup):
+                dk(i)
+                dd(i)
+            compare[name] = {"routed_decode_us": round(time_loop(dk, args.steps, stream) * 1e3, 2),
+                             "dense_decode_us": round(time_loop(dd, args.steps, stream) * 1e3, 2)}
+            log(f"kernel {name}: {compare[name]}")
+
     alg_dense = algorithmic_bytes(wl, wl.batch * wl.num_kv_heads)
     gbs = alg / (ms_routed * 1e-3) / 1e9
     dec_gbs = alg / (ms_decode * 1e-3) / 1e9
     dense_gbs = alg_dense / (ms_dense * 1e-3) / 1e9
     splits = sr.splits_for(shape, lau, n_active)
-    kname = "k_decode_mfma" if (kernel == "mfma") else "k_decode_valu"
     traffic = traffic_record(kname, wl.name)
+    ceiling, _ = read_ceiling([t for c in caches for t in c[:2]], stream, grids=(256, 512),
+                              unrolls=(8,))
 
     sweep_rows = []
     if not args.no_sweep:
@@ -229,7 +403,7 @@ def main():
             ms = time_loop(st, args.steps, stream)
             sweep_rows.append({"sink_fraction": f, "n_active": na, "us": round(ms * 1e3, 2),
                                "t_over_t_dense": round(ms / ms_dense, 4),
-                               "active_fraction": round(na / 8, 4),
+                               "active_fraction": round(na / (wl.batch * wl.num_kv_heads), 4),
                                "gbs": round(algorithmic_bytes(wl, na) / (ms * 1e-3) / 1e9, 1)})
             log(f"sweep f={f}: {ms * 1e3:.1f} us (n_active={na})")
 
@@ -241,6 +415,7 @@ def main():
 
     line = {
         "metric": "decode-attn µs/layer-step + effective HBM GB/s at 512K ctx bf16, vs dense path",
+        "workload": wl.name,
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -250,10 +425,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": wl.kv_dtype,
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: B={wl.batch} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} "
-                               f"d={wl.head_dim} T={wl.seq_len} bf16 K/V, 4/8 groups sink, tau={tau}",
+                               f"d={wl.head_dim} T={wl.seq_len} {wl.kv_dtype} K/V, "
+                               f"{wl.batch * wl.num_kv_heads - n_active}/{wl.batch * wl.num_kv_heads} "
+                               f"groups sink, tau={tau}",
                    "global_batch": wl.batch, "seq_len": wl.seq_len, "parallelism": "none (1 GPU)",
                    "rotated_layers": R},
         "us_per_layer_step": round(ms_routed * 1e3, 2),
@@ -267,9 +444,12 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": kname,
-                     "algorithmic_bytes_per_launch": alg},
+                     "algorithmic_bytes_per_launch": alg,
+                     "measured_read_ceiling_gbs": round(ceiling, 1),
+                     "frac_of_measured_ceiling": round(dec_gbs / ceiling, 4)},
         "cpu_baseline": cpu,
-        "sweep_512k": sweep_rows,
+        "sink_fraction_sweep": sweep_rows,
+        "kernel_compare": compare,
         "context": "pages report 2.03x decode speedup at 512K (hardware not stated)",
     }
     print(json.dumps(line), flush=True)

@@ -44,7 +44,7 @@
  *  standard attention path, as the README's routing-controls section does
  *  for shapes its kernel does not cover).  SR_ERR_HIP reports a failed launch.
  *
- *  Envelope: 1 <= G <= 16, d in {64, 128}, T >= 1, B*Hkv <= 2^20,
+ *  Envelope: 1 <= G <= 16, d in {64, 128}, T >= 1, B*Hkv <= 32768,
  *  T <= 2^31 - 1.
  */
 #ifndef SINKROUTE_H
@@ -68,7 +68,7 @@ typedef enum { SR_KV_BF16 = 0, SR_KV_F32 = 1 } sr_kv_dtype;
 
 /* Which decode kernel runs the active groups. */
 typedef enum {
-    SR_KERNEL_AUTO = 0,  /* MFMA for bf16 caches, VALU for fp32 caches */
+    SR_KERNEL_AUTO = 0,  /* MFMA for bf16 caches with G > 4, VALU otherwise */
     SR_KERNEL_VALU = 1,  /* vector-ALU dot products for QK and PV */
     SR_KERNEL_MFMA = 2   /* bf16 matrix cores for QK (bf16 caches only) */
 } sr_kernel;
@@ -88,16 +88,18 @@ typedef struct {
 
 /* Launch policy for the decode kernels.  A NULL pointer means all zeros. */
 typedef struct {
-    /* > 0: every item is split into exactly this many contiguous ranges of
-     *      ceil(T / num_splits) positions (ranges past T are empty).
+    /* > 0: every item is split into exactly this many parts: its positions
+     *      are dealt round-robin in chunks of 64 (or 128) positions, part s
+     *      taking chunks s, s + S, s + 2S, ... (a part with no chunk below T
+     *      is empty).
      *   0: adaptive: the grid is a fixed number of workgroups sized from the
      *      device's CU count, and the kernel splits each active item into
      *      (grid / n_active) ranges, read from the device-side n_active, so
      *      the GPU stays full at any sink fraction without a host sync. */
     int32_t num_splits;
     int32_t kernel;        /* sr_kernel */
-    int32_t wgs_per_cu;    /* adaptive grid size in workgroups per CU (0 = 2) */
-    int32_t reserved;      /* must be 0 */
+    int32_t wgs_per_cu;    /* adaptive grid size in workgroups per CU (0 = 1) */
+    int32_t waves_per_wg;  /* 4 or 8 wave64s per workgroup (0 = 4) */
 } sr_launch;
 
 /* Prefill side (README decode-time steps: the prefill path keeps the key at
@@ -165,6 +167,18 @@ int32_t sr_splits_for(const sr_shape* shape, const sr_launch* launch, int32_t n_
 int32_t sr_grid_size(const sr_shape* shape, const sr_launch* launch);
 
 const char* sr_status_string(sr_status status);
+
+/* Measurement helper, not part of the decode path: streams `bytes` (rounded
+ * down to 16) of device memory with 16-byte loads per lane (the decode
+ * kernels' access width) on `grid` workgroups of 256 threads, `unroll` loads
+ * in flight per thread (1, 2, 4, 8 or 16), so a benchmark can measure the
+ * achievable HBM read bandwidth.  blocked = 0: the grid walks the buffer
+ * together; blocked = 1: each workgroup streams its own contiguous slice.
+ * `sink` (>= grid u32, device) is written only in the practically impossible
+ * case that a workgroup's XOR of the data is 0x9e3779b9; it exists so no load
+ * can be optimised away. */
+sr_status sr_stream_read(const void* buf, size_t bytes, int32_t grid, int32_t unroll,
+                         int32_t blocked, uint32_t* sink, void* stream);
 
 /* Library version, e.g. 100 for 0.1.0. */
 int32_t sr_version(void);

@@ -60,8 +60,9 @@ def make_shape(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None = None) 
     return N.SrShape(B, Hq, Hkv, d, T, k.stride(0), k.stride(1), k.stride(2), dt, 0)
 
 
-def make_launch(num_splits: int = 0, kernel: int = SR_KERNEL_AUTO, wgs_per_cu: int = 0):
-    return N.SrLaunch(num_splits, kernel, wgs_per_cu, 0)
+def make_launch(num_splits: int = 0, kernel: int = SR_KERNEL_AUTO, wgs_per_cu: int = 0,
+                waves_per_wg: int = 0):
+    return N.SrLaunch(num_splits, kernel, wgs_per_cu, waves_per_wg)
 
 
 def splits_for(shape: N.SrShape, launch: N.SrLaunch | None, n_active: int) -> int:

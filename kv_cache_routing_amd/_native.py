@@ -19,7 +19,7 @@ SR_KERNEL_AUTO, SR_KERNEL_VALU, SR_KERNEL_MFMA = 0, 1, 2
 EXPORTS = (
     "sr_record_sink", "sr_route", "sr_workspace_bytes", "sr_workspace_init",
     "sr_decode_attn", "sr_dense_decode", "sr_splits_for", "sr_grid_size",
-    "sr_status_string", "sr_version",
+    "sr_status_string", "sr_version", "sr_stream_read",
 )
 
 
@@ -36,7 +36,7 @@ class SrShape(ctypes.Structure):
 class SrLaunch(ctypes.Structure):
     _fields_ = [
         ("num_splits", ctypes.c_int32), ("kernel", ctypes.c_int32),
-        ("wgs_per_cu", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("wgs_per_cu", ctypes.c_int32), ("waves_per_wg", ctypes.c_int32),
     ]
 
 
@@ -49,7 +49,7 @@ class SinkRouteError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m kv_cache_routing_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python kv_cache_routing_amd/build.py` "
             "(or __graft_entry__.build())")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
@@ -67,6 +67,7 @@ def _load():
         "sr_grid_size": (i32, [S, Lp]),
         "sr_status_string": (ctypes.c_char_p, [i32]),
         "sr_version": (i32, []),
+        "sr_stream_read": (i32, [P, sz, i32, i32, i32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -1,6 +1,6 @@
 """Build libsinkroute.so in-tree for gfx950 with hipcc.
 
-    python -m kv_cache_routing_amd.build        # or __graft_entry__.build()
+    python kv_cache_routing_amd/build.py        # or __graft_entry__.build()
 
 Every HIP source under csrc/ is compiled to an object and linked into
 kv_cache_routing_amd/libsinkroute.so.  Always rebuilds.

@@ -55,15 +55,22 @@ sr_status check_caches(const sr_shape& s, const void* k, const void* v) {
 }
 
 struct Plan {
-    int32_t fixed_splits, grid, split_cap, gp, kernel;
+    int32_t fixed_splits, grid, split_cap, gp, kernel, waves;
 };
 
 sr_status make_plan(const sr_shape& s, const sr_launch* launch, Plan& p) {
     sr_launch l{};
     if (launch) l = *launch;
-    if (l.reserved != 0 || l.num_splits < 0 || l.wgs_per_cu < 0) return SR_ERR_INVALID_ARG;
+    if (l.num_splits < 0 || l.wgs_per_cu < 0) return SR_ERR_INVALID_ARG;
+    if (l.waves_per_wg != 0 && l.waves_per_wg != 4 && l.waves_per_wg != 8) return SR_ERR_INVALID_ARG;
+    p.waves = l.waves_per_wg ? l.waves_per_wg : kDefaultWaves;
     if (l.kernel < SR_KERNEL_AUTO || l.kernel > SR_KERNEL_MFMA) return SR_ERR_INVALID_ARG;
-    p.kernel = l.kernel == SR_KERNEL_AUTO ? SR_KERNEL_VALU : l.kernel;
+    // Measured on MI355X: at G <= 4 the vector-ALU kernel streams as fast as
+    // the matrix-core one (both HBM-bound); from G = 5 up the ALU work of QK
+    // outgrows the memory time and the MFMA kernel is ahead (1.8x at G = 8).
+    const int32_t G = s.num_q_heads / s.num_kv_heads;
+    p.kernel = l.kernel != SR_KERNEL_AUTO ? l.kernel
+               : (s.kv_dtype == SR_KV_BF16 && G > 4 ? SR_KERNEL_MFMA : SR_KERNEL_VALU);
     if (p.kernel == SR_KERNEL_MFMA && s.kv_dtype != SR_KV_BF16) return SR_ERR_UNSUPPORTED;
     const int64_t n_items = static_cast<int64_t>(s.batch) * s.num_kv_heads;
     p.gp = pad_group(s.num_q_heads / s.num_kv_heads);
@@ -75,7 +82,7 @@ sr_status make_plan(const sr_shape& s, const sr_launch* launch, Plan& p) {
         p.grid = static_cast<int32_t>(grid);
         p.split_cap = l.num_splits;
     } else {
-        const int32_t per_cu = l.wgs_per_cu > 0 ? l.wgs_per_cu : 2;
+        const int32_t per_cu = l.wgs_per_cu > 0 ? l.wgs_per_cu : kDefaultWgsPerCu;
         int64_t grid = static_cast<int64_t>(per_cu) * cu_count();
         if (grid < n_items) grid = n_items;
         if (grid > INT32_MAX) return SR_ERR_UNSUPPORTED;
@@ -146,8 +153,8 @@ sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float
     a.routed = routed ? 1 : 0;
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    hipError_t e = p.kernel == SR_KERNEL_MFMA ? launch_decode_mfma(s, a, p.gp, hs)
-                                               : launch_decode_valu(s, a, p.gp, hs);
+    hipError_t e = p.kernel == SR_KERNEL_MFMA ? launch_decode_mfma(s, a, p.gp, p.waves, hs)
+                                               : launch_decode_valu(s, a, p.gp, p.waves, hs);
     return e == hipSuccess ? SR_OK : SR_ERR_HIP;
 }
 
@@ -230,6 +237,17 @@ const char* sr_status_string(sr_status status) {
         case SR_ERR_HIP: return "HIP error";
         default: return "unknown status";
     }
+}
+
+sr_status sr_stream_read(const void* buf, size_t bytes, int32_t grid, int32_t unroll,
+                         int32_t blocked, uint32_t* sink, void* stream) {
+    if (!buf || !sink || !aligned16(buf) || bytes < 16 || grid < 1) return SR_ERR_INVALID_ARG;
+    if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8 && unroll != 16)
+        return SR_ERR_INVALID_ARG;
+    if (blocked != 0 && blocked != 1) return SR_ERR_INVALID_ARG;
+    hipError_t e = launch_stream_read(buf, bytes, grid, unroll, blocked, sink,
+                                      static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SR_OK : SR_ERR_HIP;
 }
 
 int32_t sr_version(void) { return 100; }

@@ -56,16 +56,23 @@ __device__ inline float wave_max(float x) {
 }
 
 // What one workgroup owns: split `split` of the item at work-list slot `slot`.
+// The item's positions are dealt to its S splits round-robin in chunks of
+// CHUNK positions: split s takes chunks s, s + S, s + 2S, ...  So at any
+// moment all workgroups of an item stream one window of the cache together
+// (DRAM pages stay open) instead of S distant ranges.
 struct WorkUnit {
     int32_t slot, split, splits, b, g;
-    int64_t t0, t1;  // positions [t0, t1) of the item's cache
+    int64_t first;   // first position of this split's first chunk
+    int64_t stride;  // positions between this split's consecutive chunks (S * CHUNK)
+    int64_t t1;      // positions [0, t1) exist (t1 = T)
 };
 
 // Sink duty, then the work mapping.  Workgroup w first copies v0 into the G
 // output rows of the sink at list position n_active + w (if there is one);
 // then it takes split (w mod S) of active slot (w / S), S = splits per item.
+// A split with no chunk below T (S * CHUNK > T) is empty and still merges.
 // Returns false when the workgroup has no split to compute.
-template <int D, int NT>
+template <int D, int NT, int CHUNK>
 __device__ inline bool map_work(const DecodeArgs& a, WorkUnit& u) {
     const int32_t n_items = a.batch * a.num_kv_heads;
     const int32_t n_act = a.routed ? *a.n_active : n_items;
@@ -92,12 +99,125 @@ __device__ inline bool map_work(const DecodeArgs& a, WorkUnit& u) {
     const int32_t item = a.routed ? a.work_list[slot] : slot;
     u.b = item / a.num_kv_heads;
     u.g = item - u.b * a.num_kv_heads;
-    const int64_t L = split_len(a.seq_len, S);
-    u.t0 = static_cast<int64_t>(u.split) * L;
-    const int64_t e = u.t0 + L;
-    u.t1 = e < a.seq_len ? e : a.seq_len;
-    if (u.t0 > u.t1) u.t0 = u.t1;  // empty split
+    u.first = static_cast<int64_t>(u.split) * CHUNK;
+    u.stride = static_cast<int64_t>(S) * CHUNK;
+    u.t1 = a.seq_len;
     return true;
+}
+
+// Last-arriver merge of the S split partials of one item (all threads of the
+// workgroup).  Every global load of the merge is independent of the others,
+// so they are issued in unrolled batches: the merge costs a few memory round
+// trips, not one per split.  Order is fixed: maxima, then per split weights
+// w_s = exp2(m_s - M) into LDS, then the weighted accumulators.  When a
+// partial has fewer float4 slots than the workgroup has threads, GROUPS
+// thread groups take splits s = gi, gi + GROUPS, ... each in ascending order
+// and the group sums are added in ascending gi: results are bitwise
+// reproducible for a given split count.
+template <int D, int GP, int NW>
+__device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, float* out_item) {
+    constexpr int NT = NW * 64;
+    constexpr int NV = GP * D / 4;                 // float4 slots per partial
+    constexpr int GROUPS = NV >= NT ? 1 : NT / NV;
+    constexpr int SLOTS = NV >= NT ? NV / NT : 1;  // float4 slots per thread
+    constexpr int CH = 1024 / GP;                  // splits per weight chunk
+    static_assert(NT % GP == 0 && NV % (NV >= NT ? NT : NV) == 0, "merge layout");
+    __shared__ float s_red[NW][GP];
+    __shared__ float s_M[GP], s_L[GP];
+    __shared__ float s_w[CH][GP];
+    __shared__ float s_lw[CH][GP];
+    __shared__ float4 s_grp[GROUPS][GROUPS > 1 ? NV : 1];
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int32_t G = a.group;
+    const int32_t S = u.splits;
+    const float* ml0 = a.part_ml + static_cast<int64_t>(u.slot) * S * 2 * GP;
+    const float4* acc0 =
+        reinterpret_cast<const float4*>(a.part_acc + static_cast<int64_t>(u.slot) * S * GP * D);
+
+    {  // M[h]: thread t only ever reads head t % GP
+        const int h = t % GP;
+        float mx = kNegInf;
+#pragma unroll 8
+        for (int s = t / GP; s < S; s += NT / GP)
+            mx = fmaxf(mx, ml0[static_cast<int64_t>(s) * 2 * GP + h]);
+        for (int o = GP; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        if (lane < GP) s_red[wave][lane] = mx;
+        __syncthreads();
+        if (t < GP) {
+            float M = kNegInf;
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, s_red[w][t]);
+            s_M[t] = M;
+        }
+        __syncthreads();
+    }
+
+    const int gi = GROUPS > 1 ? t / NV : 0;
+    const int v0 = GROUPS > 1 ? t % NV : t;
+    float4 acc[SLOTS];
+#pragma unroll
+    for (int k = 0; k < SLOTS; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lsum = 0.f;
+    for (int c0 = 0; c0 < S; c0 += CH) {
+        const int n = S - c0 < CH ? S - c0 : CH;
+        for (int x = t; x < n * GP; x += NT) {
+            const int s = x / GP, h = x - (x / GP) * GP;
+            const float* p = ml0 + static_cast<int64_t>(c0 + s) * 2 * GP;
+            const float w = merge_weight(p[h], s_M[h]);
+            s_w[s][h] = w;
+            s_lw[s][h] = w * p[GP + h];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < SLOTS; ++k) {
+            const int v = v0 + k * NT;
+            const int h = (4 * v) / D;
+            const float4* src = acc0 + static_cast<int64_t>(c0) * NV + v;
+            float4 r = acc[k];
+#pragma unroll 16
+            for (int s = gi; s < n; s += GROUPS) {
+                const float4 x = src[static_cast<int64_t>(s) * NV];
+                const float w = s_w[s][h];
+                r.x += w * x.x;
+                r.y += w * x.y;
+                r.z += w * x.z;
+                r.w += w * x.w;
+            }
+            acc[k] = r;
+        }
+        if (t < GP)
+            for (int s = 0; s < n; ++s) lsum += s_lw[s][t];
+        __syncthreads();
+    }
+    if (t < GP) s_L[t] = lsum;
+    if constexpr (GROUPS > 1) s_grp[gi][v0] = acc[0];
+    __syncthreads();
+    if constexpr (GROUPS > 1) {
+        if (gi == 0 && 4 * v0 < G * D) {
+            float4 r = s_grp[0][v0];
+            for (int g = 1; g < GROUPS; ++g) {
+                const float4 x = s_grp[g][v0];
+                r.x += x.x;
+                r.y += x.y;
+                r.z += x.z;
+                r.w += x.w;
+            }
+            const float L = s_L[(4 * v0) / D];
+            *reinterpret_cast<float4*>(out_item + 4 * v0) =
+                make_float4(r.x / L, r.y / L, r.z / L, r.w / L);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < SLOTS; ++k) {
+            const int v = v0 + k * NT;
+            if (4 * v < G * D) {
+                const float L = s_L[(4 * v) / D];
+                const float4 r = acc[k];
+                *reinterpret_cast<float4*>(out_item + 4 * v) =
+                    make_float4(r.x / L, r.y / L, r.z / L, r.w / L);
+            }
+        }
+    }
 }
 
 // Merge the per-wave states held in LDS (s_m/s_l [NW][GP], s_acc [NW][GP][D])
@@ -150,67 +270,26 @@ __device__ inline void finish_split(const DecodeArgs& a, const WorkUnit& u,
         }
     }
 
+    // Publish the partial and take a ticket.  Every wave releases its own
+    // stores at agent scope (an L2 write-back, so the other XCDs see them)
+    // before the barrier; thread 0 then moves the ticket.  Only the workgroup
+    // that draws the last ticket pays for an acquire (an L2 invalidation): a
+    // sequentially consistent fence in every workgroup would invalidate this
+    // XCD's L2 under the other workgroups' streaming loads.
     __shared__ int s_last;
-    __threadfence();  // release this workgroup's partial at agent scope
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     if (threadIdx.x == 0) {
-        const uint32_t prev = atomicAdd(a.tickets + u.slot, 1u);
-        s_last = prev == static_cast<uint32_t>(u.splits - 1);
+        const uint32_t prev = __hip_atomic_fetch_add(a.tickets + u.slot, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = prev == static_cast<uint32_t>(u.splits - 1);
+        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        s_last = last;
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();  // acquire the other workgroups' partials
 
-    constexpr int CH = 64;
-    __shared__ float s_M[GP], s_L[GP];
-    __shared__ float s_w[CH][GP];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int32_t S = u.splits;
-    const float* ml0 = a.part_ml + static_cast<int64_t>(u.slot) * S * 2 * GP;
-    const float* acc0 = a.part_acc + static_cast<int64_t>(u.slot) * S * GP * D;
-
-    for (int h = wave; h < GP; h += NW) {
-        float M = kNegInf;
-        for (int s = lane; s < S; s += 64) M = fmaxf(M, ml0[static_cast<int64_t>(s) * 2 * GP + h]);
-        M = wave_max(M);
-        if (lane == 0) s_M[h] = M;
-    }
-    constexpr int PER = (GP * D + NT - 1) / NT;
-    float A[PER];
-    for (int k = 0; k < PER; ++k) A[k] = 0.f;
-    float Lh = 0.f;
-    __syncthreads();
-    for (int c0 = 0; c0 < S; c0 += CH) {
-        const int n = S - c0 < CH ? S - c0 : CH;
-        for (int x = threadIdx.x; x < CH * GP; x += NT) {
-            const int k = x / GP, h = x - (x / GP) * GP;
-            s_w[k][h] = k < n ? merge_weight(ml0[static_cast<int64_t>(c0 + k) * 2 * GP + h], s_M[h])
-                              : 0.f;
-        }
-        __syncthreads();
-        for (int k = 0; k < PER; ++k) {
-            const int x = threadIdx.x + k * NT;
-            if (x < GP * D) {
-                const int h = x / D;
-                const float* p = acc0 + static_cast<int64_t>(c0) * GP * D + x;
-                float acc = A[k];
-                for (int s = 0; s < n; ++s) acc += s_w[s][h] * p[static_cast<int64_t>(s) * GP * D];
-                A[k] = acc;
-            }
-        }
-        if (threadIdx.x < GP) {
-            const int h = threadIdx.x;
-            const float* p = ml0 + static_cast<int64_t>(c0) * 2 * GP + GP + h;
-            for (int s = 0; s < n; ++s) Lh += s_w[s][h] * p[static_cast<int64_t>(s) * 2 * GP];
-        }
-        __syncthreads();
-    }
-    if (threadIdx.x < GP) s_L[threadIdx.x] = Lh;
-    __syncthreads();
-    for (int k = 0; k < PER; ++k) {
-        const int x = threadIdx.x + k * NT;
-        if (x < G * D) out_item[x] = A[k] / s_L[x / D];
-    }
+    merge_splits<D, GP, NW>(a, u, out_item);
     if (threadIdx.x == 0) a.tickets[u.slot] = 0u;  // ready for the next call
 }
 

@@ -1,10 +1,269 @@
-// Placeholder until the matrix-core decode kernel lands.
+// Split-K flash-decode of the active groups with QK on the bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16) and PV on the vector ALUs.  bf16 caches only.
+//
+// QK as a 16x16 tile product per 16 cache rows: A = the G query heads padded
+// to 16 rows, B = 16 key rows (column = row of the cache), fp32 result
+// S[head][position].  Lane l feeds key row (l mod 16) with the 8 bf16 at
+// d = 32*kb + 8*(l/16) of k-block kb, so each load instruction takes 64
+// contiguous bytes of 16 rows.  The query is pre-scaled by sm_scale*log2(e)
+// and split exactly enough into hi + lo bf16 terms (two MFMAs per k-block):
+// products with the stored bf16 keys are exact and the logits carry ~2^-16
+// relative error in the query.
+//
+// Softmax in the MFMA output layout: lane l holds heads 4*(l/16)..+3 of
+// position (l mod 16), so the running maximum of a head is uniform across a
+// 16-lane row and is only recomputed (DPP row max) when some logit exceeds it.
+// The probabilities go through LDS to the PV layout, where lane l owns 8
+// consecutive elements of one value row (16 B, coalesced 1 KiB per wave
+// instruction) and accumulates p * V in fp32 for the group's heads.
+//
+// Method: SinkRouter README (github.com/streamer-AP/SinkRouter), decode-time
+// steps (tiled QK/PV with an online softmax, Split-K, in-kernel merge);
+// result defined by Eq. (1) of the paper (pith.science, Figure 1 caption).
 #include "decode_common.h"
 
 namespace sr {
+namespace {
 
-hipError_t launch_decode_mfma(const sr_shape&, const DecodeArgs&, int, hipStream_t) {
-    return hipErrorNotSupported;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+__device__ inline uint32_t bf16_rne_bits(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ inline float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ inline bf16x8 load_bf16x8(const uint16_t* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+__device__ inline float readlane_f(float x, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
+template <int D, int GP, int NW>
+__global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
+    constexpr int KB = D / 32;        // k-blocks of the QK product
+    constexpr int LPT = D / 8;        // PV: lanes per value row
+    constexpr int TPI = 64 / LPT;     // PV: rows per load instruction
+    constexpr int UPS = 16 / TPI;     // PV: load instructions per 16 rows
+    static_assert(GP <= 16, "at most 16 heads per group");
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;      // MFMA layout
+    const int prow = lane / LPT, pchunk = lane % LPT;  // PV layout
+
+    __shared__ __attribute__((aligned(16))) float s_p[NW][16][16];  // [pos][head]
+    __shared__ float s_m[NW][GP], s_l[NW][GP];
+    __shared__ float s_acc[NW][GP][D];
+
+    WorkUnit u;
+    if (!map_work<D, NW * 64, NW * 16>(a, u)) return;
+    const int32_t G = a.group;
+
+    // A operands: query row = col, elements d = 32*kb + 8*grp + e
+    bf16x8 qhi[KB], qlo[KB];
+    {
+        const float* qr = a.q + (static_cast<int64_t>(u.b) * a.num_q_heads +
+                                 static_cast<int64_t>(u.g) * G + col) * D;
+        const bool real = col < G;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                float x0 = real ? qr[32 * kb + 8 * grp + e] * a.qscale : 0.f;
+                float x1 = real ? qr[32 * kb + 8 * grp + e + 1] * a.qscale : 0.f;
+                const uint32_t h0 = bf16_rne_bits(x0), h1 = bf16_rne_bits(x1);
+                const uint32_t l0 = bf16_rne_bits(x0 - bf16_bits_to_float(h0));
+                const uint32_t l1 = bf16_rne_bits(x1 - bf16_bits_to_float(h1));
+                hw[e / 2] = h0 | (h1 << 16);
+                lw[e / 2] = l0 | (l1 << 16);
+            }
+            qhi[kb] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+            qlo[kb] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        }
+    }
+
+    const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + u.b * a.stride_b + u.g * a.stride_h;
+    const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + u.b * a.stride_b + u.g * a.stride_h;
+    const int64_t st = a.stride_t;
+
+    float m[4], lsum[4];  // heads 4*grp + i, uniform across the 16-lane row
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        m[i] = kNegInf;
+        lsum[i] = 0.f;
+    }
+    float acc[GP][8];
+#pragma unroll
+    for (int h = 0; h < GP; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+
+    // One 16-position tile: the raw key and value bytes this lane loads.
+    struct Raw {
+        uint4 k[KB];
+        uint4 v[UPS];
+    };
+    const int64_t last = u.t1 - 1;
+    // Positions past T are clamped to the last row: every lane then reads the
+    // same row, so a prefetch past the end costs one row and no branch.
+    auto issue = [&](Raw& r, int64_t tile) {
+        int64_t tk = tile + col;
+        tk = tk < u.t1 ? tk : last;
+        const uint16_t* kp = kbase + tk * st + 8 * grp;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) r.k[kb] = *reinterpret_cast<const uint4*>(kp + 32 * kb);
+#pragma unroll
+        for (int uu = 0; uu < UPS; ++uu) {
+            int64_t tv = tile + prow + TPI * uu;
+            tv = tv < u.t1 ? tv : last;
+            r.v[uu] = *reinterpret_cast<const uint4*>(vbase + tv * st + pchunk * 8);
+        }
+    };
+    auto compute = [&](const Raw& r, int64_t tile) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const bf16x8 kv = __builtin_bit_cast(bf16x8, r.k[kb]);
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi[kb], kv, s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qlo[kb], kv, s, 0, 0, 0);
+        }
+        if (tile + col >= u.t1) {  // ragged tail: positions past T weigh nothing
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[i] = kNegInf;
+        }
+        bool up = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) up = up || (s[i] > m[i]);
+        if (__any(up)) {
+            float alpha[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float mx = group_allreduce_max<16>(s[i]);
+                const float mn = fmaxf(m[i], mx);
+                alpha[i] = mn > m[i] ? fast_exp2(m[i] - mn) : 1.f;
+                m[i] = mn;
+                lsum[i] *= alpha[i];
+            }
+#pragma unroll
+            for (int h = 0; h < GP; ++h) {
+                const float al = readlane_f(alpha[h & 3], 16 * (h >> 2));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] *= al;
+            }
+        }
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[i] = s[i] == kNegInf ? 0.f : fast_exp2(s[i] - m[i]);
+            lsum[i] += p[i];
+        }
+        *reinterpret_cast<float4*>(&s_p[wave][col][4 * grp]) = make_float4(p[0], p[1], p[2], p[3]);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int uu = 0; uu < UPS; ++uu) {
+            const int pos = prow + TPI * uu;
+            float pr[GP];
+            if constexpr (GP >= 4) {
+#pragma unroll
+                for (int h4 = 0; h4 < GP; h4 += 4) {
+                    const float4 x = *reinterpret_cast<const float4*>(&s_p[wave][pos][h4]);
+                    pr[h4] = x.x;
+                    pr[h4 + 1] = x.y;
+                    pr[h4 + 2] = x.z;
+                    pr[h4 + 3] = x.w;
+                }
+            } else {
+#pragma unroll
+                for (int h = 0; h < GP; ++h) pr[h] = s_p[wave][pos][h];
+            }
+            const uint32_t w4[4] = {r.v[uu].x, r.v[uu].y, r.v[uu].z, r.v[uu].w};
+            float vf[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                vf[2 * i] = __uint_as_float(w4[i] << 16);
+                vf[2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u);
+            }
+#pragma unroll
+            for (int h = 0; h < GP; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] += pr[h] * vf[e];
+        }
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    // Two-stage register pipeline: the next tile's loads are in flight while
+    // the current tile is computed.
+    const int64_t step = u.stride;
+    Raw ra, rb;
+    int64_t tile = u.first + static_cast<int64_t>(wave) * 16;
+    if (tile < u.t1) issue(ra, tile);
+    for (; tile < u.t1; tile += 2 * step) {
+        issue(rb, tile + step);
+        compute(ra, tile);
+        if (tile + step >= u.t1) break;
+        issue(ra, tile + 2 * step);
+        compute(rb, tile + step);
+    }
+
+    // wave totals: sums over the 16 positions of a row, values over PV rows
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lsum[i] = group_allreduce_sum<16>(lsum[i]);
+#pragma unroll
+    for (int o = LPT; o < 64; o <<= 1)
+#pragma unroll
+        for (int h = 0; h < GP; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], o);
+    if (prow == 0) {
+#pragma unroll
+        for (int h = 0; h < GP; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s_acc[wave][h][pchunk * 8 + e] = acc[h][e];
+    }
+    if (col == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = 4 * grp + i;
+            if (h < GP) {
+                s_m[wave][h] = m[i];
+                s_l[wave][h] = lsum[i];
+            }
+        }
+    }
+    __syncthreads();
+    finish_split<D, GP, NW>(a, u, s_m, s_l, s_acc);
+}
+
+template <int D, int GP, int NW>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL((k_decode_mfma<D, GP, NW>), dim3(a.grid), dim3(NW * 64), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int D, int NW>
+hipError_t launch_g(const DecodeArgs& a, int gp, hipStream_t st) {
+    switch (gp) {
+        case 1: return launch_t<D, 1, NW>(a, st);
+        case 2: return launch_t<D, 2, NW>(a, st);
+        case 4: return launch_t<D, 4, NW>(a, st);
+        case 8: return launch_t<D, 8, NW>(a, st);
+        case 16: return launch_t<D, 16, NW>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const sr_shape& s, const DecodeArgs& a, int gp, int waves,
+                              hipStream_t st) {
+    if (s.kv_dtype != SR_KV_BF16) return hipErrorInvalidValue;
+    if (waves == 8) return s.head_dim == 128 ? launch_g<128, 8>(a, gp, st) : launch_g<64, 8>(a, gp, st);
+    return s.head_dim == 128 ? launch_g<128, 4>(a, gp, st) : launch_g<64, 4>(a, gp, st);
 }
 
 }  // namespace sr

@@ -22,10 +22,9 @@ template <typename KV>
 struct Row8;
 
 template <>
-struct Row8<uint16_t> {  // bf16 bits
-    __device__ static inline void load(const uint16_t* p, float (&x)[8]) {
-        const uint4 r = *reinterpret_cast<const uint4*>(p);
-        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+struct Row8<uint16_t> {  // 8 bf16 in one 16-byte load
+    __device__ static inline void unpack(const uint4 (&r)[1], float (&x)[8]) {
+        const uint32_t w[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             x[2 * i] = __uint_as_float(w[i] << 16);
@@ -35,12 +34,11 @@ struct Row8<uint16_t> {  // bf16 bits
 };
 
 template <>
-struct Row8<float> {
-    __device__ static inline void load(const float* p, float (&x)[8]) {
-        const float4 a = *reinterpret_cast<const float4*>(p);
-        const float4 b = *reinterpret_cast<const float4*>(p + 4);
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+struct Row8<float> {  // 8 fp32 in two 16-byte loads
+    __device__ static inline void unpack(const uint4 (&r)[2], float (&x)[8]) {
+        const uint32_t w[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = __uint_as_float(w[i]);
     }
 };
 
@@ -54,7 +52,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
     __shared__ float s_acc[NW][GP][D];
 
     WorkUnit u;
-    if (!map_work<D, NW * 64>(a, u)) return;
+    if (!map_work<D, NW * 64, NW * TILE>(a, u)) return;
     const int32_t G = a.group;
 
     float qs[GP][E];
@@ -90,29 +88,43 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
         for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
     }
 
+    // One tile of TILE rows: the raw 8-element slices this lane loads.
+    constexpr int W = sizeof(KV) * E / 16;  // 16-byte loads per 8-element slice
+    struct Raw {
+        uint4 k[U][W];
+        uint4 v[U][W];
+    };
     const int64_t last = u.t1 - 1;
-    for (int64_t tile = u.t0 + static_cast<int64_t>(wave) * TILE; tile < u.t1;
-         tile += static_cast<int64_t>(NW) * TILE) {
-        float kf[U][E], vf[U][E];
-        bool valid[U];
+    // Rows past T are clamped to the last row: every lane then reads the same
+    // row, so a prefetch past the end costs one row and no branch.
+    auto issue = [&](Raw& r, int64_t tile) {
 #pragma unroll
         for (int v = 0; v < U; ++v) {
-            const int64_t t = tile + v * TPI + row;
-            valid[v] = t < u.t1;
-            const int64_t tl = valid[v] ? t : last;  // clamped: always a real row
-            Row8<KV>::load(kb + tl * st, kf[v]);
-            Row8<KV>::load(vb + tl * st, vf[v]);
+            int64_t t = tile + v * TPI + row;
+            t = t < u.t1 ? t : last;
+            const uint4* kp = reinterpret_cast<const uint4*>(kb + t * st);
+            const uint4* vp = reinterpret_cast<const uint4*>(vb + t * st);
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                r.k[v][w] = kp[w];
+                r.v[v][w] = vp[w];
+            }
         }
+    };
+    auto compute = [&](const Raw& r, int64_t tile) {
         float z[U][GP];
 #pragma unroll
         for (int v = 0; v < U; ++v) {
+            float kf[E];
+            Row8<KV>::unpack(r.k[v], kf);
+            const bool valid = tile + v * TPI + row < u.t1;
 #pragma unroll
             for (int h = 0; h < GP; ++h) {
                 float s = 0.f;
 #pragma unroll
-                for (int e = 0; e < E; ++e) s += qs[h][e] * kf[v][e];
+                for (int e = 0; e < E; ++e) s += qs[h][e] * kf[e];
                 s = group_allreduce_sum<LPT>(s);
-                z[v][h] = valid[v] ? s : kNegInf;
+                z[v][h] = valid ? s : kNegInf;
             }
         }
         bool up = false;
@@ -137,14 +149,30 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
         }
 #pragma unroll
         for (int v = 0; v < U; ++v) {
+            float vf[E];
+            Row8<KV>::unpack(r.v[v], vf);
 #pragma unroll
             for (int h = 0; h < GP; ++h) {
-                const float p = valid[v] ? fast_exp2(z[v][h] - m[h]) : 0.f;
+                const float p = z[v][h] == kNegInf ? 0.f : fast_exp2(z[v][h] - m[h]);
                 l[h] += p;
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[h][e] += p * vf[v][e];
+                for (int e = 0; e < E; ++e) acc[h][e] += p * vf[e];
             }
         }
+    };
+
+    // Two-stage register pipeline: the next tile's loads are in flight while
+    // the current tile is computed.
+    const int64_t step = u.stride;
+    Raw ra, rb;
+    int64_t tile = u.first + static_cast<int64_t>(wave) * TILE;
+    if (tile < u.t1) issue(ra, tile);
+    for (; tile < u.t1; tile += 2 * step) {
+        issue(rb, tile + step);
+        compute(ra, tile);
+        if (tile + step >= u.t1) break;
+        issue(ra, tile + 2 * step);
+        compute(rb, tile + step);
     }
 
     // merge the lane groups of this wave (lanes with the same chunk)
@@ -180,34 +208,37 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
     finish_split<D, GP, NW>(a, u, s_m, s_l, s_acc);
 }
 
-template <typename KV, int D, int GP>
+template <typename KV, int D, int GP, int NW>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
-    constexpr int NW = kDecodeThreads / 64;
     constexpr int U = GP >= 16 ? 1 : (GP >= 8 ? 2 : 4);
     hipLaunchKernelGGL((k_decode_valu<KV, D, GP, NW, U>), dim3(a.grid), dim3(NW * 64), 0, st, a);
     return hipGetLastError();
 }
 
-template <typename KV, int D>
+template <typename KV, int D, int NW>
 hipError_t launch_g(const DecodeArgs& a, int gp, hipStream_t st) {
     switch (gp) {
-        case 1: return launch_t<KV, D, 1>(a, st);
-        case 2: return launch_t<KV, D, 2>(a, st);
-        case 4: return launch_t<KV, D, 4>(a, st);
-        case 8: return launch_t<KV, D, 8>(a, st);
-        case 16: return launch_t<KV, D, 16>(a, st);
+        case 1: return launch_t<KV, D, 1, NW>(a, st);
+        case 2: return launch_t<KV, D, 2, NW>(a, st);
+        case 4: return launch_t<KV, D, 4, NW>(a, st);
+        case 8: return launch_t<KV, D, 8, NW>(a, st);
+        case 16: return launch_t<KV, D, 16, NW>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
+template <typename KV, int NW>
+hipError_t launch_d(const sr_shape& s, const DecodeArgs& a, int gp, hipStream_t st) {
+    return s.head_dim == 128 ? launch_g<KV, 128, NW>(a, gp, st) : launch_g<KV, 64, NW>(a, gp, st);
+}
+
 }  // namespace
 
-hipError_t launch_decode_valu(const sr_shape& s, const DecodeArgs& a, int gp, hipStream_t st) {
-    if (s.kv_dtype == SR_KV_BF16) {
-        return s.head_dim == 128 ? launch_g<uint16_t, 128>(a, gp, st)
-                                 : launch_g<uint16_t, 64>(a, gp, st);
-    }
-    return s.head_dim == 128 ? launch_g<float, 128>(a, gp, st) : launch_g<float, 64>(a, gp, st);
+hipError_t launch_decode_valu(const sr_shape& s, const DecodeArgs& a, int gp, int waves,
+                              hipStream_t st) {
+    if (s.kv_dtype == SR_KV_BF16)
+        return waves == 8 ? launch_d<uint16_t, 8>(s, a, gp, st) : launch_d<uint16_t, 4>(s, a, gp, st);
+    return waves == 8 ? launch_d<float, 8>(s, a, gp, st) : launch_d<float, 4>(s, a, gp, st);
 }
 
 }  // namespace sr

@@ -6,7 +6,7 @@
 // or down the attention path before any of its cache is read.  The score is
 // a cosine (README routing controls; pith.science rendering of arXiv
 // 2604.16883, Figure 10: cos(q, K_BOS) judged per KV group).
-#include "sr_internal.h"
+#include "decode_common.h"
 
 namespace sr {
 namespace {
@@ -39,10 +39,15 @@ __device__ inline X wave_sum(X x) {
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kMaxItems = 32768;
+constexpr int kHeadsPerPass = kRouteThreads / 16;  // one 16-lane group per head
+constexpr int kPassUnroll = 4;                       // heads per group per round
 
-// One workgroup.  Phase 1: a wave per item computes the G head cosines and
-// the group decision (sink iff every head has cos >= tau).  Phase 2: a stable
-// partition of the items, active first, by ballot prefix counts.
+// One workgroup.  Phase 1: a 16-lane group per query head loads its query row
+// and its group's k0 row (d/16 contiguous floats per lane, all loads of a
+// round in flight together), reduces <q,k0>, |q|^2, |k0|^2 with DPP and
+// writes the cosine; a head below tau marks its item active in LDS.
+// Phase 2: mask, then a stable partition of the items (active first) by
+// ballot prefix counts.
 __global__ __launch_bounds__(kRouteThreads) void k_route(
     const float* __restrict__ q, const float* __restrict__ k0, float tau,
     float* __restrict__ scores, uint8_t* __restrict__ mask, int32_t* __restrict__ work_list,
@@ -54,41 +59,52 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int32_t G = Hq / Hkv;
     const int32_t n_items = B * Hkv;
+    const int64_t n_heads = static_cast<int64_t>(n_items) * G;  // head j*G + i belongs to item j
+    const int hl = tid & 15, hg = tid >> 4;
 
-    for (int32_t j = wave; j < n_items; j += kRouteWaves) {
-        const int32_t b = j / Hkv, g = j - b * Hkv;
-        const float* kp = k0 + static_cast<int64_t>(j) * d;
-        float kk = 0.f;
-        for (int i = lane; i < d; i += 64) kk += kp[i] * kp[i];
-        kk = wave_sum(kk);
-        bool sink = true;
-        for (int32_t hi = 0; hi < G; ++hi) {
-            const int64_t head = static_cast<int64_t>(b) * Hq + g * G + hi;
-            const float* qp = q + head * d;
-            float qk = 0.f, qq = 0.f;
-            for (int i = lane; i < d; i += 64) {
-                const float x = qp[i];
-                qk += x * kp[i];
-                qq += x * x;
-            }
-            qk = wave_sum(qk);
-            qq = wave_sum(qq);
-            const float den = sqrtf(qq) * sqrtf(kk);
-            const float c = den > 0.f ? qk / den : 0.f;
-            if (lane == 0) scores[head] = c;
-            sink = sink && (c >= tau);
-        }
-        if (lane == 0) {
-            mask[j] = sink ? 1 : 0;
-            s_sink[j] = sink ? 1 : 0;
-        }
-    }
+    for (int32_t j = tid; j < n_items; j += kRouteThreads) s_sink[j] = 1;
     if (tid == 0) s_count = 0;
     __syncthreads();
 
-    // number of active items
+    for (int64_t base = 0; base < n_heads; base += kHeadsPerPass * kPassUnroll) {
+        float qk[kPassUnroll], qq[kPassUnroll], kk[kPassUnroll];
+#pragma unroll
+        for (int r = 0; r < kPassUnroll; ++r) {
+            qk[r] = qq[r] = kk[r] = 0.f;
+            const int64_t hh = base + hg + static_cast<int64_t>(r) * kHeadsPerPass;
+            if (hh < n_heads) {
+                const float* qp = q + hh * d;
+                const float* kp = k0 + (hh / G) * d;
+                for (int e = 4 * hl; e < d; e += 64) {
+                    const float4 x = *reinterpret_cast<const float4*>(qp + e);
+                    const float4 y = *reinterpret_cast<const float4*>(kp + e);
+                    qk[r] += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+                    qq[r] += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+                    kk[r] += y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kPassUnroll; ++r) {
+            const float dot = group_allreduce_sum<16>(qk[r]);
+            const float nq = group_allreduce_sum<16>(qq[r]);
+            const float nk = group_allreduce_sum<16>(kk[r]);
+            const int64_t hh = base + hg + static_cast<int64_t>(r) * kHeadsPerPass;
+            if (hh < n_heads && hl == 0) {
+                const float den = sqrtf(nq) * sqrtf(nk);
+                const float c = den > 0.f ? dot / den : 0.f;
+                scores[hh] = c;
+                if (!(c >= tau)) s_sink[hh / G] = 0;  // one dissenting head keeps the group active
+            }
+        }
+    }
+    __syncthreads();
+
     int32_t local = 0;
-    for (int32_t j = tid; j < n_items; j += kRouteThreads) local += s_sink[j] ? 0 : 1;
+    for (int32_t j = tid; j < n_items; j += kRouteThreads) {
+        mask[j] = s_sink[j];
+        local += s_sink[j] ? 0 : 1;
+    }
     local = wave_sum(local);
     if (lane == 0) atomicAdd(&s_count, local);
     __syncthreads();

@@ -31,12 +31,12 @@ struct DecodeArgs {
     int32_t routed;            // work_list / n_active / v0 are valid
 };
 
-// Positions per split are rounded up to this multiple so every split starts
-// on a whole tile.
-constexpr int64_t kSplitAlign = 64;
 // Adaptive mode never makes a split shorter than this many positions.
 constexpr int64_t kMinSplitLen = 512;
-constexpr int kDecodeThreads = 256;
+// Launch defaults: wave64s per decode workgroup and workgroups per CU in
+// the adaptive grid.
+constexpr int kDefaultWaves = 4;
+constexpr int kDefaultWgsPerCu = 1;
 
 // Splits per active item; the kernels and the host use this same function.
 __host__ __device__ inline int32_t splits_for(int32_t fixed_splits, int32_t grid,
@@ -46,11 +46,6 @@ __host__ __device__ inline int32_t splits_for(int32_t fixed_splits, int32_t grid
     int32_t s = grid / n_act;
     if (s > split_cap) s = split_cap;
     return s < 1 ? 1 : s;
-}
-
-__host__ __device__ inline int64_t split_len(int64_t T, int32_t S) {
-    int64_t L = (T + S - 1) / S;
-    return (L + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
 }
 
 inline int32_t pad_group(int32_t g) {
@@ -66,7 +61,11 @@ hipError_t launch_route(const sr_shape& s, const float* q, const float* k0, floa
                         float* scores, uint8_t* mask, int32_t* work_list, int32_t* n_active,
                         hipStream_t st);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
-hipError_t launch_decode_valu(const sr_shape& s, const DecodeArgs& a, int gp, hipStream_t st);
-hipError_t launch_decode_mfma(const sr_shape& s, const DecodeArgs& a, int gp, hipStream_t st);
+hipError_t launch_decode_valu(const sr_shape& s, const DecodeArgs& a, int gp, int waves,
+                              hipStream_t st);
+hipError_t launch_decode_mfma(const sr_shape& s, const DecodeArgs& a, int gp, int waves,
+                              hipStream_t st);
+hipError_t launch_stream_read(const void* buf, size_t bytes, int32_t grid, int32_t unroll,
+                              int32_t blocked, uint32_t* sink, hipStream_t st);
 
 }  // namespace sr

@@ -97,7 +97,8 @@ def test_launch_policy_checks():
     s = shape()
     assert decode(s, launch=N.SrLaunch(-1, 0, 0, 0)) == N.SR_ERR_INVALID_ARG
     assert decode(s, launch=N.SrLaunch(0, 9, 0, 0)) == N.SR_ERR_INVALID_ARG
-    assert decode(s, launch=N.SrLaunch(0, 0, 0, 5)) == N.SR_ERR_INVALID_ARG
+    assert decode(s, launch=N.SrLaunch(0, 0, 0, 5)) == N.SR_ERR_INVALID_ARG   # 5 waves
+    assert decode(s, launch=N.SrLaunch(0, 0, -1, 0)) == N.SR_ERR_INVALID_ARG
     f32 = shape(dt=N.SR_KV_F32)
     assert decode(f32, launch=N.SrLaunch(0, N.SR_KERNEL_MFMA, 0, 0)) == N.SR_ERR_UNSUPPORTED
 

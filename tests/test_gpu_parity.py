@@ -25,7 +25,7 @@ if torch.cuda.is_available():
 else:  # collected on CPU only to be deselected by -m "not gpu"
     sr = None
 
-BF16_KERNELS = ["valu"]
+BF16_KERNELS = ["valu", "mfma"]
 KERNEL_ID = {"valu": 1, "mfma": 2, "auto": 0}
 
 
