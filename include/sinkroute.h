@@ -152,6 +152,20 @@ sr_status sr_decode_attn(const sr_shape* shape, const sr_launch* launch, const f
                          const int32_t* work_list, const int32_t* n_active, float sm_scale,
                          void* ws, size_t ws_bytes, float* out, void* stream);
 
+/* Routing and decode in one launch (the fused form of sr_route followed by
+ * sr_decode_attn, same arguments).  Every workgroup derives the routing
+ * decision itself from q and k0 with the arithmetic of sr_route, so the
+ * decisions, the work list and the output are bit-identical to the two-call
+ * form under the same launch policy; workgroup 0 writes the routing outputs
+ * scores / mask / work_list / n_active, each of which may be NULL.  Saves a
+ * launch and the routing kernel per layer-step.  Envelope: B*Hkv <= 4096
+ * (else SR_ERR_UNSUPPORTED: use the two calls). */
+sr_status sr_route_decode(const sr_shape* shape, const sr_launch* launch, const float* q,
+                          const void* k_cache, const void* v_cache, const float* k0,
+                          const float* v0, float tau, float sm_scale, float* scores,
+                          uint8_t* mask, int32_t* work_list, int32_t* n_active, void* ws,
+                          size_t ws_bytes, float* out, void* stream);
+
 /* Dense baseline: the decode kernel of sr_decode_attn with routing off
  * (identity work list, every item active).  sr_decode_attn with a work list
  * routed at tau > 1 gives the same bits for the same launch policy. */

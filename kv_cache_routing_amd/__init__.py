@@ -22,7 +22,8 @@ from . import _native as N
 from ._native import (SR_KERNEL_AUTO, SR_KERNEL_MFMA, SR_KERNEL_VALU,  # noqa: F401
                       SinkRouteError)
 
-__all__ = ["record_sink", "route", "decode_attn", "dense_decode", "Workspace", "make_shape",
+__all__ = ["record_sink", "route", "decode_attn", "route_decode", "dense_decode", "Workspace",
+           "make_shape",
            "make_launch", "splits_for", "grid_size", "SinkRouteError", "Routing",
            "SR_KERNEL_AUTO", "SR_KERNEL_VALU", "SR_KERNEL_MFMA"]
 
@@ -153,6 +154,26 @@ def decode_attn(q, k, v, v0, work_list, n_active, sm_scale: float = 0.0,
                                  ctypes.c_float(sm_scale), _ptr(ws.buf), ws.nbytes, _ptr(out),
                                  _stream()), "sr_decode_attn")
     return out
+
+
+def route_decode(q, k, v, k0, v0, tau: float = 0.5, sm_scale: float = 0.0,
+                 launch: N.SrLaunch | None = None, ws: Workspace | None = None,
+                 out: torch.Tensor | None = None, routing: Routing | None = None):
+    """Routing and decode in one launch; returns (out, routing outputs)."""
+    shape, ws, out = _prep(q, k, v, launch, ws, out)
+    B, Hkv, d = k0.shape
+    if routing is None:
+        dev = q.device
+        routing = Routing(torch.empty((B, q.shape[1]), dtype=torch.float32, device=dev),
+                          torch.empty((B, Hkv), dtype=torch.uint8, device=dev),
+                          torch.empty((B * Hkv,), dtype=torch.int32, device=dev),
+                          torch.empty((1,), dtype=torch.int32, device=dev))
+    N.check(N.lib.sr_route_decode(ctypes.byref(shape), _lp(launch), _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(k0), _ptr(v0), ctypes.c_float(tau), ctypes.c_float(sm_scale),
+                                  _ptr(routing.scores), _ptr(routing.mask),
+                                  _ptr(routing.work_list), _ptr(routing.n_active), _ptr(ws.buf),
+                                  ws.nbytes, _ptr(out), _stream()), "sr_route_decode")
+    return out, routing
 
 
 def dense_decode(q, k, v, sm_scale: float = 0.0, launch: N.SrLaunch | None = None,

@@ -109,17 +109,32 @@ WsLayout ws_layout(const sr_shape& s, const Plan& p) {
     return w;
 }
 
+struct FusedRoute {
+    const float* k0;
+    float tau;
+    float* scores;
+    uint8_t* mask;
+    int32_t* work_list;
+    int32_t* n_active;
+};
+
 sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float* q,
                      const void* k, const void* v, const float* v0, const int32_t* work_list,
                      const int32_t* n_active, float sm_scale, void* ws, size_t ws_bytes,
-                     float* out, void* stream, bool routed) {
+                     float* out, void* stream, bool routed, const FusedRoute* fused = nullptr) {
     sr_status st = check_shape(shape);
     if (st != SR_OK) return st;
     const sr_shape& s = *shape;
     if ((st = check_caches(s, k, v)) != SR_OK) return st;
     if (!q || !out || !ws || !aligned16(q) || !aligned16(out) || !aligned16(ws))
         return SR_ERR_INVALID_ARG;
-    if (routed && (!v0 || !work_list || !n_active)) return SR_ERR_INVALID_ARG;
+    if (routed && !v0) return SR_ERR_INVALID_ARG;
+    if (routed && !fused && (!work_list || !n_active)) return SR_ERR_INVALID_ARG;
+    if (fused) {
+        if (!fused->k0 || !aligned16(fused->k0) || isnan(fused->tau)) return SR_ERR_INVALID_ARG;
+        if (static_cast<int64_t>(s.batch) * s.num_kv_heads > kMaxFusedItems)
+            return SR_ERR_UNSUPPORTED;
+    }
     Plan p;
     if ((st = make_plan(s, launch, p)) != SR_OK) return st;
     const WsLayout w = ws_layout(s, p);
@@ -151,6 +166,15 @@ sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float
     a.grid = p.grid;
     a.split_cap = p.split_cap;
     a.routed = routed ? 1 : 0;
+    if (fused) {
+        a.fused = 1;
+        a.k0 = fused->k0;
+        a.tau = fused->tau;
+        a.scores_out = fused->scores;
+        a.mask_out = fused->mask;
+        a.list_out = fused->work_list;
+        a.n_active_out = fused->n_active;
+    }
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
     hipError_t e = p.kernel == SR_KERNEL_MFMA ? launch_decode_mfma(s, a, p.gp, p.waves, hs)
@@ -206,6 +230,16 @@ sr_status sr_decode_attn(const sr_shape* shape, const sr_launch* launch, const f
                          void* ws, size_t ws_bytes, float* out, void* stream) {
     return run_decode(shape, launch, q, k_cache, v_cache, v0, work_list, n_active, sm_scale, ws,
                       ws_bytes, out, stream, true);
+}
+
+sr_status sr_route_decode(const sr_shape* shape, const sr_launch* launch, const float* q,
+                          const void* k_cache, const void* v_cache, const float* k0,
+                          const float* v0, float tau, float sm_scale, float* scores,
+                          uint8_t* mask, int32_t* work_list, int32_t* n_active, void* ws,
+                          size_t ws_bytes, float* out, void* stream) {
+    const FusedRoute f{k0, tau, scores, mask, work_list, n_active};
+    return run_decode(shape, launch, q, k_cache, v_cache, v0, nullptr, nullptr, sm_scale, ws,
+                      ws_bytes, out, stream, true, &f);
 }
 
 sr_status sr_dense_decode(const sr_shape* shape, const sr_launch* launch, const float* q,

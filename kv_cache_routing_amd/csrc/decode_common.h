@@ -67,45 +67,19 @@ struct WorkUnit {
     int64_t t1;      // positions [0, t1) exist (t1 = T)
 };
 
-// Sink duty, then the work mapping.  Workgroup w first copies v0 into the G
-// output rows of the sink at list position n_active + w (if there is one);
-// then it takes split (w mod S) of active slot (w / S), S = splits per item.
+// Routing decision and work mapping of one workgroup, then its sink duty.
+// Workgroup w copies v0 into the G output rows of the sink at list position
+// n_active + w (if there is one), then takes split (w mod S) of the active
+// item at list position (w / S), S = splits per item.  Without routing the
+// list is the identity; with sr_route the list and n_active come from device
+// memory; in fused mode every workgroup derives the decisions itself (the
+// same arithmetic as sr_route, so every workgroup agrees) and workgroup 0
+// writes the routing outputs.  Returns false when there is no split to do.
 // A split with no chunk below T (S * CHUNK > T) is empty and still merges.
-// Returns false when the workgroup has no split to compute.
 template <int D, int NT, int CHUNK>
-__device__ inline bool map_work(const DecodeArgs& a, WorkUnit& u) {
-    const int32_t n_items = a.batch * a.num_kv_heads;
-    const int32_t n_act = a.routed ? *a.n_active : n_items;
-    const int32_t wg = blockIdx.x;
-    const int32_t G = a.group;
-    if (a.routed) {
-        const int32_t ss = n_act + wg;
-        if (ss < n_items) {
-            const int32_t j = a.work_list[ss];
-            const int32_t b = j / a.num_kv_heads, g = j - b * a.num_kv_heads;
-            const float* src = a.v0 + static_cast<int64_t>(j) * D;
-            float* dst = a.out + (static_cast<int64_t>(b) * a.num_q_heads +
-                                  static_cast<int64_t>(g) * G) * D;
-            for (int x = threadIdx.x; x < G * D; x += NT) dst[x] = src[x % D];
-        }
-    }
-    if (n_act <= 0) return false;
-    const int32_t S = splits_for(a.fixed_splits, a.grid, a.split_cap, n_act);
-    const int32_t slot = wg / S;
-    if (slot >= n_act) return false;
-    u.slot = slot;
-    u.split = wg - slot * S;
-    u.splits = S;
-    const int32_t item = a.routed ? a.work_list[slot] : slot;
-    u.b = item / a.num_kv_heads;
-    u.g = item - u.b * a.num_kv_heads;
-    u.first = static_cast<int64_t>(u.split) * CHUNK;
-    u.stride = static_cast<int64_t>(S) * CHUNK;
-    u.t1 = a.seq_len;
-    return true;
-}
+__device__ inline bool map_work(const DecodeArgs& a, WorkUnit& u);
 
-// Last-arriver merge of the S split partials of one item (all threads of the
+// Last-arriver merge of the S split partials// Last-arriver merge of the S split partials of one item (all threads of the
 // workgroup).  Every global load of the merge is independent of the others,
 // so they are issued in unrolled batches: the merge costs a few memory round
 // trips, not one per split.  Order is fixed: maxima, then per split weights

@@ -20,7 +20,7 @@
 // Method: SinkRouter README (github.com/streamer-AP/SinkRouter), decode-time
 // steps (tiled QK/PV with an online softmax, Split-K, in-kernel merge);
 // result defined by Eq. (1) of the paper (pith.science, Figure 1 caption).
-#include "decode_common.h"
+#include "routing.h"
 
 namespace sr {
 namespace {

@@ -13,7 +13,7 @@
 //
 // Method: SinkRouter README (github.com/streamer-AP/SinkRouter), decode-time
 // steps (tiled QK/PV with an online softmax, Split-K, in-kernel merge).
-#include "decode_common.h"
+#include "routing.h"
 
 namespace sr {
 namespace {
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
 
 template <typename KV, int D, int GP, int NW>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
-    constexpr int U = GP >= 16 ? 1 : (GP >= 8 ? 2 : 4);
+    constexpr int U = GP >= 16 ? 1 : (GP >= 8 ? 2 : (GP >= 4 ? 8 : 8));
     hipLaunchKernelGGL((k_decode_valu<KV, D, GP, NW, U>), dim3(a.grid), dim3(NW * 64), 0, st, a);
     return hipGetLastError();
 }

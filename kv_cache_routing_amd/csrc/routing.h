@@ -1,0 +1,204 @@
+// Routing arithmetic shared by the routing kernel and the fused route+decode
+// prologue, so both take bit-identical decisions.
+//
+// SinkRouter README (github.com/streamer-AP/SinkRouter): at decode each GQA KV
+// group is scored by the cosine between the rotated query and the key kept at
+// position 0 (routing-controls section: a cosine threshold), and is sent down
+// the sink bypass or the attention path before its cache is read
+// (decode-time steps); pith.science rendering of arXiv 2604.16883, Figure 10:
+// cos(q, K_BOS) judged at the KV-group level.  Reading: a group is a sink only
+// when every one of its heads has cos >= tau; a zero norm scores 0.
+#pragma once
+
+#include "decode_common.h"
+
+namespace sr {
+
+// Cosines of U query heads, one head per aligned 16-lane group: head
+// first + r * stride (r < U) in group lane hl.  Lane hl accumulates elements
+// 4*hl + 64*k with explicit fmaf in a fixed order, then a fixed DPP tree
+// reduces the group, so a head's score does not depend on which kernel or
+// which lane group computed it.  All 64 lanes of the wave must be active.
+template <int U>
+__device__ inline void head_cosines16(const float* __restrict__ q, const float* __restrict__ k0,
+                                      int64_t first, int64_t stride, int64_t n_heads, int32_t G,
+                                      int32_t d, int hl, float (&c)[U]) {
+    float qk[U], qq[U], kk[U];
+#pragma unroll
+    for (int r = 0; r < U; ++r) {
+        qk[r] = qq[r] = kk[r] = 0.f;
+        const int64_t hh = first + static_cast<int64_t>(r) * stride;
+        if (hh < n_heads) {
+            const float* qp = q + hh * d;
+            const float* kp = k0 + (hh / G) * d;
+            for (int e = 4 * hl; e < d; e += 64) {
+                const float4 x = *reinterpret_cast<const float4*>(qp + e);
+                const float4 y = *reinterpret_cast<const float4*>(kp + e);
+                qk[r] = fmaf(x.x, y.x, qk[r]);
+                qk[r] = fmaf(x.y, y.y, qk[r]);
+                qk[r] = fmaf(x.z, y.z, qk[r]);
+                qk[r] = fmaf(x.w, y.w, qk[r]);
+                qq[r] = fmaf(x.x, x.x, qq[r]);
+                qq[r] = fmaf(x.y, x.y, qq[r]);
+                qq[r] = fmaf(x.z, x.z, qq[r]);
+                qq[r] = fmaf(x.w, x.w, qq[r]);
+                kk[r] = fmaf(y.x, y.x, kk[r]);
+                kk[r] = fmaf(y.y, y.y, kk[r]);
+                kk[r] = fmaf(y.z, y.z, kk[r]);
+                kk[r] = fmaf(y.w, y.w, kk[r]);
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < U; ++r) {
+        const float dot = group_allreduce_sum<16>(qk[r]);
+        const float nq = group_allreduce_sum<16>(qq[r]);
+        const float nk = group_allreduce_sum<16>(kk[r]);
+        const float den = sqrtf(nq) * sqrtf(nk);
+        c[r] = den > 0.f ? dot / den : 0.f;
+    }
+}
+
+// Scores of every head of the layer (B*Hq heads of G per item), computed by
+// NT threads; s_sink[j] ends 1 iff every head of item j has cos >= tau.
+// Heads and items are written to `scores` / `mask` when those are non-null.
+// Ends with a workgroup barrier.
+template <int NT, int U>
+__device__ inline void route_items(const float* __restrict__ q, const float* __restrict__ k0,
+                                   float tau, int32_t n_items, int32_t G, int32_t d,
+                                   uint8_t* s_sink, float* scores, uint8_t* mask) {
+    constexpr int GROUPS = NT / 16;
+    const int tid = threadIdx.x, hl = tid & 15, hg = tid >> 4;
+    const int64_t n_heads = static_cast<int64_t>(n_items) * G;
+    for (int32_t j = tid; j < n_items; j += NT) s_sink[j] = 1;
+    __syncthreads();
+    for (int64_t base = 0; base < n_heads; base += static_cast<int64_t>(GROUPS) * U) {
+        float c[U];
+        head_cosines16<U>(q, k0, base + hg, GROUPS, n_heads, G, d, hl, c);
+#pragma unroll
+        for (int r = 0; r < U; ++r) {
+            const int64_t hh = base + hg + static_cast<int64_t>(r) * GROUPS;
+            if (hh < n_heads && hl == 0) {
+                if (scores) scores[hh] = c[r];
+                if (!(c[r] >= tau)) s_sink[hh / G] = 0;  // one dissenting head keeps it active
+            }
+        }
+    }
+    __syncthreads();
+    if (mask)
+        for (int32_t j = tid; j < n_items; j += NT) mask[j] = s_sink[j];
+}
+
+// Number of active items (s_sink[j] == 0), from every thread.
+template <int NT>
+__device__ inline int32_t count_active(const uint8_t* s_sink, int32_t n_items, int32_t* s_tmp) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int32_t local = 0;
+    for (int32_t j = threadIdx.x; j < n_items; j += NT) local += s_sink[j] ? 0 : 1;
+    for (int o = 32; o > 0; o >>= 1) local += __shfl_xor(local, o);
+    if (lane == 0) s_tmp[wave] = local;
+    __syncthreads();
+    int32_t n = 0;
+    for (int w = 0; w < NT / 64; ++w) n += s_tmp[w];
+    __syncthreads();
+    return n;
+}
+
+// Stable partition of the items: active ones in ascending order at list
+// positions [0, n_act), sinks in ascending order at [n_act, n_items).
+// visit(pos, j) is called once for every item by the thread that owns it.
+template <int NT, typename Visit>
+__device__ inline void partition_items(const uint8_t* s_sink, int32_t n_items, int32_t n_act,
+                                       int32_t* s_wa, int32_t* s_ws, Visit visit) {
+    constexpr int NWV = NT / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int32_t base_a = 0, base_s = n_act;
+    for (int32_t c0 = 0; c0 < n_items; c0 += NT) {
+        const int32_t j = c0 + threadIdx.x;
+        const bool in = j < n_items;
+        const bool is_a = in && !s_sink[j];
+        const bool is_s = in && s_sink[j];
+        const uint64_t ba = __ballot(is_a), bs = __ballot(is_s);
+        if (lane == 0) {
+            s_wa[wave] = __popcll(ba);
+            s_ws[wave] = __popcll(bs);
+        }
+        __syncthreads();
+        int32_t pa = base_a, ps = base_s, ta = 0, ts = 0;
+        for (int w = 0; w < NWV; ++w) {
+            if (w < wave) {
+                pa += s_wa[w];
+                ps += s_ws[w];
+            }
+            ta += s_wa[w];
+            ts += s_ws[w];
+        }
+        if (is_a) visit(pa + __popcll(ba & lt), j);
+        if (is_s) visit(ps + __popcll(bs & lt), j);
+        base_a += ta;
+        base_s += ts;
+        __syncthreads();
+    }
+}
+
+}  // namespace sr
+
+namespace sr {
+
+template <int D, int NT, int CHUNK>
+__device__ inline bool map_work(const DecodeArgs& a, WorkUnit& u) {
+    const int32_t n_items = a.batch * a.num_kv_heads;
+    const int32_t wg = blockIdx.x;
+    const int32_t G = a.group;
+    int32_t n_act, S, slot, item = -1, sink_item = -1;
+    if (a.fused) {
+        __shared__ uint8_t s_flag[kMaxFusedItems];
+        __shared__ int32_t s_wa[NT / 64], s_ws[NT / 64];
+        __shared__ int32_t s_pick[2];
+        const bool w0 = wg == 0;
+        route_items<NT, 8>(a.q, a.k0, a.tau, n_items, G, D, s_flag, w0 ? a.scores_out : nullptr,
+                           w0 ? a.mask_out : nullptr);
+        n_act = count_active<NT>(s_flag, n_items, s_wa);
+        S = splits_for(a.fixed_splits, a.grid, a.split_cap, n_act);
+        slot = wg / S;
+        const int32_t want_a = (n_act > 0 && slot < n_act) ? slot : -1;
+        const int32_t want_s = n_act + wg < n_items ? n_act + wg : -1;
+        if (threadIdx.x == 0) s_pick[0] = s_pick[1] = -1;
+        __syncthreads();
+        int32_t* list = w0 ? a.list_out : nullptr;
+        partition_items<NT>(s_flag, n_items, n_act, s_wa, s_ws, [&](int32_t pos, int32_t j) {
+            if (pos == want_a) s_pick[0] = j;
+            if (pos == want_s) s_pick[1] = j;
+            if (list) list[pos] = j;
+        });
+        if (w0 && threadIdx.x == 0 && a.n_active_out) a.n_active_out[0] = n_act;
+        item = s_pick[0];
+        sink_item = s_pick[1];
+    } else {
+        n_act = a.routed ? *a.n_active : n_items;
+        S = splits_for(a.fixed_splits, a.grid, a.split_cap, n_act);
+        slot = wg / S;
+        if (a.routed && n_act + wg < n_items) sink_item = a.work_list[n_act + wg];
+        if (n_act > 0 && slot < n_act) item = a.routed ? a.work_list[slot] : slot;
+    }
+    if (sink_item >= 0) {
+        const int32_t b = sink_item / a.num_kv_heads, g = sink_item - b * a.num_kv_heads;
+        const float* src = a.v0 + static_cast<int64_t>(sink_item) * D;
+        float* dst =
+            a.out + (static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(g) * G) * D;
+        for (int x = threadIdx.x; x < G * D; x += NT) dst[x] = src[x % D];
+    }
+    if (item < 0) return false;
+    u.slot = slot;
+    u.split = wg - slot * S;
+    u.splits = S;
+    u.b = item / a.num_kv_heads;
+    u.g = item - u.b * a.num_kv_heads;
+    u.first = static_cast<int64_t>(u.split) * CHUNK;
+    u.stride = static_cast<int64_t>(S) * CHUNK;
+    u.t1 = a.seq_len;
+    return true;
+}
+
+}  // namespace sr

@@ -28,8 +28,21 @@ struct DecodeArgs {
     int32_t fixed_splits;      // > 0: fixed split count; 0: adaptive
     int32_t grid;              // workgroups launched
     int32_t split_cap;         // adaptive: upper bound on splits per item
-    int32_t routed;            // work_list / n_active / v0 are valid
+    int32_t routed;            // v0 is valid; sinks are bypassed
+    // Fused routing (sr_route_decode): every workgroup derives the routing
+    // decision from q and k0 itself; workgroup 0 also writes the optional
+    // routing outputs.  When 0, work_list / n_active come from sr_route.
+    int32_t fused;
+    const float* k0;           // [B][Hkv][d] fp32 (fused only)
+    float tau;
+    float* scores_out;         // [B][Hq]   (fused, optional)
+    uint8_t* mask_out;         // [B][Hkv]  (fused, optional)
+    int32_t* list_out;         // [B*Hkv]   (fused, optional)
+    int32_t* n_active_out;     // [1]       (fused, optional)
 };
+
+// The fused route+decode prologue keeps one flag per item in LDS.
+constexpr int32_t kMaxFusedItems = 4096;
 
 // Adaptive mode never makes a split shorter than this many positions.
 constexpr int64_t kMinSplitLen = 512;

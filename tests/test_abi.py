@@ -140,3 +140,18 @@ def test_route_and_record_validation():
     r = N.lib.sr_record_sink(None, p(), p(), p(), p(), None)
     assert r == N.SR_ERR_INVALID_ARG
     assert N.lib.sr_workspace_init(p(0), 16, None) == N.SR_ERR_INVALID_ARG
+
+
+def test_fused_route_decode_validation():
+    s = shape()
+
+    def fused(s, k0=FAKE, v0=FAKE, tau=0.5, ws_bytes=1 << 30):
+        return N.lib.sr_route_decode(ctypes.byref(s), None, p(), p(), p(), p(k0), p(v0),
+                                     ctypes.c_float(tau), 0.0, p(0), p(0), p(0), p(0), p(),
+                                     ws_bytes, p(), None)
+    assert fused(s, k0=0) == N.SR_ERR_INVALID_ARG
+    assert fused(s, v0=0) == N.SR_ERR_INVALID_ARG
+    assert fused(s, tau=float("nan")) == N.SR_ERR_INVALID_ARG
+    assert fused(s, ws_bytes=16) == N.SR_ERR_INVALID_ARG
+    big = shape(B=1024, Hq=8, Hkv=8)            # 8192 items > 4096
+    assert fused(big) == N.SR_ERR_UNSUPPORTED

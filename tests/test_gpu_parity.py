@@ -269,3 +269,77 @@ def test_full_size_256k_b4_sink_fraction_sweep():
         layer = Layer(wl, q_cpu, k_cpu, v_cpu, planted)
         r = sampled_check(layer, q_cpu.cuda(), k, v, launch("auto"), n_samples=1, seed=int(f * 4))
         assert int(r.n_active.cpu()[0]) == round((1 - f) * 8) * 4
+
+
+# --- fused route + decode (one launch) ------------------------------------------
+FUSED_CASES = [
+    Workload("f-8b-ragged", 1, 32, 8, 128, 12345, "bf16", seed=61, sink_plan=("count", 4)),
+    Workload("f-70b", 2, 64, 8, 128, 6000, "bf16", seed=62, sink_plan=("bernoulli", 0.5)),
+    Workload("f-g3", 3, 12, 4, 64, 2100, "bf16", seed=63, sink_plan=("bernoulli", 0.5)),
+    Workload("f-f32", 1, 16, 4, 128, 3333, "f32", seed=64, sink_plan=("count", 2)),
+]
+
+
+@pytest.mark.parametrize("wl", FUSED_CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("kernel", ["auto", "valu", "mfma"])
+def test_fused_route_decode_matches_two_calls_bitwise(wl, kernel):
+    if wl.kv_dtype == "f32" and kernel == "mfma":
+        pytest.skip("matrix-core kernel takes bf16 caches")
+    layer = make_layer(wl)
+    q, k, v = upload(layer)
+    lau = launch(kernel)
+    k0, v0, r, out2 = run_routed(q, k, v, wl.tau, lau)
+    out1, rf = sr.route_decode(q, k, v, k0, v0, wl.tau, launch=lau)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    assert torch.equal(rf.scores, r.scores)
+    assert torch.equal(rf.mask, r.mask)
+    assert torch.equal(rf.work_list, r.work_list)
+    assert torch.equal(rf.n_active, r.n_active)
+    q_np, k_np, v_np = oracle_inputs(layer)
+    mask = assert_route(rf, q_np, as_numpy(layer.k[:, :, 0]), wl.tau)[0]
+    ref = oracle.routed_decode(q_np, k_np, v_np, as_numpy(layer.v[:, :, 0]), mask)
+    assert_outputs(out1.cpu().numpy(), ref, f"fused {wl.name}")
+
+
+def test_fused_edges_all_sinks_no_sinks_and_repeats():
+    wl = Workload("f-edges", 2, 16, 4, 128, 4000, "bf16", seed=65, sink_plan=("count", 2))
+    layer = make_layer(wl)
+    q, k, v = upload(layer)
+    k0, v0 = sr.record_sink(k, v)
+    out, r = sr.route_decode(q, k, v, k0, v0, -2.0)
+    assert int(r.n_active.cpu()[0]) == 0
+    assert torch.equal(out, v0.repeat_interleave(4, dim=1))
+    out, r = sr.route_decode(q, k, v, k0, v0, 1.5)
+    assert int(r.n_active.cpu()[0]) == 8
+    assert torch.equal(out, sr.dense_decode(q, k, v))
+    lau = launch("auto")
+    ws = sr.Workspace(sr.make_shape(q, k, v), lau, q.device)
+    first, _ = sr.route_decode(q, k, v, k0, v0, wl.tau, launch=lau, ws=ws)
+    first = first.clone()
+    for _ in range(100):
+        again, _ = sr.route_decode(q, k, v, k0, v0, wl.tau, launch=lau, ws=ws)
+        assert torch.equal(again, first)
+    torch.cuda.synchronize()
+    assert int(ticket_region(ws, 8).abs().sum()) == 0
+
+
+def test_fused_full_size_70b_layer_sampled():
+    wl = L70B_128K_B8
+    layer = make_layer(wl)
+    q, k, v = upload(layer)
+    k0, v0 = sr.record_sink(k, v)
+    out, r = sr.route_decode(q, k, v, k0, v0, wl.tau)
+    r2 = sr.route(q, k0, wl.tau)
+    out2 = sr.decode_attn(q, k, v, v0, r2.work_list, r2.n_active)
+    torch.cuda.synchronize()
+    assert torch.equal(r.mask, r2.mask) and torch.equal(r.work_list, r2.work_list)
+    assert torch.equal(out, out2)
+    G = wl.group_size
+    q_np = as_numpy(layer.q)
+    n_act = int(r.n_active.cpu()[0])
+    j = int(r.work_list.cpu()[n_act // 2])
+    b, g = divmod(j, wl.num_kv_heads)
+    ref = oracle.attend_group(q_np[b, g * G:(g + 1) * G], as_numpy(layer.k[b, g]),
+                              as_numpy(layer.v[b, g]), 1.0 / math.sqrt(wl.head_dim))
+    assert_outputs(out.cpu().numpy()[b, g * G:(g + 1) * G], ref, f"fused 70b item {j}")
