@@ -229,6 +229,33 @@ def cpu_baseline(layer, n_active_items, budget_s=12.0):
     }
 
 
+def bos_proxy_report(sr, torch):
+    """Routing proxy vs position-0 attention mass, GPU outputs only."""
+    from kv_cache_routing_amd import proxy
+    from workloads import L8B_128K, make_layer
+    dev = torch.device("cuda:0")
+    taus = [round(0.05 * i, 2) for i in range(21)]
+    report = []
+    for k0_norm in (30.0, 120.0, 400.0):
+        wl = L8B_128K.with_(name=f"llama8b-32k-b4-k0norm{int(k0_norm)}", batch=4, seq_len=32768,
+                            seed=7000 + int(k0_norm), k0_norm=k0_norm)
+        layer = make_layer(wl)
+        q, k, v = layer.q.to(dev), layer.k.to(dev), layer.v.to(dev)
+        k0, _ = sr.record_sink(k, v)
+        r = sr.route(q, k0, wl.tau)
+        _, a0 = sr.dense_decode_alpha0(q, k, v)
+        torch.cuda.synchronize()
+        ev = proxy.sink_events(a0, wl.num_kv_heads, 0.5)
+        report.append({"layer": wl.name, "planted_sinks": int(layer.planted.sum()),
+                       "events": int(ev.sum()), "groups": wl.batch * wl.num_kv_heads,
+                       "alpha0_planted_mean": float(a0.view(wl.batch, wl.num_kv_heads, -1)[
+                           layer.planted.to(dev)].mean()),
+                       "sweep": proxy.threshold_sweep(r.scores, a0, wl.num_kv_heads, taus, 0.5)})
+        log(f"bos proxy {wl.name}: events {int(ev.sum())}")
+    print(json.dumps({"bos_proxy": report}), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,6 +271,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-compare", action="store_true",
                     help="skip timing the decode kernel under each kernel variant")
+    ap.add_argument("--bos-proxy", action="store_true",
+                    help="precision/recall of the cosine routing rule against position-0 "
+                         "attention-mass events (alpha_0 >= 0.5 in every head) over a tau "
+                         "sweep, on synthetic 8B-shaped layers at several k0 norms, and exit")
     ap.add_argument("--read-ceiling", action="store_true",
                     help="print the HBM read-probe sweep over the layer caches and exit")
     ap.add_argument("--roofline-only", action="store_true",
@@ -269,6 +300,9 @@ def main():
     import kv_cache_routing_amd as sr
     from workloads import (CONFIGS, L8B_256K_B4, SINK_FRACTIONS, make_caches, make_queries,
                            sweep)
+
+    if args.bos_proxy:
+        return bos_proxy_report(sr, torch)
 
     names = {w.name: w for w in CONFIGS}
     names.update({sweep(L8B_256K_B4, f).name: sweep(L8B_256K_B4, f) for f in SINK_FRACTIONS})

@@ -124,7 +124,8 @@ sr_status sr_route(const sr_shape* shape, const float* q, const float* k0, float
                    void* stream);
 
 /* Bytes of scratch the decode calls need for this shape and launch policy:
- * per-workgroup split partials (m, l and acc, fp32) plus one ticket per item.
+ * per-workgroup split partials (m, l, the position-0 logit and acc, fp32)
+ * plus one ticket per item.
  * Depends on the current device's CU count in adaptive mode. Returns 0 on an
  * invalid or unsupported shape. */
 size_t sr_workspace_bytes(const sr_shape* shape, const sr_launch* launch);
@@ -172,6 +173,16 @@ sr_status sr_route_decode(const sr_shape* shape, const sr_launch* launch, const 
 sr_status sr_dense_decode(const sr_shape* shape, const sr_launch* launch, const float* q,
                           const void* k_cache, const void* v_cache, float sm_scale,
                           void* ws, size_t ws_bytes, float* out, void* stream);
+
+/* Dense decode that also reports, per query head, the attention weight of
+ * position 0: alpha0[b][h] = softmax weight of the first cached position
+ * (Eq. (1) of the paper; the pith.science Figure 10 caption evaluates the
+ * cosine routing proxy against sink events defined from this full-attention
+ * weight).  alpha0: fp32 [B][Hq], required.  Same contract as
+ * sr_dense_decode otherwise; the output is bitwise equal to it. */
+sr_status sr_dense_decode_alpha0(const sr_shape* shape, const sr_launch* launch, const float* q,
+                                 const void* k_cache, const void* v_cache, float sm_scale, void* ws,
+                                 size_t ws_bytes, float* out, float* alpha0, void* stream);
 
 /* Number of splits per active item the decode kernel will use for a given
  * n_active under this policy (what the adaptive mode derives on the device). */

@@ -22,7 +22,8 @@ from . import _native as N
 from ._native import (SR_KERNEL_AUTO, SR_KERNEL_MFMA, SR_KERNEL_VALU,  # noqa: F401
                       SinkRouteError)
 
-__all__ = ["record_sink", "route", "decode_attn", "route_decode", "dense_decode", "Workspace",
+__all__ = ["record_sink", "route", "decode_attn", "route_decode", "dense_decode",
+           "dense_decode_alpha0", "Workspace",
            "make_shape",
            "make_launch", "splits_for", "grid_size", "SinkRouteError", "Routing",
            "SR_KERNEL_AUTO", "SR_KERNEL_VALU", "SR_KERNEL_MFMA"]
@@ -174,6 +175,18 @@ def route_decode(q, k, v, k0, v0, tau: float = 0.5, sm_scale: float = 0.0,
                                   _ptr(routing.work_list), _ptr(routing.n_active), _ptr(ws.buf),
                                   ws.nbytes, _ptr(out), _stream()), "sr_route_decode")
     return out, routing
+
+
+def dense_decode_alpha0(q, k, v, sm_scale: float = 0.0, launch: N.SrLaunch | None = None,
+                        ws: Workspace | None = None, out: torch.Tensor | None = None):
+    """Dense decode plus the attention weight of position 0 per head."""
+    shape, ws, out = _prep(q, k, v, launch, ws, out)
+    alpha0 = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    N.check(N.lib.sr_dense_decode_alpha0(ctypes.byref(shape), _lp(launch), _ptr(q), _ptr(k),
+                                         _ptr(v), ctypes.c_float(sm_scale), _ptr(ws.buf),
+                                         ws.nbytes, _ptr(out), _ptr(alpha0), _stream()),
+            "sr_dense_decode_alpha0")
+    return out, alpha0
 
 
 def dense_decode(q, k, v, sm_scale: float = 0.0, launch: N.SrLaunch | None = None,

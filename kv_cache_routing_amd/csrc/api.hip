@@ -104,7 +104,7 @@ WsLayout ws_layout(const sr_shape& s, const Plan& p) {
     WsLayout w;
     w.tickets = 0;
     w.ml = align256(n_items * sizeof(uint32_t));
-    w.acc = w.ml + align256(static_cast<size_t>(p.grid) * 2 * p.gp * sizeof(float));
+    w.acc = w.ml + align256(static_cast<size_t>(p.grid) * 3 * p.gp * sizeof(float));
     w.total = w.acc + align256(static_cast<size_t>(p.grid) * p.gp * s.head_dim * sizeof(float));
     return w;
 }
@@ -121,7 +121,8 @@ struct FusedRoute {
 sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float* q,
                      const void* k, const void* v, const float* v0, const int32_t* work_list,
                      const int32_t* n_active, float sm_scale, void* ws, size_t ws_bytes,
-                     float* out, void* stream, bool routed, const FusedRoute* fused = nullptr) {
+                     float* out, void* stream, bool routed, const FusedRoute* fused = nullptr,
+                     float* alpha0 = nullptr) {
     sr_status st = check_shape(shape);
     if (st != SR_OK) return st;
     const sr_shape& s = *shape;
@@ -166,6 +167,7 @@ sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float
     a.grid = p.grid;
     a.split_cap = p.split_cap;
     a.routed = routed ? 1 : 0;
+    a.alpha0_out = alpha0;
     if (fused) {
         a.fused = 1;
         a.k0 = fused->k0;
@@ -247,6 +249,14 @@ sr_status sr_dense_decode(const sr_shape* shape, const sr_launch* launch, const 
                           size_t ws_bytes, float* out, void* stream) {
     return run_decode(shape, launch, q, k_cache, v_cache, nullptr, nullptr, nullptr, sm_scale, ws,
                       ws_bytes, out, stream, false);
+}
+
+sr_status sr_dense_decode_alpha0(const sr_shape* shape, const sr_launch* launch, const float* q,
+                                 const void* k_cache, const void* v_cache, float sm_scale, void* ws,
+                                 size_t ws_bytes, float* out, float* alpha0, void* stream) {
+    if (!alpha0) return SR_ERR_INVALID_ARG;
+    return run_decode(shape, launch, q, k_cache, v_cache, nullptr, nullptr, nullptr, sm_scale, ws,
+                      ws_bytes, out, stream, false, nullptr, alpha0);
 }
 
 int32_t sr_splits_for(const sr_shape* shape, const sr_launch* launch, int32_t n_active) {

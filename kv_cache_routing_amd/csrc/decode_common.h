@@ -79,7 +79,17 @@ struct WorkUnit {
 template <int D, int NT, int CHUNK>
 __device__ inline bool map_work(const DecodeArgs& a, WorkUnit& u);
 
-// Last-arriver merge of the S split partials// Last-arriver merge of the S split partials of one item (all threads of the
+// Weight of position 0 in head h of the item: exp2(z0 - M) / L, with z0 the
+// base-2 logit the kernel computed for position 0 and (M, L) the item's final
+// maximum and sum (Eq. (1): alpha_0).
+__device__ inline void write_alpha0(const DecodeArgs& a, const WorkUnit& u, int h, float z0,
+                                    float M, float L) {
+    if (h >= a.group) return;
+    a.alpha0_out[static_cast<int64_t>(u.b) * a.num_q_heads + static_cast<int64_t>(u.g) * a.group +
+                 h] = fast_exp2(z0 - M) / L;
+}
+
+// Last-arriver merge of the S split partials of one item (all threads of the
 // workgroup).  Every global load of the merge is independent of the others,
 // so they are issued in unrolled batches: the merge costs a few memory round
 // trips, not one per split.  Order is fixed: maxima, then per split weights
@@ -105,7 +115,7 @@ __device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, floa
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int32_t G = a.group;
     const int32_t S = u.splits;
-    const float* ml0 = a.part_ml + static_cast<int64_t>(u.slot) * S * 2 * GP;
+    const float* ml0 = a.part_ml + static_cast<int64_t>(u.slot) * S * 3 * GP;
     const float4* acc0 =
         reinterpret_cast<const float4*>(a.part_acc + static_cast<int64_t>(u.slot) * S * GP * D);
 
@@ -114,7 +124,7 @@ __device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, floa
         float mx = kNegInf;
 #pragma unroll 8
         for (int s = t / GP; s < S; s += NT / GP)
-            mx = fmaxf(mx, ml0[static_cast<int64_t>(s) * 2 * GP + h]);
+            mx = fmaxf(mx, ml0[static_cast<int64_t>(s) * 3 * GP + h]);
         for (int o = GP; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
         if (lane < GP) s_red[wave][lane] = mx;
         __syncthreads();
@@ -136,7 +146,7 @@ __device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, floa
         const int n = S - c0 < CH ? S - c0 : CH;
         for (int x = t; x < n * GP; x += NT) {
             const int s = x / GP, h = x - (x / GP) * GP;
-            const float* p = ml0 + static_cast<int64_t>(c0 + s) * 2 * GP;
+            const float* p = ml0 + static_cast<int64_t>(c0 + s) * 3 * GP;
             const float w = merge_weight(p[h], s_M[h]);
             s_w[s][h] = w;
             s_lw[s][h] = w * p[GP + h];
@@ -164,6 +174,7 @@ __device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, floa
         __syncthreads();
     }
     if (t < GP) s_L[t] = lsum;
+    if (t < G && a.alpha0_out) write_alpha0(a, u, t, ml0[2 * GP + t], s_M[t], lsum);
     if constexpr (GROUPS > 1) s_grp[gi][v0] = acc[0];
     __syncthreads();
     if constexpr (GROUPS > 1) {
@@ -202,7 +213,7 @@ __device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, floa
 template <int D, int GP, int NW>
 __device__ inline void finish_split(const DecodeArgs& a, const WorkUnit& u,
                                     const float (*s_m)[GP], const float (*s_l)[GP],
-                                    const float (*s_acc)[GP][D]) {
+                                    const float (*s_acc)[GP][D], const float* s_z0) {
     constexpr int NT = NW * 64;
     const int32_t G = a.group;
     float* out_item = a.out + (static_cast<int64_t>(u.b) * a.num_q_heads +
@@ -221,11 +232,12 @@ __device__ inline void finish_split(const DecodeArgs& a, const WorkUnit& u,
                 L += wt * s_l[w][h];
             }
             out_item[x] = A / L;
+            if (i == 0 && a.alpha0_out) write_alpha0(a, u, h, s_z0[h], M, L);
         }
         return;
     }
 
-    float* pml = a.part_ml + wg * 2 * GP;
+    float* pml = a.part_ml + wg * 3 * GP;
     float* pacc = a.part_acc + wg * GP * D;
     for (int x = threadIdx.x; x < GP * D; x += NT) {
         const int h = x / D, i = x - (x / D) * D;
@@ -241,6 +253,7 @@ __device__ inline void finish_split(const DecodeArgs& a, const WorkUnit& u,
         if (i == 0) {
             pml[h] = M;
             pml[GP + h] = L;
+            pml[2 * GP + h] = s_z0[h];  // meaningful in the split holding position 0
         }
     }
 

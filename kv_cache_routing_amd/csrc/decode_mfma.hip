@@ -58,6 +58,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) float s_p[NW][16][16];  // [pos][head]
     __shared__ float s_m[NW][GP], s_l[NW][GP];
     __shared__ float s_acc[NW][GP][D];
+    __shared__ float s_z0[GP];  // logits of position 0 (split 0 only)
 
     WorkUnit u;
     if (!map_work<D, NW * 64, NW * 16>(a, u)) return;
@@ -135,6 +136,11 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
         if (tile + col >= u.t1) {  // ragged tail: positions past T weigh nothing
 #pragma unroll
             for (int i = 0; i < 4; ++i) s[i] = kNegInf;
+        }
+        if (tile == 0 && col == 0) {  // position 0 is column 0 of tile 0
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * grp + i < GP) s_z0[4 * grp + i] = s[i];
         }
         bool up = false;
 #pragma unroll
@@ -236,7 +242,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
         }
     }
     __syncthreads();
-    finish_split<D, GP, NW>(a, u, s_m, s_l, s_acc);
+    finish_split<D, GP, NW>(a, u, s_m, s_l, s_acc, s_z0);
 }
 
 template <int D, int GP, int NW>

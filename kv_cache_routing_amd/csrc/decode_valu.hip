@@ -50,6 +50,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
 
     __shared__ float s_m[NW][GP], s_l[NW][GP];
     __shared__ float s_acc[NW][GP][D];
+    __shared__ float s_z0[GP];  // logits of position 0 (split 0 only)
 
     WorkUnit u;
     if (!map_work<D, NW * 64, NW * TILE>(a, u)) return;
@@ -126,6 +127,10 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
                 s = group_allreduce_sum<LPT>(s);
                 z[v][h] = valid ? s : kNegInf;
             }
+        }
+        if (tile == 0 && row == 0 && chunk == 0) {  // position 0 is row 0 of tile 0
+#pragma unroll
+            for (int h = 0; h < GP; ++h) s_z0[h] = z[0][h];
         }
         bool up = false;
         float zm[GP];
@@ -205,7 +210,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
         }
     }
     __syncthreads();
-    finish_split<D, GP, NW>(a, u, s_m, s_l, s_acc);
+    finish_split<D, GP, NW>(a, u, s_m, s_l, s_acc, s_z0);
 }
 
 template <typename KV, int D, int GP, int NW>

@@ -39,6 +39,7 @@ struct DecodeArgs {
     uint8_t* mask_out;         // [B][Hkv]  (fused, optional)
     int32_t* list_out;         // [B*Hkv]   (fused, optional)
     int32_t* n_active_out;     // [1]       (fused, optional)
+    float* alpha0_out;         // [B][Hq] weight of position 0 per head (optional)
 };
 
 // The fused route+decode prologue keeps one flag per item in LDS.

@@ -5,7 +5,8 @@ package; the HIP library never does.  Parity-pinned functions are listed in
 ``sinkrouter``'s module docstring; none is unpinned.
 """
 from .sinkrouter import (  # noqa: F401
-    attend_group, cosine, default_scale, dense_decode, group_mask, merge_partials,
-    record_sink, route, route_scores, routed_decode, routed_decode_items,
-    split_k_decode, split_partials, work_list,
+    attend_group, bos_mass, cosine, default_scale, dense_decode, group_mask, merge_partials,
+    oracle_sink_events, proxy_precision_recall, record_sink, route, route_scores,
+    routed_decode, routed_decode_items, split_k_decode, split_partials, threshold_sweep,
+    work_list,
 )

@@ -272,3 +272,67 @@ def split_k_decode(q, k_cache, v_cache, num_splits: int, scale: float | None = N
             out[b, rows] = merge_partials(split_partials(
                 q[b, rows], k_cache[b, g], v_cache[b, g], s, num_splits))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Position-0 attention mass and the routing proxy's precision/recall.
+# pith.science rendering of arXiv 2604.16883: Eq. (1) (Figure 1 caption)
+# gives the weights alpha_i; the Figure 10 caption scores cos(q, K_BOS) as a
+# predictor of an "oracle" sink event defined from the full-attention weight
+# on the first position, per KV group, as a function of the threshold tau
+# (Figure 8 sweeps that threshold).  The event threshold is not printed:
+# reading taken here: a group is an oracle sink when every head puts at least
+# `event_mass` of its attention on position 0.
+# ---------------------------------------------------------------------------
+def bos_mass(q, k_cache, scale: float | None = None):
+    """alpha_0[b, h]: softmax weight of position 0 for every query head."""
+    q = np.asarray(q)
+    B, Hq, d = q.shape
+    Hkv, T = np.asarray(k_cache).shape[1], np.asarray(k_cache).shape[2]
+    G = Hq // Hkv
+    s = default_scale(d) if scale is None else scale
+    out = np.zeros((B, Hq))
+    for b in range(B):
+        for g in range(Hkv):
+            qg = _f64(q[b, g * G:(g + 1) * G])
+            logits = np.empty((G, T))
+            for t0 in range(0, T, _CHUNK):
+                kc = _f64(k_cache[b, g, t0:t0 + _CHUNK])
+                logits[:, t0:t0 + kc.shape[0]] = s * (qg @ kc.T)
+            zmax = logits.max(axis=1)
+            w = np.exp(logits - zmax[:, None])
+            out[b, g * G:(g + 1) * G] = w[:, 0] / w.sum(axis=1)
+    return out
+
+
+def oracle_sink_events(alpha0, num_kv_heads: int, event_mass: float):
+    """[B][Hkv] bool: every head of the group has alpha_0 >= event_mass."""
+    a = np.asarray(alpha0)
+    B, Hq = a.shape
+    G = Hq // num_kv_heads
+    return np.array([[all(a[b, g * G + i] >= event_mass for i in range(G))
+                      for g in range(num_kv_heads)] for b in range(B)])
+
+
+def proxy_precision_recall(predicted, events):
+    """Precision, recall and F1 of predicted sinks against oracle events.
+    Conventions: precision = 1 when nothing is predicted, recall = 1 when
+    there is no event, F1 = 0 when precision + recall = 0."""
+    p = np.asarray(predicted, dtype=bool).reshape(-1)
+    e = np.asarray(events, dtype=bool).reshape(-1)
+    tp = int(np.sum(p & e))
+    fp = int(np.sum(p & ~e))
+    fn = int(np.sum(~p & e))
+    precision = tp / (tp + fp) if tp + fp else 1.0
+    recall = tp / (tp + fn) if tp + fn else 1.0
+    f1 = 2 * precision * recall / (precision + recall) if precision + recall else 0.0
+    return precision, recall, f1
+
+
+def threshold_sweep(scores, events, num_kv_heads: int, taus):
+    """(tau, precision, recall, F1) of the group rule at every tau."""
+    rows = []
+    for tau in taus:
+        pred = group_mask(scores, num_kv_heads, float(tau)).astype(bool)
+        rows.append((float(tau), *proxy_precision_recall(pred, events)))
+    return rows

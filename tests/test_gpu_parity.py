@@ -343,3 +343,52 @@ def test_fused_full_size_70b_layer_sampled():
     ref = oracle.attend_group(q_np[b, g * G:(g + 1) * G], as_numpy(layer.k[b, g]),
                               as_numpy(layer.v[b, g]), 1.0 / math.sqrt(wl.head_dim))
     assert_outputs(out.cpu().numpy()[b, g * G:(g + 1) * G], ref, f"fused 70b item {j}")
+
+
+# --- attention weight of position 0 (alpha_0) -----------------------------------
+ALPHA_CASES = [
+    Workload("a-8b", 1, 32, 8, 128, 9000, "bf16", seed=81, sink_plan=("count", 4)),
+    Workload("a-70b", 2, 64, 8, 128, 3000, "bf16", seed=82, sink_plan=("bernoulli", 0.5)),
+    Workload("a-g3-d64", 1, 12, 4, 64, 777, "bf16", seed=83, sink_plan=("count", 1)),
+    Workload("a-f32", 1, 8, 2, 128, 2048, "f32", seed=84, sink_plan=("count", 1)),
+]
+
+
+@pytest.mark.parametrize("wl", ALPHA_CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("splits", [0, 1, 7])
+def test_dense_alpha0_matches_oracle(wl, kernel, splits):
+    if wl.kv_dtype == "f32" and kernel == "mfma":
+        pytest.skip("matrix-core kernel takes bf16 caches")
+    layer = make_layer(wl)
+    q, k, v = upload(layer)
+    lau = launch(kernel, splits=splits)
+    out, a0 = sr.dense_decode_alpha0(q, k, v, launch=lau)
+    assert torch.equal(out, sr.dense_decode(q, k, v, launch=lau))
+    q_np, k_np, _ = oracle_inputs(layer)
+    ref = oracle.bos_mass(q_np, k_np)
+    got = a0.cpu().numpy().astype(np.float64)
+    rel = np.abs(got - ref) / ref
+    log(f"  alpha0 {wl.name} {kernel} S={splits}: max rel err {rel.max():.2e}, "
+        f"range [{ref.min():.2e}, {ref.max():.2e}]")
+    assert rel.max() <= 1e-4
+
+
+def test_alpha0_fixed_point_bound_on_gpu():
+    d, T = 64, 4096
+    gen = torch.Generator().manual_seed(85)
+    kk = torch.randn((1, 2, T, d), generator=gen)
+    vv = torch.randn((1, 2, T, d), generator=gen)
+    kk[0, :, 0] *= (40.0 / kk[0, :, 0].norm(dim=-1))[:, None]
+    # head 0 of each group aligned with k0 (alpha_0 near 1), head 1 random
+    qq = torch.randn((1, 4, d), generator=gen)
+    qq[0, 0] = kk[0, 0, 0] / kk[0, 0, 0].norm() * 2.0
+    qq[0, 2] = kk[0, 1, 0] / kk[0, 1, 0].norm() * 2.0
+    out, a0 = sr.dense_decode_alpha0(qq.cuda(), kk.cuda(), vv.cuda())
+    out, a0 = out.cpu().double(), a0.cpu().double()
+    for h in range(4):
+        g = h // 2
+        spread = (vv[0, g, 1:] - vv[0, g, 0]).norm(dim=-1).max().double()
+        lhs = (out[0, h] - vv[0, g, 0].double()).norm()
+        assert lhs <= (1 - a0[0, h]) * spread * (1 + 1e-4) + 1e-6, (h, lhs, a0[0, h])
+    assert a0[0, 0] > 0.5 and a0[0, 2] > 0.5

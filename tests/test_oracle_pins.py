@@ -342,3 +342,52 @@ def test_threshold_tie_counts_as_sink():
     # layers keep every score at least 0.05 away from tau, so ties never occur.
     assert orc.group_mask(np.array([[0.5, 0.5]]), 1, 0.5).tolist() == [[1]]
     assert orc.group_mask(np.array([[0.5, np.nextafter(0.5, 0.0)]]), 1, 0.5).tolist() == [[0]]
+
+
+# --- position-0 attention mass and the proxy's precision/recall --------------
+def test_bos_mass_against_torch_softmax_weights():
+    q, k, v = rand_layer(71, 2, 8, 2, 150, 32, k0_norm=20.0)
+    a0 = oracle.bos_mass(q, k)
+    qt = torch.from_numpy(q)
+    kt = torch.from_numpy(np.repeat(k, 4, axis=1))
+    w = torch.softmax((qt[:, :, None, :] @ kt.transpose(-1, -2)).squeeze(2) / math.sqrt(32), dim=-1)
+    np.testing.assert_allclose(a0, w[..., 0].numpy(), rtol=0, atol=1e-14)
+
+
+def test_bos_mass_closed_forms():
+    q, k, v = rand_layer(72, 1, 4, 2, 1, 16)
+    assert np.array_equal(oracle.bos_mass(q, k), np.ones((1, 4)))       # T = 1
+    q, k, v = rand_layer(73, 1, 4, 2, 37, 16)
+    q[:] = 0.0
+    np.testing.assert_allclose(oracle.bos_mass(q, k), np.full((1, 4), 1 / 37), rtol=0, atol=1e-15)
+    # dominant position 0: 1 - alpha_0 = sum_{t>=1} alpha_t <= (T-1) e^{-delta}
+    d, T = 64, 2048
+    rng = np.random.default_rng(74)
+    k = rng.standard_normal((1, 1, T, d))
+    k[0, 0, 0] *= 300.0 / np.linalg.norm(k[0, 0, 0])
+    q = (k[0, 0, 0] / np.linalg.norm(k[0, 0, 0]))[None, None, :]
+    z = (k[0, 0] @ q[0, 0]) / 8.0
+    delta = z[0] - z[1:].max()
+    assert 1.0 - oracle.bos_mass(q, k)[0, 0] <= (T - 1) * math.exp(-delta) + 1e-15
+
+
+def test_precision_recall_hand_counts():
+    pred = np.array([[1, 1, 0, 0], [1, 0, 1, 0]], dtype=bool)
+    ev = np.array([[1, 0, 0, 1], [1, 0, 1, 1]], dtype=bool)
+    # tp = 3 (00, 10, 12), fp = 1 (01), fn = 2 (03, 13)
+    p, r, f = oracle.proxy_precision_recall(pred, ev)
+    assert (p, r) == (0.75, 0.6)
+    assert abs(f - 2 * 0.75 * 0.6 / 1.35) < 1e-15
+    assert oracle.proxy_precision_recall(np.zeros(3, bool), np.zeros(3, bool)) == (1.0, 1.0, 1.0)
+    assert oracle.proxy_precision_recall(np.zeros(3, bool), np.ones(3, bool))[:2] == (1.0, 0.0)
+
+
+def test_threshold_sweep_is_monotone_in_predictions():
+    # raising tau can only remove predicted sinks: recall never increases
+    rng = np.random.default_rng(75)
+    scores = rng.uniform(-1, 1, size=(4, 16))
+    events = rng.random((4, 8)) < 0.5
+    rows = oracle.threshold_sweep(scores, events, 8, np.linspace(-1, 1, 21))
+    recalls = [r[2] for r in rows]
+    assert all(a >= b - 1e-15 for a, b in zip(recalls, recalls[1:]))
+    assert rows[0][2] == 1.0          # tau = -1: every group predicted

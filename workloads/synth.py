@@ -55,6 +55,7 @@ class Workload:
     seed: int
     sink_plan: tuple = ("none",)
     tau: float = 0.5
+    k0_norm: float = K0_NORM
     tags: dict = field(default_factory=dict, compare=False)
 
     @property
@@ -118,7 +119,7 @@ def make_k0(wl: Workload) -> torch.Tensor:
         for g in range(Hkv):
             row = torch.randn(d, generator=_stream(wl.seed + b, _TAG_K0 + g),
                               dtype=torch.float32)
-            k0[b, g] = row * (K0_NORM / row.norm())
+            k0[b, g] = row * (wl.k0_norm / row.norm())
     return k0.to(wl.torch_dtype).to(torch.float32)
 
 
