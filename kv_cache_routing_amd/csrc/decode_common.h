@@ -79,6 +79,12 @@ struct WorkUnit {
 template <int D, int NT, int CHUNK>
 __device__ inline bool map_work(const DecodeArgs& a, WorkUnit& u);
 
+// A store that is visible to every XCD once acknowledged (device-scope
+// coherent: it is written through the local L2 instead of staying dirty).
+__device__ inline void store_coherent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Weight of position 0 in head h of the item: exp2(z0 - M) / L, with z0 the
 // base-2 logit the kernel computed for position 0 and (M, L) the item's final
 // maximum and sum (Eq. (1): alpha_0).
@@ -249,22 +255,24 @@ __device__ inline void finish_split(const DecodeArgs& a, const WorkUnit& u,
             A += wt * s_acc[w][h][i];
             L += wt * s_l[w][h];
         }
-        pacc[x] = A;
+        store_coherent(pacc + x, A);
         if (i == 0) {
-            pml[h] = M;
-            pml[GP + h] = L;
-            pml[2 * GP + h] = s_z0[h];  // meaningful in the split holding position 0
+            store_coherent(pml + h, M);
+            store_coherent(pml + GP + h, L);
+            store_coherent(pml + 2 * GP + h, s_z0[h]);  // meaningful in the split with position 0
         }
     }
 
-    // Publish the partial and take a ticket.  Every wave releases its own
-    // stores at agent scope (an L2 write-back, so the other XCDs see them)
-    // before the barrier; thread 0 then moves the ticket.  Only the workgroup
-    // that draws the last ticket pays for an acquire (an L2 invalidation): a
-    // sequentially consistent fence in every workgroup would invalidate this
-    // XCD's L2 under the other workgroups' streaming loads.
+    // Publish the partial and take a ticket.  The partial went out with
+    // device-coherent stores, which write through this XCD's L2; each wave
+    // waits until its stores are acknowledged, then thread 0 moves the ticket.
+    // An agent-scope release fence here would instead write back the whole
+    // L2 of the XCD in every wave of every workgroup at the end of the launch
+    // (measured ~10 us of tail).  Only the workgroup that draws the last
+    // ticket pays for an acquire (an L2 invalidation) before it reads the
+    // other partials.
     __shared__ int s_last;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt = expcnt = lgkmcnt = 0: stores acknowledged
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t prev = __hip_atomic_fetch_add(a.tickets + u.slot, 1u, __ATOMIC_RELAXED,

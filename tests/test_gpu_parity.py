@@ -392,3 +392,34 @@ def test_alpha0_fixed_point_bound_on_gpu():
         lhs = (out[0, h] - vv[0, g, 0].double()).norm()
         assert lhs <= (1 - a0[0, h]) * spread * (1 + 1e-4) + 1e-6, (h, lhs, a0[0, h])
     assert a0[0, 0] > 0.5 and a0[0, 2] > 0.5
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+@pytest.mark.parametrize("splits", [0, 13])
+def test_alternating_layers_on_one_workspace(kernel, splits):
+    # Two different layers through the same workspace, interleaved: a split
+    # partial that is not yet visible to the merging workgroup would be read
+    # from the other layer's previous call and change the result.
+    wls = [Workload(f"alt{i}", 1, 32, 8, 128, 20000 + 37 * i, "bf16", seed=91 + i,
+                    sink_plan=("count", 3)) for i in range(2)]
+    layers = [make_layer(w) for w in wls]
+    dev = [upload(L) for L in layers]
+    lau = launch(kernel, splits=splits)
+    T = max(w.seq_len for w in wls)
+    shape = sr.make_shape(dev[0][0], dev[0][1], dev[0][2])
+    ws = sr.Workspace(shape, lau, dev[0][0].device)
+    k0v0 = [sr.record_sink(k, v) for _, k, v in dev]
+    refs = [sr.route_decode(q, k, v, k0, v0, 0.5, launch=lau, ws=ws)[0].clone()
+            for (q, k, v), (k0, v0) in zip(dev, k0v0)]
+    dense_refs = [sr.dense_decode(q, k, v, launch=lau, ws=ws).clone() for q, k, v in dev]
+    for it in range(150):
+        i = it % 2
+        q, k, v = dev[i]
+        k0, v0 = k0v0[i]
+        out, _ = sr.route_decode(q, k, v, k0, v0, 0.5, launch=lau, ws=ws)
+        assert torch.equal(out, refs[i]), it
+        assert torch.equal(sr.dense_decode(q, k, v, launch=lau, ws=ws), dense_refs[i]), it
+    for (q, k, v), L, r in zip(dev, layers, refs):
+        q_np, k_np, v_np = oracle_inputs(L)
+        ref = oracle.dense_decode(q_np, k_np, v_np)
+        assert_outputs(sr.dense_decode(q, k, v, launch=lau, ws=ws).cpu().numpy(), ref, "alt dense")
