@@ -229,6 +229,141 @@ def cpu_baseline(layer, n_active_items, budget_s=12.0):
     }
 
 
+def decode_layers_report(sr, torch, args):
+    """Per-token attention over a stack of layers: each layer rotates the new
+    token's q and k and appends k, v (sr_rope_append), then runs routed
+    attention (sr_route_decode) inside the gated layer range and dense
+    attention (sr_dense_decode) outside it.  Caches come from the seeded GPU
+    generator (timing only; every kernel's parity is tested elsewhere).  Sink
+    groups' queries are built in the rotated frame (0.9 k0/|k0| + 0.05 noise)
+    and turned back by -pos on the host, so the routing sees planted sinks."""
+    from workloads import rope_inv_freq
+    from workloads.synth import K0_NORM
+    L, T0, N = args.decode_layers, args.context, args.tokens
+    B, Hq, Hkv, d = 1, 32, 8, 128
+    G = Hq // Hkv
+    start, end = args.layer_range if args.layer_range else (0, L - 1)
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(9000)
+    cap = T0 + N
+    caches = []
+    for layer in range(L):
+        k = torch.randn((B, Hkv, cap, d), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((B, Hkv, cap, d), generator=gen, device=dev).to(torch.bfloat16)
+        k0 = k[:, :, 0].float()
+        k[:, :, 0] = (k0 * (K0_NORM / k0.norm(dim=-1, keepdim=True))).to(torch.bfloat16)
+        caches.append((k, v))
+    inv_freq = rope_inv_freq(d)
+    f64 = inv_freq.double()
+    hgen = torch.Generator().manual_seed(9001)
+    plans = []  # per (token, layer): q_pre, k_new, v_new
+    sinks = torch.zeros((L, Hkv), dtype=torch.bool)
+    for layer in range(L):
+        sinks[layer, torch.randperm(Hkv, generator=hgen)[:Hkv // 2]] = True
+    for t in range(N):
+        pos = T0 + t
+        ang = -pos * f64
+        c, s = torch.cos(ang), torch.sin(ang)
+        row = []
+        for layer in range(L):
+            k0 = caches[layer][0][0, :, 0].double().cpu()
+            target = torch.randn((B, Hq, d), generator=hgen, dtype=torch.float64)
+            for h in range(Hq):
+                if sinks[layer, h // G]:
+                    target[0, h] = 0.9 * k0[h // G] / k0[h // G].norm() + 0.05 * target[0, h]
+            lo, hi = target[..., : d // 2], target[..., d // 2:]
+            q_pre = torch.cat([lo * c - hi * s, hi * c + lo * s], dim=-1).float()
+            kn = torch.randn((B, Hkv, d), generator=hgen)
+            vn = torch.randn((B, Hkv, d), generator=hgen)
+            row.append((q_pre.to(dev), kn.to(dev), vn.to(dev)))
+        plans.append(row)
+    freq = inv_freq.to(dev)
+    k0v0 = [sr.record_sink(k[:, :, :T0], v[:, :, :T0]) for k, v in caches]
+    lau = sr.make_launch()
+    shape = sr.make_shape(plans[0][0][0], caches[0][0][:, :, :cap], caches[0][1][:, :, :cap])
+    ws = sr.Workspace(shape, lau, dev)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    q_rot = torch.empty_like(out)
+    n_active = torch.zeros(L, dtype=torch.int32, device=dev)
+    routing = [sr.Routing(torch.empty((B, Hq), device=dev), torch.empty((B, Hkv), dtype=torch.uint8,
+                                                                          device=dev),
+                          torch.empty(B * Hkv, dtype=torch.int32, device=dev), n_active[i:i + 1])
+               for i in range(L)]
+
+    q_rots = [[torch.empty_like(out) for _ in range(L)] for _ in range(N)]
+
+    def token(t, routed=True, attend=True, append=True):
+        pos = T0 + t
+        for layer in range(L):
+            k, v = caches[layer]
+            qp, kn, vn = plans[t][layer]
+            q_rot = q_rots[t][layer]
+            if append:
+                sr.rope_append(qp, kn, vn, k, v, pos, freq, q_out=q_rot)
+            if not attend:
+                continue
+            kv = (k[:, :, :pos + 1], v[:, :, :pos + 1])
+            if routed and start <= layer <= end:
+                k0, v0 = k0v0[layer]
+                sr.route_decode(q_rot, *kv, k0, v0, 0.5, launch=lau, ws=ws, out=out,
+                                routing=routing[layer])
+            else:
+                sr.dense_decode(q_rot, *kv, launch=lau, ws=ws, out=out)
+
+    # Eager pass: appends every token, fills the rotated queries.
+    for t in range(N):
+        token(t)
+    torch.cuda.synchronize()
+    active = int(n_active.sum())
+
+    # One HIP graph per token and per variant, replayed like a serving loop
+    # (host launch overhead out of the measurement).  Replays rewrite the same
+    # cache positions with the same values.
+    def graphs(**kw):
+        gs = []
+        for t in range(N):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                token(t, **kw)
+            gs.append(g)
+        return gs
+
+    stream = torch.cuda.current_stream()
+
+    def run(gs, reps=3):
+        for g in gs:
+            g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            for g in gs:
+                g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (reps * len(gs)) * 1e3  # us per token
+
+    routed = run(graphs(routed=True))
+    dense = run(graphs(routed=False))
+    append_only = run(graphs(attend=False))
+    attend_routed = run(graphs(routed=True, append=False))
+    attend_dense = run(graphs(routed=False, append=False))
+    gated = sum(1 for layer in range(L) if start <= layer <= end)
+    rep = {"decode_layers": {
+        "layers": L, "context": T0, "tokens": N, "routed_layers": [start, end],
+        "shape": f"B={B} Hq={Hq} Hkv={Hkv} d={d} bf16 K/V, half of the groups planted as sinks",
+        "timing": "one HIP graph per token (rotary + append + attention for every layer)",
+        "active_groups_last_token": active, "groups_routed_layers": gated * B * Hkv,
+        "us_per_token_routed": round(routed, 1), "us_per_token_dense": round(dense, 1),
+        "speedup": round(dense / routed, 4),
+        "composition_us_per_token": {"rope_append": round(append_only, 1),
+                                     "attention_routed": round(attend_routed, 1),
+                                     "attention_dense": round(attend_dense, 1)},
+        "kv_gib_per_token_dense": round(L * 2 * B * Hkv * T0 * d * 2 / 2 ** 30, 2)}}
+    print(json.dumps(rep), flush=True)
+    return 0
+
+
 def bos_proxy_report(sr, torch):
     """Routing proxy vs position-0 attention mass, GPU outputs only."""
     from kv_cache_routing_amd import proxy
@@ -275,6 +410,13 @@ def main():
                     help="precision/recall of the cosine routing rule against position-0 "
                          "attention-mass events (alpha_0 >= 0.5 in every head) over a tau "
                          "sweep, on synthetic 8B-shaped layers at several k0 norms, and exit")
+    ap.add_argument("--decode-layers", type=int, default=0, metavar="L",
+                    help="per-token decode over L layers (rotary + append, then routed or "
+                         "dense attention per layer) and exit")
+    ap.add_argument("--context", type=int, default=131072, help="context of --decode-layers")
+    ap.add_argument("--tokens", type=int, default=8, help="decode steps of --decode-layers")
+    ap.add_argument("--layer-range", type=int, nargs=2, default=None, metavar=("START", "END"),
+                    help="layers routed by --decode-layers (inclusive); the rest run dense")
     ap.add_argument("--read-ceiling", action="store_true",
                     help="print the HBM read-probe sweep over the layer caches and exit")
     ap.add_argument("--roofline-only", action="store_true",
@@ -303,6 +445,8 @@ def main():
 
     if args.bos_proxy:
         return bos_proxy_report(sr, torch)
+    if args.decode_layers:
+        return decode_layers_report(sr, torch, args)
 
     names = {w.name: w for w in CONFIGS}
     names.update({sweep(L8B_256K_B4, f).name: sweep(L8B_256K_B4, f) for f in SINK_FRACTIONS})

@@ -123,6 +123,22 @@ sr_status sr_route(const sr_shape* shape, const float* q, const float* k0, float
                    float* scores, uint8_t* mask, int32_t* work_list, int32_t* n_active,
                    void* stream);
 
+/* Decode-step neighbour: rotary embedding of the new token, then the append
+ * of its key and value (README decode-time steps: routing compares the
+ * RoPE-rotated query with the position-0 key).  Rotary form: element i pairs
+ * with element i + d/2 and both turn by the angle pos * inv_freq[i]; angles,
+ * sines, cosines and rotations are computed in fp64.
+ *   q_new, k_new, v_new: fp32 [B][Hq][d], [B][Hkv][d], [B][Hkv][d], unrotated.
+ *   inv_freq: fp32 [d/2] rotary frequencies (any scaling scheme).
+ *   pos: position of the new token, 0 <= pos < shape->seq_len, where
+ *        shape->seq_len is the caches' capacity.
+ *   q_out: fp32 [B][Hq][d], the rotated query (rounded once to fp32).
+ *   k_cache[b][g][pos][:] = rotated key, v_cache[b][g][pos][:] = value, each
+ *   rounded once to the cache dtype (nearest even); nothing else is written. */
+sr_status sr_rope_append(const sr_shape* shape, const float* q_new, const float* k_new,
+                         const float* v_new, const float* inv_freq, int64_t pos, float* q_out,
+                         void* k_cache, void* v_cache, void* stream);
+
 /* Bytes of scratch the decode calls need for this shape and launch policy:
  * per-workgroup split partials (m, l, the position-0 logit and acc, fp32)
  * plus one ticket per item.

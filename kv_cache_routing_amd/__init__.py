@@ -23,7 +23,7 @@ from ._native import (SR_KERNEL_AUTO, SR_KERNEL_MFMA, SR_KERNEL_VALU,  # noqa: F
                       SinkRouteError)
 
 __all__ = ["record_sink", "route", "decode_attn", "route_decode", "dense_decode",
-           "dense_decode_alpha0", "Workspace",
+           "dense_decode_alpha0", "rope_append", "Workspace",
            "make_shape",
            "make_launch", "splits_for", "grid_size", "SinkRouteError", "Routing",
            "SR_KERNEL_AUTO", "SR_KERNEL_VALU", "SR_KERNEL_MFMA"]
@@ -92,6 +92,23 @@ class Workspace:
 
     def fits(self, shape, launch) -> bool:
         return int(N.lib.sr_workspace_bytes(ctypes.byref(shape), _lp(launch))) <= self.nbytes
+
+
+def rope_append(q_new, k_new, v_new, k_cache, v_cache, pos: int, inv_freq,
+                q_out: torch.Tensor | None = None):
+    """Rotate the new token's query/key to `pos`, append key and value to the
+    full-capacity caches [B][Hkv][T_max][d] at `pos`; returns the rotated q."""
+    _need_cuda(q_new, k_new, v_new, k_cache, v_cache, inv_freq)
+    for t in (q_new, k_new, v_new, inv_freq):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("q_new, k_new, v_new, inv_freq are contiguous fp32")
+    shape = make_shape(q_new, k_cache, v_cache)
+    if q_out is None:
+        q_out = torch.empty_like(q_new)
+    N.check(N.lib.sr_rope_append(ctypes.byref(shape), _ptr(q_new), _ptr(k_new), _ptr(v_new),
+                                 _ptr(inv_freq), int(pos), _ptr(q_out), _ptr(k_cache),
+                                 _ptr(v_cache), _stream()), "sr_rope_append")
+    return q_out
 
 
 def record_sink(k: torch.Tensor, v: torch.Tensor, q_heads: int | None = None):

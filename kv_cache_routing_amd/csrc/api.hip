@@ -213,6 +213,19 @@ sr_status sr_route(const sr_shape* shape, const float* q, const float* k0, float
     return e == hipSuccess ? SR_OK : SR_ERR_HIP;
 }
 
+sr_status sr_rope_append(const sr_shape* shape, const float* q_new, const float* k_new,
+                         const float* v_new, const float* inv_freq, int64_t pos, float* q_out,
+                         void* k_cache, void* v_cache, void* stream) {
+    sr_status st = check_shape(shape);
+    if (st != SR_OK) return st;
+    if ((st = check_caches(*shape, k_cache, v_cache)) != SR_OK) return st;
+    if (!q_new || !k_new || !v_new || !inv_freq || !q_out) return SR_ERR_INVALID_ARG;
+    if (pos < 0 || pos >= shape->seq_len) return SR_ERR_INVALID_ARG;
+    hipError_t e = launch_rope_append(*shape, q_new, k_new, v_new, inv_freq, pos, q_out, k_cache,
+                                      v_cache, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SR_OK : SR_ERR_HIP;
+}
+
 size_t sr_workspace_bytes(const sr_shape* shape, const sr_launch* launch) {
     if (check_shape(shape) != SR_OK) return 0;
     Plan p;

@@ -75,6 +75,9 @@ hipError_t launch_route(const sr_shape& s, const float* q, const float* k0, floa
                         float* scores, uint8_t* mask, int32_t* work_list, int32_t* n_active,
                         hipStream_t st);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
+hipError_t launch_rope_append(const sr_shape& s, const float* q_new, const float* k_new,
+                              const float* v_new, const float* inv_freq, int64_t pos,
+                              float* q_out, void* k_cache, void* v_cache, hipStream_t st);
 hipError_t launch_decode_valu(const sr_shape& s, const DecodeArgs& a, int gp, int waves,
                               hipStream_t st);
 hipError_t launch_decode_mfma(const sr_shape& s, const DecodeArgs& a, int gp, int waves,

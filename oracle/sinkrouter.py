@@ -336,3 +336,43 @@ def threshold_sweep(scores, events, num_kv_heads: int, taus):
         pred = group_mask(scores, num_kv_heads, float(tau)).astype(bool)
         rows.append((float(tau), *proxy_precision_recall(pred, events)))
     return rows
+
+
+# ---------------------------------------------------------------------------
+# Decode-step neighbours: rotary position embedding of the new token's query
+# and key, and the append of its key and value to the caches.  README
+# decode-time steps: routing compares the *RoPE* query with the position-0
+# key, so the query is rotated first.  Reading (the pages do not print the
+# rotary form): the Hugging Face Llama "rotate half" convention, element i
+# paired with element i + d/2, angle pos * inv_freq[i], in exact arithmetic.
+# ---------------------------------------------------------------------------
+def rope(x, pos: int, inv_freq):
+    """Rotate the last axis of x (..., d) to position pos (fp64)."""
+    x = _f64(x)
+    d = x.shape[-1]
+    f = _f64(inv_freq)
+    ang = float(pos) * f
+    c, s = np.cos(ang), np.sin(ang)
+    lo, hi = x[..., : d // 2], x[..., d // 2:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+
+
+def round_bf16(x):
+    """fp64 -> bf16 value (as fp64), rounding to nearest even in one step."""
+    x = _f64(x)
+    m, e = np.frexp(x)                      # x = m * 2^e, 0.5 <= |m| < 1
+    scaled = np.ldexp(m, 8)                 # 8 significant bits before the point
+    return np.ldexp(np.round(scaled), e - 8)  # np.round is round-half-even
+
+
+def rope_append(q_new, k_new, v_new, k_cache, v_cache, pos: int, inv_freq, bf16: bool):
+    """Return (rotated q fp64, caches with the rotated key and the value
+    written at position pos, rounded to bf16 when the caches are bf16)."""
+    q_rot = rope(q_new, pos, inv_freq)
+    k_rot = rope(k_new, pos, inv_freq)
+    v = _f64(v_new)
+    kc = _f64(k_cache).copy()
+    vc = _f64(v_cache).copy()
+    kc[:, :, pos] = round_bf16(k_rot) if bf16 else k_rot.astype(np.float32)
+    vc[:, :, pos] = round_bf16(v) if bf16 else v.astype(np.float32)
+    return q_rot, kc, vc

@@ -423,3 +423,117 @@ def test_alternating_layers_on_one_workspace(kernel, splits):
         q_np, k_np, v_np = oracle_inputs(L)
         ref = oracle.dense_decode(q_np, k_np, v_np)
         assert_outputs(sr.dense_decode(q, k, v, launch=lau, ws=ws).cpu().numpy(), ref, "alt dense")
+
+
+# --- decode-step neighbours: rotary embedding and cache append -------------------
+from workloads import rope_inv_freq  # noqa: E402
+
+
+def _bf16_ulp(x):
+    return np.ldexp(1.0, np.frexp(np.abs(x))[1] - 8)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128)])
+@pytest.mark.parametrize("pos", [0, 1, 777, 131071])
+def test_rope_append_matches_oracle(dtype, d, pos):
+    B, Hq, Hkv, T = 2, 16, 4, 131072 if pos == 131071 else 1024
+    gen = torch.Generator().manual_seed(111 + pos)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kc = torch.randn((B, Hkv, T, d), generator=gen).to(tdt)
+    vc = torch.randn((B, Hkv, T, d), generator=gen).to(tdt)
+    qn, kn, vn = (torch.randn((B, H, d), generator=gen) for H in (Hq, Hkv, Hkv))
+    f = rope_inv_freq(d)
+    kd, vd = kc.cuda(), vc.cuda()
+    q_rot = sr.rope_append(qn.cuda(), kn.cuda(), vn.cuda(), kd, vd, pos, f.cuda()).cpu()
+    ref_q = oracle.rope(qn.numpy(), pos, f.numpy())
+    err = np.abs(q_rot.numpy().astype(np.float64) - ref_q)
+    assert (err <= np.abs(ref_q) * 2 ** -23 + 1e-30).all(), err.max()
+    if pos == 0:
+        assert torch.equal(q_rot, qn)
+    kd_np, vd_np = as_numpy(kd.cpu()).astype(np.float64), as_numpy(vd.cpu()).astype(np.float64)
+    ref_k = oracle.rope(kn.numpy(), pos, f.numpy())
+    if dtype == "bf16":
+        assert (np.abs(kd_np[:, :, pos] - ref_k) <= _bf16_ulp(ref_k)).all()
+        assert np.array_equal(vd_np[:, :, pos], oracle.round_bf16(vn.numpy().astype(np.float64)))
+    else:
+        assert (np.abs(kd_np[:, :, pos] - ref_k) <= np.abs(ref_k) * 2 ** -23 + 1e-30).all()
+        assert np.array_equal(vd_np[:, :, pos], vn.numpy().astype(np.float64))
+    keep = torch.ones(T, dtype=torch.bool)
+    keep[pos] = False
+    assert torch.equal(kd.cpu()[:, :, keep], kc[:, :, keep])
+    assert torch.equal(vd.cpu()[:, :, keep], vc[:, :, keep])
+
+
+def test_decode_steps_with_append_match_oracle():
+    # three decode steps: rotate + append the new token, then routed decode
+    # over the grown cache; compare with the oracle stepping the same way
+    wl = Workload("steps", 1, 32, 8, 128, 3000, "bf16", seed=121, sink_plan=("count", 4))
+    layer = make_layer(wl)
+    cap = wl.seq_len + 8
+    kc = torch.zeros((1, 8, cap, 128), dtype=torch.bfloat16)
+    vc = torch.zeros_like(kc)
+    kc[:, :, :wl.seq_len] = layer.k
+    vc[:, :, :wl.seq_len] = layer.v
+    kd, vd = kc.cuda(), vc.cuda()
+    f = rope_inv_freq(128)
+    k_np, v_np = as_numpy(kc).astype(np.float64), as_numpy(vc).astype(np.float64)
+    gen = torch.Generator().manual_seed(122)
+    k0, v0 = sr.record_sink(kd[:, :, :wl.seq_len], vd[:, :, :wl.seq_len])
+    for step in range(3):
+        pos = wl.seq_len + step
+        qn, kn, vn = (torch.randn((1, H, 128), generator=gen) for H in (32, 8, 8))
+        q_rot = sr.rope_append(qn.cuda(), kn.cuda(), vn.cuda(), kd, vd, pos, f.cuda())
+        T = pos + 1
+        out, r = sr.route_decode(q_rot, kd[:, :, :T], vd[:, :, :T], k0, v0, 0.5)
+        q_ref, k_np, v_np = oracle.rope_append(qn.numpy(), kn.numpy(), vn.numpy(), k_np, v_np,
+                                               pos, f.numpy(), bf16=True)
+        # the device appended key may differ from the oracle's by one bf16 ulp:
+        # attend with the device's stored cache, compare rotation separately
+        k_dev = as_numpy(kd.cpu()).astype(np.float64)
+        assert (np.abs(k_dev[:, :, pos] - k_np[:, :, pos]) <= _bf16_ulp(k_np[:, :, pos])).all()
+        q_dev = q_rot.cpu().numpy().astype(np.float64)
+        assert np.abs(q_dev - q_ref).max() <= 1e-5
+        _, mask, wl_ref, n_act = oracle.route(q_dev, k_dev[:, :, 0], 0.5)
+        assert np.array_equal(r.mask.cpu().numpy(), mask)
+        ref = oracle.routed_decode(q_dev, k_dev[:, :, :T], v_np[:, :, :T], v_np[:, :, 0], mask)
+        assert_outputs(out.cpu().numpy(), ref, f"step {step} T={T}")
+
+
+def test_graph_replay_matches_eager():
+    # The decode calls allocate nothing and never wait for the host, so they
+    # can be captured; replay several times with eager work in between and
+    # compare every replay with the eager result.
+    wl = Workload("graph", 1, 32, 8, 128, 10000, "bf16", seed=131, sink_plan=("count", 4))
+    layer = make_layer(wl)
+    q, k, v = upload(layer)
+    lau = launch("auto")
+    ws = sr.Workspace(sr.make_shape(q, k, v), lau, q.device)
+    k0, v0 = sr.record_sink(k, v)
+    r = sr.route(q, k0, wl.tau)
+    out_f = torch.empty_like(q)
+    out_t = torch.empty_like(q)
+    out_d = torch.empty_like(q)
+    rf = sr.route(q, k0, wl.tau)
+    eager_f = sr.route_decode(q, k, v, k0, v0, wl.tau, launch=lau, ws=ws, routing=rf)[0].clone()
+    sr.route(q, k0, wl.tau, out=r)
+    eager_t = sr.decode_attn(q, k, v, v0, r.work_list, r.n_active, launch=lau, ws=ws).clone()
+    eager_d = sr.dense_decode(q, k, v, launch=lau, ws=ws).clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sr.route_decode(q, k, v, k0, v0, wl.tau, launch=lau, ws=ws, out=out_f, routing=rf)
+        sr.route(q, k0, wl.tau, out=r)
+        sr.decode_attn(q, k, v, v0, r.work_list, r.n_active, launch=lau, ws=ws, out=out_t)
+        sr.dense_decode(q, k, v, launch=lau, ws=ws, out=out_d)
+    for it in range(5):
+        out_f.zero_()
+        out_t.zero_()
+        out_d.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_f, eager_f), it
+        assert torch.equal(out_t, eager_t), it
+        assert torch.equal(out_d, eager_d), it
+        sr.dense_decode(q, k, v, launch=lau, ws=ws)  # eager work between replays
+        torch.cuda.synchronize()
+    assert int(ticket_region(ws, 8).abs().sum()) == 0

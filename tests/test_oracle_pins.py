@@ -391,3 +391,56 @@ def test_threshold_sweep_is_monotone_in_predictions():
     recalls = [r[2] for r in rows]
     assert all(a >= b - 1e-15 for a, b in zip(recalls, recalls[1:]))
     assert rows[0][2] == 1.0          # tau = -1: every group predicted
+
+
+# --- rotary embedding and cache append ------------------------------------------
+def _inv_freq(d, base=500000.0):
+    return base ** (-np.arange(0, d, 2) / d)
+
+
+def test_rope_identity_norm_and_complex_form():
+    rng = np.random.default_rng(101)
+    x = rng.standard_normal((3, 5, 128))
+    f = _inv_freq(128)
+    assert np.array_equal(oracle.rope(x, 0, f), x)                        # position 0
+    y = oracle.rope(x, 12345, f)
+    np.testing.assert_allclose(np.hypot(y[..., :64], y[..., 64:]),
+                               np.hypot(x[..., :64], x[..., 64:]), rtol=1e-13)
+    z = (x[..., :64] + 1j * x[..., 64:]) * np.exp(1j * 12345 * f)         # complex form
+    np.testing.assert_allclose(y, np.concatenate([z.real, z.imag], axis=-1), rtol=0, atol=1e-12)
+
+
+def test_rope_relative_position_and_composition():
+    rng = np.random.default_rng(102)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    f = _inv_freq(64, 10000.0)
+    a = oracle.rope(q, 700, f) @ oracle.rope(k, 650, f)
+    b = oracle.rope(q, 50, f) @ k
+    assert abs(a - b) < 1e-11
+    np.testing.assert_allclose(oracle.rope(oracle.rope(q, 300, f), 400, f), oracle.rope(q, 700, f),
+                               rtol=0, atol=1e-12)
+
+
+def test_round_bf16_matches_torch_on_float32_values_and_ties():
+    rng = np.random.default_rng(103)
+    x = rng.standard_normal(100000).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.round_bf16(x.astype(np.float64)), ref)
+    # exact ties round to even; one step avoids double rounding
+    assert oracle.round_bf16(np.array([1.0 + 2 ** -8]))[0] == 1.0
+    assert oracle.round_bf16(np.array([1.0 + 3 * 2 ** -8]))[0] == 1.0 + 2 ** -6
+    assert oracle.round_bf16(np.array([1.0 + 2 ** -8 + 2 ** -40]))[0] == 1.0 + 2 ** -7
+
+
+def test_rope_append_writes_only_position_pos():
+    rng = np.random.default_rng(104)
+    B, Hq, Hkv, T, d = 2, 8, 2, 10, 32
+    q, k, v = (rng.standard_normal((B, H, d)) for H in (Hq, Hkv, Hkv))
+    kc = rng.standard_normal((B, Hkv, T, d))
+    vc = rng.standard_normal((B, Hkv, T, d))
+    f = _inv_freq(d)
+    q_rot, kc2, vc2 = oracle.rope_append(q, k, v, kc, vc, 7, f, bf16=False)
+    keep = [t for t in range(T) if t != 7]
+    assert np.array_equal(kc2[:, :, keep], kc[:, :, keep]) and np.array_equal(vc2[:, :, keep], vc[:, :, keep])
+    np.testing.assert_allclose(kc2[:, :, 7], oracle.rope(k, 7, f).astype(np.float32), rtol=0, atol=0)
+    np.testing.assert_allclose(q_rot, oracle.rope(q, 7, f), rtol=0, atol=0)

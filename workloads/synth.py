@@ -201,6 +201,12 @@ def make_layer(wl: Workload, *, threads: int | None = None) -> Layer:
     return Layer(wl, q, k, v, planted)
 
 
+def rope_inv_freq(head_dim: int, base: float = 500000.0) -> torch.Tensor:
+    """Rotary frequencies base^(-2i/d), fp32 [d/2] (Llama-3.1 uses base 5e5)."""
+    i = torch.arange(0, head_dim, 2, dtype=torch.float64)
+    return (base ** (-i / head_dim)).to(torch.float32)
+
+
 def as_numpy(t: torch.Tensor):
     """Exact host copy for the oracle: bf16 widens to fp32 without rounding."""
     if t.dtype == torch.bfloat16:
