@@ -510,7 +510,7 @@ def main():
         k, v, _, _ = caches[i % R]
         sr.dense_decode(q, k, v, launch=lau, ws=ws, out=out)
 
-    kname = "k_decode_mfma" if (kernel == "mfma" or (kernel == "auto" and wl.group_size > 4)
+    kname = "k_decode_mfma" if (kernel == "mfma" or (kernel == "auto" and wl.group_size > 2)
                                 and wl.kv_dtype == "bf16") else "k_decode_valu"
     alg = algorithmic_bytes(wl, n_active)
     if args.read_ceiling:

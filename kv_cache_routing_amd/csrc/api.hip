@@ -65,12 +65,13 @@ sr_status make_plan(const sr_shape& s, const sr_launch* launch, Plan& p) {
     if (l.waves_per_wg != 0 && l.waves_per_wg != 4 && l.waves_per_wg != 8) return SR_ERR_INVALID_ARG;
     p.waves = l.waves_per_wg ? l.waves_per_wg : kDefaultWaves;
     if (l.kernel < SR_KERNEL_AUTO || l.kernel > SR_KERNEL_MFMA) return SR_ERR_INVALID_ARG;
-    // Measured on MI355X: at G <= 4 the vector-ALU kernel streams as fast as
-    // the matrix-core one (both HBM-bound); from G = 5 up the ALU work of QK
-    // outgrows the memory time and the MFMA kernel is ahead (1.8x at G = 8).
+    // Measured on MI355X (interleaved A/B): the matrix-core kernel is 2.5-4 %
+    // faster at G = 4 and 1.7x faster at G = 8, where QK outgrows the vector
+    // ALUs.  At G <= 2 the vector-ALU kernel's QK work is at most half of its
+    // G = 4 load, and it also serves fp32 caches.
     const int32_t G = s.num_q_heads / s.num_kv_heads;
     p.kernel = l.kernel != SR_KERNEL_AUTO ? l.kernel
-               : (s.kv_dtype == SR_KV_BF16 && G > 4 ? SR_KERNEL_MFMA : SR_KERNEL_VALU);
+               : (s.kv_dtype == SR_KV_BF16 && G > 2 ? SR_KERNEL_MFMA : SR_KERNEL_VALU);
     if (p.kernel == SR_KERNEL_MFMA && s.kv_dtype != SR_KV_BF16) return SR_ERR_UNSUPPORTED;
     const int64_t n_items = static_cast<int64_t>(s.batch) * s.num_kv_heads;
     p.gp = pad_group(s.num_q_heads / s.num_kv_heads);

@@ -96,21 +96,23 @@ __device__ inline void write_alpha0(const DecodeArgs& a, const WorkUnit& u, int 
 }
 
 // Last-arriver merge of the S split partials of one item (all threads of the
-// workgroup).  Every global load of the merge is independent of the others,
-// so they are issued in unrolled batches: the merge costs a few memory round
-// trips, not one per split.  Order is fixed: maxima, then per split weights
+// workgroup).  Order is fixed: maxima, then per split weights
 // w_s = exp2(m_s - M) into LDS, then the weighted accumulators.  When a
 // partial has fewer float4 slots than the workgroup has threads, GROUPS
 // thread groups take splits s = gi, gi + GROUPS, ... each in ascending order
 // and the group sums are added in ascending gi: results are bitwise
-// reproducible for a given split count.
+// reproducible for a given split count.  Latency: the accumulator loads of
+// the first PF * GROUPS splits do not depend on the maxima, so they are
+// issued before the maxima pass; a merge of up to that many splits costs one
+// memory round trip plus LDS work.
 template <int D, int GP, int NW>
 __device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, float* out_item) {
     constexpr int NT = NW * 64;
     constexpr int NV = GP * D / 4;                 // float4 slots per partial
     constexpr int GROUPS = NV >= NT ? 1 : NT / NV;
     constexpr int SLOTS = NV >= NT ? NV / NT : 1;  // float4 slots per thread
-    constexpr int CH = 1024 / GP;                  // splits per weight chunk
+    constexpr int PF = SLOTS >= 2 ? 16 : 32;       // splits prefetched per thread and slot
+    constexpr int CH = PF * GROUPS;                // splits per chunk
     static_assert(NT % GP == 0 && NV % (NV >= NT ? NT : NV) == 0, "merge layout");
     __shared__ float s_red[NW][GP];
     __shared__ float s_M[GP], s_L[GP];
@@ -124,6 +126,22 @@ __device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, floa
     const float* ml0 = a.part_ml + static_cast<int64_t>(u.slot) * S * 3 * GP;
     const float4* acc0 =
         reinterpret_cast<const float4*>(a.part_acc + static_cast<int64_t>(u.slot) * S * GP * D);
+    const int gi = GROUPS > 1 ? t / NV : 0;
+    const int v0 = GROUPS > 1 ? t % NV : t;
+
+    // accumulators of chunk c: split gi + GROUPS * k, slot v0 + j * NT
+    float4 pre[SLOTS][PF];
+    auto fetch = [&](int c0) {
+#pragma unroll
+        for (int j = 0; j < SLOTS; ++j)
+#pragma unroll
+            for (int k = 0; k < PF; ++k) {
+                const int sp = c0 + gi + GROUPS * k;
+                pre[j][k] = sp < S ? acc0[static_cast<int64_t>(sp) * NV + v0 + j * NT]
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+    };
+    fetch(0);
 
     {  // M[h]: thread t only ever reads head t % GP
         const int h = t % GP;
@@ -142,13 +160,12 @@ __device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, floa
         __syncthreads();
     }
 
-    const int gi = GROUPS > 1 ? t / NV : 0;
-    const int v0 = GROUPS > 1 ? t % NV : t;
     float4 acc[SLOTS];
 #pragma unroll
-    for (int k = 0; k < SLOTS; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < SLOTS; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     float lsum = 0.f;
     for (int c0 = 0; c0 < S; c0 += CH) {
+        if (c0 > 0) fetch(c0);
         const int n = S - c0 < CH ? S - c0 : CH;
         for (int x = t; x < n * GP; x += NT) {
             const int s = x / GP, h = x - (x / GP) * GP;
@@ -159,21 +176,19 @@ __device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, floa
         }
         __syncthreads();
 #pragma unroll
-        for (int k = 0; k < SLOTS; ++k) {
-            const int v = v0 + k * NT;
-            const int h = (4 * v) / D;
-            const float4* src = acc0 + static_cast<int64_t>(c0) * NV + v;
-            float4 r = acc[k];
-#pragma unroll 16
-            for (int s = gi; s < n; s += GROUPS) {
-                const float4 x = src[static_cast<int64_t>(s) * NV];
-                const float w = s_w[s][h];
-                r.x += w * x.x;
-                r.y += w * x.y;
-                r.z += w * x.z;
-                r.w += w * x.w;
+        for (int j = 0; j < SLOTS; ++j) {
+            const int h = (4 * (v0 + j * NT)) / D;
+            float4 r = acc[j];
+#pragma unroll
+            for (int k = 0; k < PF; ++k) {
+                const int s = gi + GROUPS * k;  // splits past S carry zeros and weight 0
+                const float w = s < n ? s_w[s][h] : 0.f;
+                r.x += w * pre[j][k].x;
+                r.y += w * pre[j][k].y;
+                r.z += w * pre[j][k].z;
+                r.w += w * pre[j][k].w;
             }
-            acc[k] = r;
+            acc[j] = r;
         }
         if (t < GP)
             for (int s = 0; s < n; ++s) lsum += s_lw[s][t];
@@ -199,11 +214,11 @@ __device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, floa
         }
     } else {
 #pragma unroll
-        for (int k = 0; k < SLOTS; ++k) {
-            const int v = v0 + k * NT;
+        for (int j = 0; j < SLOTS; ++j) {
+            const int v = v0 + j * NT;
             if (4 * v < G * D) {
                 const float L = s_L[(4 * v) / D];
-                const float4 r = acc[k];
+                const float4 r = acc[j];
                 *reinterpret_cast<float4*>(out_item + 4 * v) =
                     make_float4(r.x / L, r.y / L, r.z / L, r.w / L);
             }

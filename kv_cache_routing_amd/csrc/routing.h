@@ -175,6 +175,18 @@ __device__ inline bool map_work(const DecodeArgs& a, WorkUnit& u) {
         if (w0 && threadIdx.x == 0 && a.n_active_out) a.n_active_out[0] = n_act;
         item = s_pick[0];
         sink_item = s_pick[1];
+    } else if (a.routed && n_items <= NT) {
+        // one round trip: the whole list and n_active load together
+        __shared__ int32_t s_list[NT];
+        __shared__ int32_t s_nact;
+        if (static_cast<int32_t>(threadIdx.x) < n_items) s_list[threadIdx.x] = a.work_list[threadIdx.x];
+        if (threadIdx.x == 0) s_nact = *a.n_active;
+        __syncthreads();
+        n_act = s_nact;
+        S = splits_for(a.fixed_splits, a.grid, a.split_cap, n_act);
+        slot = wg / S;
+        if (n_act + wg < n_items) sink_item = s_list[n_act + wg];
+        if (n_act > 0 && slot < n_act) item = s_list[slot];
     } else {
         n_act = a.routed ? *a.n_active : n_items;
         S = splits_for(a.fixed_splits, a.grid, a.split_cap, n_act);
