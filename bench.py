@@ -28,6 +28,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -42,13 +43,22 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and whitespace, so that editing a comment
+    does not invalidate counters taken on the same code."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return re.sub(r"\s+", "", text)
+
+
 def decode_sources_digest() -> str:
+    """Digest of the kernel sources' code (comments and whitespace ignored)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "kv_cache_routing_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + fh.read())
+            with open(os.path.join(csrc, f)) as fh:
+                h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -228,8 +228,8 @@ __device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, floa
 
 // Merge the per-wave states held in LDS (s_m/s_l [NW][GP], s_acc [NW][GP][D])
 // into this workgroup's split partial.  With one split per item the partial
-// is final and goes straight to `out`; otherwise it is stored, published with
-// an agent-scope release, and the last workgroup of the item to take a ticket
+// is final and goes straight to `out`; otherwise it is stored with
+// device-coherent stores, a ticket is taken, and the last workgroup of the item
 // merges all S partials in ascending split order and writes `out`.
 template <int D, int GP, int NW>
 __device__ inline void finish_split(const DecodeArgs& a, const WorkUnit& u,
