@@ -155,7 +155,7 @@ def time_launches(fn, steps, stream):
 def read_ceiling(tensors, stream, grids=(256, 512, 1024), unrolls=(4, 8)):
     """Best read bandwidth of the library's streaming probe over the given
     device tensors (16-byte loads per lane, the decode kernels' access width),
-    grid-strided and per-workgroup-blocked."""
+    grid-strided and per-workgroup-blocked, default and non-temporal loads."""
     import ctypes
 
     import torch
@@ -164,20 +164,23 @@ def read_ceiling(tensors, stream, grids=(256, 512, 1024), unrolls=(4, 8)):
     sink = torch.zeros(max(grids), dtype=torch.int32, device=tensors[0].device)
     total = sum(t.numel() * t.element_size() for t in tensors)
     best, rows = 0.0, []
-    for blocked in (0, 1):
-        for grid in grids:
-            for un in unrolls:
-                def f(i):
-                    for t in tensors:
-                        N.check(N.lib.sr_stream_read(
-                            ctypes.c_void_p(t.data_ptr()), t.numel() * t.element_size(), grid, un,
-                            blocked, ctypes.c_void_p(sink.data_ptr()),
-                            ctypes.c_void_p(stream.cuda_stream)), "sr_stream_read")
-                f(0)
-                ms = time_loop(f, 5, stream)
-                gbs = total / (ms * 1e-3) / 1e9
-                rows.append({"blocked": blocked, "grid": grid, "unroll": un, "gbs": round(gbs, 1)})
-                best = max(best, gbs)
+    for nontemporal in (0, 1):
+        for blocked in (0, 1):
+            flags = blocked * N.SR_READ_BLOCKED + nontemporal * N.SR_READ_NONTEMPORAL
+            for grid in grids:
+                for un in unrolls:
+                    def f(i):
+                        for t in tensors:
+                            N.check(N.lib.sr_stream_read(
+                                ctypes.c_void_p(t.data_ptr()), t.numel() * t.element_size(), grid,
+                                un, flags, ctypes.c_void_p(sink.data_ptr()),
+                                ctypes.c_void_p(stream.cuda_stream)), "sr_stream_read")
+                    f(0)
+                    ms = time_loop(f, 5, stream)
+                    gbs = total / (ms * 1e-3) / 1e9
+                    rows.append({"nontemporal": nontemporal, "blocked": blocked, "grid": grid,
+                                 "unroll": un, "gbs": round(gbs, 1)})
+                    best = max(best, gbs)
     return best, rows
 
 

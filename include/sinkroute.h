@@ -213,13 +213,17 @@ const char* sr_status_string(sr_status status);
  * down to 16) of device memory with 16-byte loads per lane (the decode
  * kernels' access width) on `grid` workgroups of 256 threads, `unroll` loads
  * in flight per thread (1, 2, 4, 8 or 16), so a benchmark can measure the
- * achievable HBM read bandwidth.  blocked = 0: the grid walks the buffer
- * together; blocked = 1: each workgroup streams its own contiguous slice.
- * `sink` (>= grid u32, device) is written only in the practically impossible
- * case that a workgroup's XOR of the data is 0x9e3779b9; it exists so no load
- * can be optimised away. */
+ * achievable HBM read bandwidth.  `flags` bit 0 (SR_READ_BLOCKED): each
+ * workgroup streams its own contiguous slice instead of the grid walking the
+ * buffer together; bit 1 (SR_READ_NONTEMPORAL): loads use the non-temporal
+ * cache policy, as the decode kernels' cache loads do.  Other bits are an
+ * error.  `sink` (>= grid u32, device) is written only in the practically
+ * impossible case that a workgroup's XOR of the data is 0x9e3779b9; it exists
+ * so no load can be optimised away. */
+#define SR_READ_BLOCKED 1
+#define SR_READ_NONTEMPORAL 2
 sr_status sr_stream_read(const void* buf, size_t bytes, int32_t grid, int32_t unroll,
-                         int32_t blocked, uint32_t* sink, void* stream);
+                         int32_t flags, uint32_t* sink, void* stream);
 
 /* Library version, e.g. 100 for 0.1.0. */
 int32_t sr_version(void);

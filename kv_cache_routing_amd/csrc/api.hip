@@ -298,12 +298,12 @@ const char* sr_status_string(sr_status status) {
 }
 
 sr_status sr_stream_read(const void* buf, size_t bytes, int32_t grid, int32_t unroll,
-                         int32_t blocked, uint32_t* sink, void* stream) {
+                         int32_t flags, uint32_t* sink, void* stream) {
     if (!buf || !sink || !aligned16(buf) || bytes < 16 || grid < 1) return SR_ERR_INVALID_ARG;
     if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8 && unroll != 16)
         return SR_ERR_INVALID_ARG;
-    if (blocked != 0 && blocked != 1) return SR_ERR_INVALID_ARG;
-    hipError_t e = launch_stream_read(buf, bytes, grid, unroll, blocked, sink,
+    if (flags & ~(SR_READ_BLOCKED | SR_READ_NONTEMPORAL)) return SR_ERR_INVALID_ARG;
+    hipError_t e = launch_stream_read(buf, bytes, grid, unroll, flags, sink,
                                       static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SR_OK : SR_ERR_HIP;
 }

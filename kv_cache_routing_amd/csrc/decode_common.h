@@ -18,6 +18,16 @@ constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// One 16-byte load of cache data with the non-temporal cache policy.  Every
+// cache byte is read once per launch, so nothing is gained by keeping it in
+// L2 or the Infinity Cache; on MI355X this policy streams measurably faster
+// than the default one (about 7.3 vs 6.4 TB/s with the read probe).
+__device__ inline uint4 load_stream(const void* p) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 t = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 // exp2(m - M) as a merge weight; a state that saw no position (m = -inf)
 // weighs nothing, even when M is -inf as well.
 __device__ inline float merge_weight(float m, float M) {

@@ -35,10 +35,6 @@ __device__ inline uint32_t bf16_rne_bits(float x) {
 
 __device__ inline float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
 
-__device__ inline bf16x8 load_bf16x8(const uint16_t* p) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
-}
-
 __device__ inline float readlane_f(float x, int lane) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
@@ -117,12 +113,12 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
         tk = tk < u.t1 ? tk : last;
         const uint16_t* kp = kbase + tk * st + 8 * grp;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) r.k[kb] = *reinterpret_cast<const uint4*>(kp + 32 * kb);
+        for (int kb = 0; kb < KB; ++kb) r.k[kb] = load_stream(kp + 32 * kb);
 #pragma unroll
         for (int uu = 0; uu < UPS; ++uu) {
             int64_t tv = tile + prow + TPI * uu;
             tv = tv < u.t1 ? tv : last;
-            r.v[uu] = *reinterpret_cast<const uint4*>(vbase + tv * st + pchunk * 8);
+            r.v[uu] = load_stream(vbase + tv * st + pchunk * 8);
         }
     };
     auto compute = [&](const Raw& r, int64_t tile) {

@@ -107,8 +107,8 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
             const uint4* vp = reinterpret_cast<const uint4*>(vb + t * st);
 #pragma unroll
             for (int w = 0; w < W; ++w) {
-                r.k[v][w] = kp[w];
-                r.v[v][w] = vp[w];
+                r.k[v][w] = load_stream(kp + w);
+                r.v[v][w] = load_stream(vp + w);
             }
         }
     };

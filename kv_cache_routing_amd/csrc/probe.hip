@@ -8,11 +8,13 @@ namespace {
 
 // blocked = 0: the grid walks the buffer together (workgroup w reads chunks
 // w, w + grid, ...); blocked = 1: workgroup w streams its own contiguous
-// slice of bytes / grid, the access shape of one decode split.
-template <int U>
+// slice of bytes / grid, the access shape of one decode split.  NTL selects
+// the non-temporal cache policy for the loads.
+template <int U, bool NTL>
 __global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ p, int64_t n16,
                                                      int32_t blocked,
                                                      uint32_t* __restrict__ sink) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     uint32_t x = 0;
     int64_t begin = static_cast<int64_t>(blockIdx.x) * 256 * U;
     int64_t step = static_cast<int64_t>(gridDim.x) * 256 * U;
@@ -28,7 +30,14 @@ __global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ p
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t i = base + u * 256 + threadIdx.x;
-            v[u] = i < end ? p[i] : make_uint4(0, 0, 0, 0);
+            if (i >= end) {
+                v[u] = make_uint4(0, 0, 0, 0);
+            } else if (NTL) {
+                const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + i);
+                v[u] = make_uint4(t.x, t.y, t.z, t.w);
+            } else {
+                v[u] = p[i];
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
@@ -38,21 +47,30 @@ __global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ p
     if (x == 0x9e3779b9u) sink[blockIdx.x] = x;
 }
 
-}  // namespace
-
-hipError_t launch_stream_read(const void* buf, size_t bytes, int32_t grid, int32_t unroll,
-                              int32_t blocked, uint32_t* sink, hipStream_t st) {
-    const int64_t n16 = static_cast<int64_t>(bytes / 16);
-    const auto* p = static_cast<const uint4*>(buf);
+template <bool NTL>
+hipError_t launch_policy(const uint4* p, int64_t n16, int32_t grid, int32_t unroll,
+                         int32_t blocked, uint32_t* sink, hipStream_t st) {
     switch (unroll) {
-        case 1: hipLaunchKernelGGL(k_stream_read<1>, dim3(grid), dim3(256), 0, st, p, n16, blocked, sink); break;
-        case 2: hipLaunchKernelGGL(k_stream_read<2>, dim3(grid), dim3(256), 0, st, p, n16, blocked, sink); break;
-        case 4: hipLaunchKernelGGL(k_stream_read<4>, dim3(grid), dim3(256), 0, st, p, n16, blocked, sink); break;
-        case 8: hipLaunchKernelGGL(k_stream_read<8>, dim3(grid), dim3(256), 0, st, p, n16, blocked, sink); break;
-        case 16: hipLaunchKernelGGL(k_stream_read<16>, dim3(grid), dim3(256), 0, st, p, n16, blocked, sink); break;
+        case 1: hipLaunchKernelGGL((k_stream_read<1, NTL>), dim3(grid), dim3(256), 0, st, p, n16, blocked, sink); break;
+        case 2: hipLaunchKernelGGL((k_stream_read<2, NTL>), dim3(grid), dim3(256), 0, st, p, n16, blocked, sink); break;
+        case 4: hipLaunchKernelGGL((k_stream_read<4, NTL>), dim3(grid), dim3(256), 0, st, p, n16, blocked, sink); break;
+        case 8: hipLaunchKernelGGL((k_stream_read<8, NTL>), dim3(grid), dim3(256), 0, st, p, n16, blocked, sink); break;
+        case 16: hipLaunchKernelGGL((k_stream_read<16, NTL>), dim3(grid), dim3(256), 0, st, p, n16, blocked, sink); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, int32_t grid, int32_t unroll,
+                              int32_t flags, uint32_t* sink, hipStream_t st) {
+    const int64_t n16 = static_cast<int64_t>(bytes / 16);
+    const auto* p = static_cast<const uint4*>(buf);
+    const int32_t blocked = flags & SR_READ_BLOCKED;
+    return (flags & SR_READ_NONTEMPORAL)
+               ? launch_policy<true>(p, n16, grid, unroll, blocked, sink, st)
+               : launch_policy<false>(p, n16, grid, unroll, blocked, sink, st);
 }
 
 }  // namespace sr

@@ -83,6 +83,6 @@ hipError_t launch_decode_valu(const sr_shape& s, const DecodeArgs& a, int gp, in
 hipError_t launch_decode_mfma(const sr_shape& s, const DecodeArgs& a, int gp, int waves,
                               hipStream_t st);
 hipError_t launch_stream_read(const void* buf, size_t bytes, int32_t grid, int32_t unroll,
-                              int32_t blocked, uint32_t* sink, hipStream_t st);
+                              int32_t flags, uint32_t* sink, hipStream_t st);
 
 }  // namespace sr

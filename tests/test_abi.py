@@ -142,6 +142,25 @@ def test_route_and_record_validation():
     assert N.lib.sr_workspace_init(p(0), 16, None) == N.SR_ERR_INVALID_ARG
 
 
+def test_stream_read_validation():
+    def rd(flags=0, unroll=4, grid=256, buf=FAKE, nbytes=1 << 20):
+        return N.lib.sr_stream_read(p(buf), nbytes, grid, unroll, flags, p(), None)
+    assert rd(flags=4) == N.SR_ERR_INVALID_ARG
+    assert rd(flags=-1) == N.SR_ERR_INVALID_ARG
+    assert rd(unroll=3) == N.SR_ERR_INVALID_ARG
+    assert rd(grid=0) == N.SR_ERR_INVALID_ARG
+    assert rd(buf=FAKE + 8) == N.SR_ERR_INVALID_ARG
+    assert rd(nbytes=8) == N.SR_ERR_INVALID_ARG
+
+
+def test_header_constants_match_binding():
+    with open(os.path.join(ROOT, "include", "sinkroute.h")) as f:
+        text = f.read()
+    defines = dict(re.findall(r"#define\s+(SR_[A-Z_0-9]+)\s+(\d+)", text))
+    assert int(defines["SR_READ_BLOCKED"]) == N.SR_READ_BLOCKED
+    assert int(defines["SR_READ_NONTEMPORAL"]) == N.SR_READ_NONTEMPORAL
+
+
 def test_fused_route_decode_validation():
     s = shape()
 
