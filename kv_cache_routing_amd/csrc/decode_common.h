@@ -106,15 +106,19 @@ __device__ inline void write_alpha0(const DecodeArgs& a, const WorkUnit& u, int 
 }
 
 // Last-arriver merge of the S split partials of one item (all threads of the
-// workgroup).  Order is fixed: maxima, then per split weights
+// workgroup).  Order is fixed: the maxima M_h, then per split the weights
 // w_s = exp2(m_s - M) into LDS, then the weighted accumulators.  When a
 // partial has fewer float4 slots than the workgroup has threads, GROUPS
 // thread groups take splits s = gi, gi + GROUPS, ... each in ascending order
-// and the group sums are added in ascending gi: results are bitwise
-// reproducible for a given split count.  Latency: the accumulator loads of
-// the first PF * GROUPS splits do not depend on the maxima, so they are
-// issued before the maxima pass; a merge of up to that many splits costs one
-// memory round trip plus LDS work.
+// and the group sums are added in ascending gi; the sums L_h = sum_s w_s l_s
+// and the maxima use one fixed shuffle + LDS tree.  Results are bitwise
+// reproducible for a given split count.
+//
+// Latency: every global load is issued before anything waits.  Each thread
+// first loads (m, l) of one (split, head) pair, then the accumulators of the
+// first CH splits; loads return in order, so the maxima wait only for the
+// (m, l) loads while the accumulators stream in.  A merge of up to SP splits
+// costs one memory round trip plus LDS work.
 template <int D, int GP, int NW>
 __device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, float* out_item) {
     constexpr int NT = NW * 64;
@@ -123,11 +127,12 @@ __device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, floa
     constexpr int SLOTS = NV >= NT ? NV / NT : 1;  // float4 slots per thread
     constexpr int PF = SLOTS >= 2 ? 16 : 32;       // splits prefetched per thread and slot
     constexpr int CH = PF * GROUPS;                // splits per chunk
+    constexpr int SP = NT / GP;                    // splits one pass over (m, l) covers
     static_assert(NT % GP == 0 && NV % (NV >= NT ? NT : NV) == 0, "merge layout");
+    static_assert(CH % SP == 0, "a chunk is whole (m, l) passes");
     __shared__ float s_red[NW][GP];
     __shared__ float s_M[GP], s_L[GP];
     __shared__ float s_w[CH][GP];
-    __shared__ float s_lw[CH][GP];
     __shared__ float4 s_grp[GROUPS][GROUPS > 1 ? NV : 1];
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -138,8 +143,17 @@ __device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, floa
         reinterpret_cast<const float4*>(a.part_acc + static_cast<int64_t>(u.slot) * S * GP * D);
     const int gi = GROUPS > 1 ? t / NV : 0;
     const int v0 = GROUPS > 1 ? t % NV : t;
+    const int hm = t % GP, sm = t / GP;  // this thread's (head, split) in every (m, l) pass
 
-    // accumulators of chunk c: split gi + GROUPS * k, slot v0 + j * NT
+    // (m, l) of split sm, z0 of split 0 (position 0's logit), then the
+    // accumulators of the first chunk.  No load sits under a branch: indexes
+    // past the last split are clamped to it and the values masked (weight 0),
+    // so the loads form one straight run and each wait counts exactly the
+    // loads it needs.
+    const int sm_c = sm < S ? sm : S - 1;
+    float m_first = ml0[static_cast<int64_t>(sm_c) * 3 * GP + hm];
+    float l_first = ml0[static_cast<int64_t>(sm_c) * 3 * GP + GP + hm];
+    const float z0 = ml0[2 * GP + (t < G ? t : 0)];
     float4 pre[SLOTS][PF];
     auto fetch = [&](int c0) {
 #pragma unroll
@@ -147,42 +161,58 @@ __device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, floa
 #pragma unroll
             for (int k = 0; k < PF; ++k) {
                 const int sp = c0 + gi + GROUPS * k;
-                pre[j][k] = sp < S ? acc0[static_cast<int64_t>(sp) * NV + v0 + j * NT]
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+                pre[j][k] = acc0[static_cast<int64_t>(sp < S ? sp : S - 1) * NV + v0 + j * NT];
             }
     };
     fetch(0);
+    if (sm >= S) {
+        m_first = kNegInf;
+        l_first = 0.f;
+    }
 
-    {  // M[h]: thread t only ever reads head t % GP
-        const int h = t % GP;
-        float mx = kNegInf;
-#pragma unroll 8
-        for (int s = t / GP; s < S; s += NT / GP)
-            mx = fmaxf(mx, ml0[static_cast<int64_t>(s) * 3 * GP + h]);
-        for (int o = GP; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-        if (lane < GP) s_red[wave][lane] = mx;
+    // Sum (or max) over the threads that hold head hm: lanes l, l ^ GP, ...
+    // within the wave, then the waves in ascending order.
+    auto head_reduce = [&](float x, bool is_max, float* dst) {
+        for (int o = GP; o < 64; o <<= 1) {
+            const float y = __shfl_xor(x, o);
+            x = is_max ? fmaxf(x, y) : x + y;
+        }
+        if (lane < GP) s_red[wave][lane] = x;
         __syncthreads();
         if (t < GP) {
-            float M = kNegInf;
-            for (int w = 0; w < NW; ++w) M = fmaxf(M, s_red[w][t]);
-            s_M[t] = M;
+            float r = s_red[0][t];
+            for (int w = 1; w < NW; ++w) r = is_max ? fmaxf(r, s_red[w][t]) : r + s_red[w][t];
+            dst[t] = r;
         }
         __syncthreads();
-    }
+    };
+
+    float mx = m_first;
+    for (int s = sm + SP; s < S; s += SP) mx = fmaxf(mx, ml0[static_cast<int64_t>(s) * 3 * GP + hm]);
+    head_reduce(mx, true, s_M);
+    const float M = s_M[hm];
 
     float4 acc[SLOTS];
 #pragma unroll
     for (int j = 0; j < SLOTS; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    float lsum = 0.f;
+    float lw = 0.f;
     for (int c0 = 0; c0 < S; c0 += CH) {
         if (c0 > 0) fetch(c0);
         const int n = S - c0 < CH ? S - c0 : CH;
-        for (int x = t; x < n * GP; x += NT) {
-            const int s = x / GP, h = x - (x / GP) * GP;
-            const float* p = ml0 + static_cast<int64_t>(c0 + s) * 3 * GP;
-            const float w = merge_weight(p[h], s_M[h]);
-            s_w[s][h] = w;
-            s_lw[s][h] = w * p[GP + h];
+#pragma unroll
+        for (int p = 0; p < CH / SP; ++p) {
+            const int s = p * SP + sm;  // split index within the chunk
+            if (s < n) {
+                float m = m_first, l = l_first;
+                if (c0 + p > 0) {
+                    const float* q = ml0 + static_cast<int64_t>(c0 + s) * 3 * GP;
+                    m = q[hm];
+                    l = q[GP + hm];
+                }
+                const float w = merge_weight(m, M);
+                s_w[s][hm] = w;
+                lw += w * l;
+            }
         }
         __syncthreads();
 #pragma unroll
@@ -200,15 +230,13 @@ __device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, floa
             }
             acc[j] = r;
         }
-        if (t < GP)
-            for (int s = 0; s < n; ++s) lsum += s_lw[s][t];
         __syncthreads();
     }
-    if (t < GP) s_L[t] = lsum;
-    if (t < G && a.alpha0_out) write_alpha0(a, u, t, ml0[2 * GP + t], s_M[t], lsum);
-    if constexpr (GROUPS > 1) s_grp[gi][v0] = acc[0];
-    __syncthreads();
+    head_reduce(lw, false, s_L);
+    if (t < G && a.alpha0_out) write_alpha0(a, u, t, z0, s_M[t], s_L[t]);
     if constexpr (GROUPS > 1) {
+        s_grp[gi][v0] = acc[0];
+        __syncthreads();
         if (gi == 0 && 4 * v0 < G * D) {
             float4 r = s_grp[0][v0];
             for (int g = 1; g < GROUPS; ++g) {
