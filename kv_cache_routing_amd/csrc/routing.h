@@ -18,42 +18,53 @@ namespace sr {
 // first + r * stride (r < U) in group lane hl.  Lane hl accumulates elements
 // 4*hl + 64*k with explicit fmaf in a fixed order, then a fixed DPP tree
 // reduces the group, so a head's score does not depend on which kernel or
-// which lane group computed it.  All 64 lanes of the wave must be active.
+// which lane group computed it.  Every load is issued before the first
+// product and none sits under a branch (a head past the end re-reads the
+// last head, whose score the caller ignores; for d = 64 the second half
+// re-reads the first and is not summed), so one wait covers them all.
+// d is 64 or 128.  All 64 lanes of the wave must be active.
 template <int U>
 __device__ inline void head_cosines16(const float* __restrict__ q, const float* __restrict__ k0,
-                                      int64_t first, int64_t stride, int64_t n_heads, int32_t G,
+                                      int32_t first, int32_t stride, int32_t n_heads, int32_t G,
                                       int32_t d, int hl, float (&c)[U]) {
-    float qk[U], qq[U], kk[U];
+    float4 xq[U][2], xk[U][2];
 #pragma unroll
     for (int r = 0; r < U; ++r) {
-        qk[r] = qq[r] = kk[r] = 0.f;
-        const int64_t hh = first + static_cast<int64_t>(r) * stride;
-        if (hh < n_heads) {
-            const float* qp = q + hh * d;
-            const float* kp = k0 + (hh / G) * d;
-            for (int e = 4 * hl; e < d; e += 64) {
-                const float4 x = *reinterpret_cast<const float4*>(qp + e);
-                const float4 y = *reinterpret_cast<const float4*>(kp + e);
-                qk[r] = fmaf(x.x, y.x, qk[r]);
-                qk[r] = fmaf(x.y, y.y, qk[r]);
-                qk[r] = fmaf(x.z, y.z, qk[r]);
-                qk[r] = fmaf(x.w, y.w, qk[r]);
-                qq[r] = fmaf(x.x, x.x, qq[r]);
-                qq[r] = fmaf(x.y, x.y, qq[r]);
-                qq[r] = fmaf(x.z, x.z, qq[r]);
-                qq[r] = fmaf(x.w, x.w, qq[r]);
-                kk[r] = fmaf(y.x, y.x, kk[r]);
-                kk[r] = fmaf(y.y, y.y, kk[r]);
-                kk[r] = fmaf(y.z, y.z, kk[r]);
-                kk[r] = fmaf(y.w, y.w, kk[r]);
-            }
+        int32_t hh = first + r * stride;
+        hh = hh < n_heads ? hh : n_heads - 1;
+        const float* qp = q + static_cast<int64_t>(hh) * d;
+        const float* kp = k0 + static_cast<int64_t>(hh / G) * d;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int e = 4 * hl + (64 * k < d ? 64 * k : 0);
+            xq[r][k] = *reinterpret_cast<const float4*>(qp + e);
+            xk[r][k] = *reinterpret_cast<const float4*>(kp + e);
         }
     }
 #pragma unroll
     for (int r = 0; r < U; ++r) {
-        const float dot = group_allreduce_sum<16>(qk[r]);
-        const float nq = group_allreduce_sum<16>(qq[r]);
-        const float nk = group_allreduce_sum<16>(kk[r]);
+        float qk = 0.f, qq = 0.f, kk = 0.f;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            if (64 * k < d) {
+                const float4 x = xq[r][k], y = xk[r][k];
+                qk = fmaf(x.x, y.x, qk);
+                qk = fmaf(x.y, y.y, qk);
+                qk = fmaf(x.z, y.z, qk);
+                qk = fmaf(x.w, y.w, qk);
+                qq = fmaf(x.x, x.x, qq);
+                qq = fmaf(x.y, x.y, qq);
+                qq = fmaf(x.z, x.z, qq);
+                qq = fmaf(x.w, x.w, qq);
+                kk = fmaf(y.x, y.x, kk);
+                kk = fmaf(y.y, y.y, kk);
+                kk = fmaf(y.z, y.z, kk);
+                kk = fmaf(y.w, y.w, kk);
+            }
+        }
+        const float dot = group_allreduce_sum<16>(qk);
+        const float nq = group_allreduce_sum<16>(qq);
+        const float nk = group_allreduce_sum<16>(kk);
         const float den = sqrtf(nq) * sqrtf(nk);
         c[r] = den > 0.f ? dot / den : 0.f;
     }
@@ -69,15 +80,15 @@ __device__ inline void route_items(const float* __restrict__ q, const float* __r
                                    uint8_t* s_sink, float* scores, uint8_t* mask) {
     constexpr int GROUPS = NT / 16;
     const int tid = threadIdx.x, hl = tid & 15, hg = tid >> 4;
-    const int64_t n_heads = static_cast<int64_t>(n_items) * G;
+    const int32_t n_heads = n_items * G;
     for (int32_t j = tid; j < n_items; j += NT) s_sink[j] = 1;
     __syncthreads();
-    for (int64_t base = 0; base < n_heads; base += static_cast<int64_t>(GROUPS) * U) {
+    for (int32_t base = 0; base < n_heads; base += GROUPS * U) {
         float c[U];
         head_cosines16<U>(q, k0, base + hg, GROUPS, n_heads, G, d, hl, c);
 #pragma unroll
         for (int r = 0; r < U; ++r) {
-            const int64_t hh = base + hg + static_cast<int64_t>(r) * GROUPS;
+            const int32_t hh = base + hg + r * GROUPS;
             if (hh < n_heads && hl == 0) {
                 if (scores) scores[hh] = c[r];
                 if (!(c[r] >= tau)) s_sink[hh / G] = 0;  // one dissenting head keeps it active
