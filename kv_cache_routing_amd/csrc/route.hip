@@ -44,6 +44,13 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(
     const int32_t G = Hq / Hkv;
     const int32_t n_items = B * Hkv;
     route_items<kRouteThreads, 4>(q, k0, tau, n_items, G, d, s_sink, scores, mask);
+    if (n_items <= kRouteThreads) {
+        int32_t pos;
+        const int32_t n_act = partition_one_pass<kRouteThreads>(s_sink, n_items, s_wa, s_ws, pos);
+        if (static_cast<int32_t>(threadIdx.x) < n_items) work_list[pos] = threadIdx.x;
+        if (threadIdx.x == 0) n_active[0] = n_act;
+        return;
+    }
     const int32_t n_act = count_active<kRouteThreads>(s_sink, n_items, s_wa);
     partition_items<kRouteThreads>(s_sink, n_items, n_act, s_wa, s_ws,
                                    [&](int32_t pos, int32_t j) { work_list[pos] = j; });

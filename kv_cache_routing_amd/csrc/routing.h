@@ -22,11 +22,13 @@ namespace sr {
 // product and none sits under a branch (a head past the end re-reads the
 // last head, whose score the caller ignores; for d = 64 the second half
 // re-reads the first and is not summed), so one wait covers them all.
+// Slots r >= n_live (no lane group has a head there; uniform across the
+// workgroup) skip the arithmetic and leave c[r] undefined.
 // d is 64 or 128.  All 64 lanes of the wave must be active.
 template <int U>
 __device__ inline void head_cosines16(const float* __restrict__ q, const float* __restrict__ k0,
                                       int32_t first, int32_t stride, int32_t n_heads, int32_t G,
-                                      int32_t d, int hl, float (&c)[U]) {
+                                      int32_t d, int hl, int32_t n_live, float (&c)[U]) {
     float4 xq[U][2], xk[U][2];
 #pragma unroll
     for (int r = 0; r < U; ++r) {
@@ -43,6 +45,8 @@ __device__ inline void head_cosines16(const float* __restrict__ q, const float* 
     }
 #pragma unroll
     for (int r = 0; r < U; ++r) {
+        c[r] = 0.f;
+        if (r >= n_live) continue;
         float qk = 0.f, qq = 0.f, kk = 0.f;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
@@ -85,7 +89,8 @@ __device__ inline void route_items(const float* __restrict__ q, const float* __r
     __syncthreads();
     for (int32_t base = 0; base < n_heads; base += GROUPS * U) {
         float c[U];
-        head_cosines16<U>(q, k0, base + hg, GROUPS, n_heads, G, d, hl, c);
+        const int32_t n_live = (n_heads - base + GROUPS - 1) / GROUPS;  // same for every thread
+        head_cosines16<U>(q, k0, base + hg, GROUPS, n_heads, G, d, hl, n_live, c);
 #pragma unroll
         for (int r = 0; r < U; ++r) {
             const int32_t hh = base + hg + r * GROUPS;
@@ -113,6 +118,38 @@ __device__ inline int32_t count_active(const uint8_t* s_sink, int32_t n_items, i
     for (int w = 0; w < NT / 64; ++w) n += s_tmp[w];
     __syncthreads();
     return n;
+}
+
+// Count and stable partition in one pass when every item has its own thread
+// (n_items <= NT): returns n_active; position_of(j) is then this thread's
+// item's list position (active items ascending at [0, n_active), sinks
+// ascending after them), valid when threadIdx.x < n_items.  Ends with a
+// workgroup barrier.
+template <int NT>
+__device__ inline int32_t partition_one_pass(const uint8_t* s_sink, int32_t n_items, int32_t* s_wa,
+                                             int32_t* s_ws, int32_t& pos) {
+    constexpr int NWV = NT / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int32_t j = threadIdx.x;
+    const bool in = j < n_items;
+    const bool is_a = in && !s_sink[j];
+    const uint64_t ba = __ballot(is_a), bs = __ballot(in && !is_a);
+    if (lane == 0) {
+        s_wa[wave] = __popcll(ba);
+        s_ws[wave] = __popcll(bs);
+    }
+    __syncthreads();
+    int32_t n_act = 0, pa = 0, ps = 0;
+    for (int w = 0; w < NWV; ++w) {
+        n_act += s_wa[w];
+        if (w < wave) {
+            pa += s_wa[w];
+            ps += s_ws[w];
+        }
+    }
+    pos = is_a ? pa + __popcll(ba & lt) : n_act + ps + __popcll(bs & lt);
+    return n_act;
 }
 
 // Stable partition of the items: active ones in ascending order at list
@@ -168,21 +205,34 @@ __device__ inline bool map_work(const DecodeArgs& a, WorkUnit& u) {
         __shared__ int32_t s_wa[NT / 64], s_ws[NT / 64];
         __shared__ int32_t s_pick[2];
         const bool w0 = wg == 0;
+        if (threadIdx.x == 0) s_pick[0] = s_pick[1] = -1;
         route_items<NT, 8>(a.q, a.k0, a.tau, n_items, G, D, s_flag, w0 ? a.scores_out : nullptr,
                            w0 ? a.mask_out : nullptr);
-        n_act = count_active<NT>(s_flag, n_items, s_wa);
-        S = splits_for(a.fixed_splits, a.grid, a.split_cap, n_act);
-        slot = wg / S;
-        const int32_t want_a = (n_act > 0 && slot < n_act) ? slot : -1;
-        const int32_t want_s = n_act + wg < n_items ? n_act + wg : -1;
-        if (threadIdx.x == 0) s_pick[0] = s_pick[1] = -1;
-        __syncthreads();
         int32_t* list = w0 ? a.list_out : nullptr;
-        partition_items<NT>(s_flag, n_items, n_act, s_wa, s_ws, [&](int32_t pos, int32_t j) {
-            if (pos == want_a) s_pick[0] = j;
-            if (pos == want_s) s_pick[1] = j;
-            if (list) list[pos] = j;
-        });
+        if (n_items <= NT) {
+            int32_t pos;
+            n_act = partition_one_pass<NT>(s_flag, n_items, s_wa, s_ws, pos);
+            S = splits_for(a.fixed_splits, a.grid, a.split_cap, n_act);
+            slot = wg / S;
+            const int32_t j = threadIdx.x;
+            if (j < n_items) {
+                if (n_act > 0 && slot < n_act && pos == slot) s_pick[0] = j;
+                if (pos == n_act + wg) s_pick[1] = j;
+                if (list) list[pos] = j;
+            }
+            __syncthreads();
+        } else {
+            n_act = count_active<NT>(s_flag, n_items, s_wa);
+            S = splits_for(a.fixed_splits, a.grid, a.split_cap, n_act);
+            slot = wg / S;
+            const int32_t want_a = (n_act > 0 && slot < n_act) ? slot : -1;
+            const int32_t want_s = n_act + wg < n_items ? n_act + wg : -1;
+            partition_items<NT>(s_flag, n_items, n_act, s_wa, s_ws, [&](int32_t pos, int32_t j) {
+                if (pos == want_a) s_pick[0] = j;
+                if (pos == want_s) s_pick[1] = j;
+                if (list) list[pos] = j;
+            });
+        }
         if (w0 && threadIdx.x == 0 && a.n_active_out) a.n_active_out[0] = n_act;
         item = s_pick[0];
         sink_item = s_pick[1];

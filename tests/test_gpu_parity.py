@@ -16,7 +16,8 @@ import oracle
 from parity import (assert_outputs, assert_route, log, oracle_inputs, sink_rows_exact,
                     ticket_region, upload)
 from workloads import (CONFIGS, L70B_128K_B8, L8B_128K, L8B_256K_B4, L8B_512K, SINK_FRACTIONS,
-                       TINY, Workload, as_numpy, make_caches, make_layer, make_queries, sweep)
+                       TINY, Workload, as_numpy, make_caches, make_layer, make_layer_bulk,
+                       make_queries, sweep)
 
 pytestmark = pytest.mark.gpu
 
@@ -343,6 +344,60 @@ def test_fused_full_size_70b_layer_sampled():
     ref = oracle.attend_group(q_np[b, g * G:(g + 1) * G], as_numpy(layer.k[b, g]),
                               as_numpy(layer.v[b, g]), 1.0 / math.sqrt(wl.head_dim))
     assert_outputs(out.cpu().numpy()[b, g * G:(g + 1) * G], ref, f"fused 70b item {j}")
+
+
+# --- many items: every branch of the routing partition ----------------------------
+# The routing partition takes one ballot pass when every item has a thread of
+# its own (up to 256 items in the fused prologue, 1024 in the routing kernel)
+# and a counted multi-pass otherwise; these layers sit on both sides of each
+# limit and at the envelope maxima (4096 items fused, 32768 two-call).
+MANY_ITEMS = [
+    Workload("items-256", 32, 8, 8, 128, 24, "bf16", seed=141, sink_plan=("bernoulli", 0.5)),
+    Workload("items-264-g2", 33, 16, 8, 128, 40, "bf16", seed=142, sink_plan=("bernoulli", 0.5)),
+    Workload("items-1024", 128, 8, 8, 64, 16, "bf16", seed=143, sink_plan=("bernoulli", 0.5)),
+    Workload("items-1032", 129, 8, 8, 64, 16, "bf16", seed=144, sink_plan=("bernoulli", 0.5)),
+    Workload("items-4096", 512, 8, 8, 64, 8, "bf16", seed=145, sink_plan=("bernoulli", 0.5)),
+]
+
+
+def _many_items_check(wl, got, r):
+    layer_np = _many_items_check.cache[wl.name]
+    q_np, k_np, v_np = layer_np
+    mask = assert_route(r, q_np, k_np[:, :, 0], wl.tau)[0]
+    ref = oracle.routed_decode(q_np, k_np, v_np, v_np[:, :, 0], mask)
+    sink_rows_exact(got, v_np[:, :, 0].astype(np.float32), mask, wl.group_size)
+    assert_outputs(got, ref, wl.name)
+
+
+_many_items_check.cache = {}
+
+
+@pytest.mark.parametrize("wl", MANY_ITEMS, ids=lambda w: w.name)
+def test_many_items_two_call_and_fused(wl):
+    layer = make_layer(wl)
+    _many_items_check.cache[wl.name] = oracle_inputs(layer)
+    q, k, v = upload(layer)
+    log(f"{wl.name}: {wl.batch * wl.num_kv_heads} items")
+    k0, v0, r, out2 = run_routed(q, k, v, wl.tau, launch("auto"))
+    _many_items_check(wl, out2.cpu().numpy(), r)
+    out1, rf = sr.route_decode(q, k, v, k0, v0, wl.tau, launch=launch("auto"))
+    torch.cuda.synchronize()
+    assert torch.equal(rf.mask, r.mask) and torch.equal(rf.work_list, r.work_list)
+    assert torch.equal(rf.n_active, r.n_active) and torch.equal(rf.scores, r.scores)
+    assert torch.equal(out1, out2)
+    _many_items_check.cache.pop(wl.name)
+
+
+def test_route_at_item_envelope_maximum():
+    wl = Workload("items-32768", 4096, 8, 8, 128, 2, "bf16", seed=146,
+                  sink_plan=("bernoulli", 0.5))
+    layer = make_layer_bulk(wl)
+    _many_items_check.cache[wl.name] = oracle_inputs(layer)
+    q, k, v = upload(layer)
+    log(f"{wl.name}: {wl.batch * wl.num_kv_heads} items")
+    _, _, r, out = run_routed(q, k, v, wl.tau, launch("auto"))
+    _many_items_check(wl, out.cpu().numpy(), r)
+    _many_items_check.cache.pop(wl.name)
 
 
 # --- attention weight of position 0 (alpha_0) -----------------------------------

@@ -73,3 +73,25 @@ def test_cache_entries_look_standard_normal():
     assert abs(vv.mean().item()) < 5e-3 and abs(vv.std().item() - 1.0) < 5e-3
     kk = k[:, :, 1:].float()
     assert abs(kk.std().item() - 1.0) < 5e-3
+
+
+def test_bulk_layer_has_the_same_recipe():
+    from workloads import Workload, make_layer_bulk
+    wl = Workload("bulk", 512, 16, 8, 128, 4, "bf16", seed=7, sink_plan=("bernoulli", 0.5))
+    L = make_layer_bulk(wl)
+    assert L.k.shape == (512, 8, 4, 128) and L.k.dtype == torch.bfloat16
+    assert L.q.shape == (512, 16, 128) and L.q.dtype == torch.float32
+    assert torch.equal(L.q, L.q.to(torch.bfloat16).to(torch.float32))
+    k0 = L.k[:, :, 0].float()
+    assert torch.allclose(k0.norm(dim=-1), torch.full((512, 8), 30.0), rtol=2e-3)
+    frac = L.planted.float().mean().item()
+    assert 0.45 < frac < 0.55
+    # planted heads point along their group's k0, the others are isotropic
+    unit = (k0 / k0.norm(dim=-1, keepdim=True)).repeat_interleave(2, dim=1)
+    cos = (L.q * unit).sum(-1) / L.q.norm(dim=-1)
+    planted = L.planted.repeat_interleave(2, dim=1)
+    assert cos[planted].min().item() > 0.7
+    assert cos[~planted].abs().max().item() < 0.45
+    again = make_layer_bulk(wl)
+    assert torch.equal(again.k, L.k) and torch.equal(again.q, L.q)
+    assert not torch.equal(make_layer_bulk(wl.with_(seed=8)).k, L.k)

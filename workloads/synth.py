@@ -201,6 +201,38 @@ def make_layer(wl: Workload, *, threads: int | None = None) -> Layer:
     return Layer(wl, q, k, v, planted)
 
 
+def make_layer_bulk(wl: Workload) -> Layer:
+    """A layer with the same distributions as make_layer, drawn in bulk: one
+    generator per tensor (seeded from wl.seed) instead of one per item and
+    group, so layers with tens of thousands of items take well under a
+    second.  The bits differ from make_layer's for the same workload.
+    Supports the "bernoulli" and "none" sink plans."""
+    B, Hq, Hkv, T, d, G = (wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.seq_len, wl.head_dim,
+                           wl.group_size)
+    gens = [torch.Generator().manual_seed(wl.seed * 4096 + 3000 + i) for i in range(4)]
+    k = torch.randn((B, Hkv, T, d), generator=gens[0], dtype=torch.float32)
+    v = torch.randn((B, Hkv, T, d), generator=gens[1], dtype=torch.float32)
+    k0 = k[:, :, 0]
+    k0.mul_(wl.k0_norm / k0.norm(dim=-1, keepdim=True))
+    k = k.to(wl.torch_dtype)
+    v = v.to(wl.torch_dtype)
+    k0 = k[:, :, 0].to(torch.float32)
+    plan = wl.sink_plan
+    if plan[0] == "bernoulli":
+        sinks = torch.rand((B, Hkv), generator=gens[2]) < float(plan[1])
+    elif plan[0] == "none":
+        sinks = torch.zeros((B, Hkv), dtype=torch.bool)
+    else:
+        raise ValueError(f"make_layer_bulk: unsupported sink plan {plan!r}")
+    noise = torch.randn((B, Hq, d), generator=gens[3], dtype=torch.float32)
+    unit = (k0 / k0.norm(dim=-1, keepdim=True)).repeat_interleave(G, dim=1)
+    aligned = SINK_ALIGN * unit + SINK_NOISE * noise
+    q = torch.where(sinks.repeat_interleave(G, dim=1)[..., None], aligned, noise)
+    if wl.kv_dtype == "bf16":
+        q = q.to(torch.bfloat16).to(torch.float32)
+    return Layer(wl, q.contiguous(), k.contiguous(), v.contiguous(), sinks)
+
+
 def rope_inv_freq(head_dim: int, base: float = 500000.0) -> torch.Tensor:
     """Rotary frequencies base^(-2i/d), fp32 [d/2] (Llama-3.1 uses base 5e5)."""
     i = torch.arange(0, head_dim, 2, dtype=torch.float64)
