@@ -86,16 +86,27 @@ typedef struct {
     int32_t reserved;      /* must be 0 */
 } sr_shape;
 
-/* Launch policy for the decode kernels.  A NULL pointer means all zeros. */
+/* Launch policy for the decode kernels.  A NULL pointer means all zeros.
+ *
+ * Work division: an item's cache is cut into chunks of one tile per wave
+ * (sr_plan_parts reports the size, 16 to 512 positions), and its chunks are
+ * dealt to S lanes round-robin (lane l: chunks l, l + S, l + 2S, ...).  In
+ * lanes mode every workgroup takes one lane of one item, so an item's
+ * workgroups stream one interleaved window of its cache.  In balanced mode
+ * (adaptive policy, when n_active * S leaves workgroups over and the items
+ * are long enough) the lanes of all active items are laid end to end and
+ * cut into one equal share per workgroup, so a share may span two lanes or
+ * two items.  Each workgroup's work on an item is a "part"; the parts of an
+ * item are merged in workgroup order. */
 typedef struct {
-    /* > 0: every item is split into exactly this many parts: its positions
-     *      are dealt round-robin in chunks of 64 (or 128) positions, part s
-     *      taking chunks s, s + S, s + 2S, ... (a part with no chunk below T
-     *      is empty).
+    /* > 0: S = num_splits lanes per item in lanes mode (a lane with no chunk
+     *      below T is an empty part).
      *   0: adaptive: the grid is a fixed number of workgroups sized from the
-     *      device's CU count, and the kernel splits each active item into
-     *      (grid / n_active) ranges, read from the device-side n_active, so
-     *      the GPU stays full at any sink fraction without a host sync. */
+     *      device's CU count; the kernel reads the device-side n_active and
+     *      takes S = min(grid / n_active, ceil(T / 512)) lanes per item, in
+     *      balanced mode when grid / n_active is not a whole number below that
+     *      cap, so the GPU stays full at any sink fraction without a host
+     *      sync. */
     int32_t num_splits;
     int32_t kernel;        /* sr_kernel */
     int32_t wgs_per_cu;    /* adaptive grid size in workgroups per CU (0 = 1) */
@@ -140,8 +151,8 @@ sr_status sr_rope_append(const sr_shape* shape, const float* q_new, const float*
                          void* k_cache, void* v_cache, void* stream);
 
 /* Bytes of scratch the decode calls need for this shape and launch policy:
- * per-workgroup split partials (m, l, the position-0 logit and acc, fp32)
- * plus one ticket per item.
+ * partial results of up to grid + B*Hkv parts (m, l, the position-0 logit
+ * and acc, fp32) plus one ticket per item.
  * Depends on the current device's CU count in adaptive mode. Returns 0 on an
  * invalid or unsupported shape. */
 size_t sr_workspace_bytes(const sr_shape* shape, const sr_launch* launch);
@@ -200,9 +211,30 @@ sr_status sr_dense_decode_alpha0(const sr_shape* shape, const sr_launch* launch,
                                  const void* k_cache, const void* v_cache, float sm_scale, void* ws,
                                  size_t ws_bytes, float* out, float* alpha0, void* stream);
 
-/* Number of splits per active item the decode kernel will use for a given
- * n_active under this policy (what the adaptive mode derives on the device). */
+/* Lanes per active item (S) the decode kernel will use for a given n_active
+ * under this policy (what the adaptive mode derives on the device). */
 int32_t sr_splits_for(const sr_shape* shape, const sr_launch* launch, int32_t n_active);
+
+/* One workgroup's part of one item, as the decode kernel divides the work. */
+typedef struct {
+    int32_t item;   /* list position of the item (0 .. n_active - 1) */
+    int32_t part;   /* index of this part among the item's parts (workgroup order) */
+    int32_t parts;  /* number of parts of the item (1: no merge) */
+    int32_t lanes;  /* S, lanes per item */
+    int64_t first;  /* the part's range of the item's lane-major chunk sequence */
+    int64_t end;    /*   [first, end): position q is chunk l + k * S of lane l */
+    int64_t chunk;  /* cache positions per chunk */
+} sr_part;
+
+/* Host-side introspection of the work division (no device work): fills
+ * parts[0 .. r) with workgroup `wg`'s parts for `n_active` active items and
+ * returns r (0 when the workgroup has no cache work; at most 2), or -1 for an
+ * invalid shape, policy, n_active (0 .. B*Hkv), wg (0 .. grid - 1) or
+ * max_parts < 2.  Lane-major order: lane l of an item holds Q + (l < rem)
+ * chunks, Q = C / S and rem = C mod S for C = ceil(T / chunk) chunks, and the
+ * lanes follow each other. */
+int32_t sr_plan_parts(const sr_shape* shape, const sr_launch* launch, int32_t n_active, int32_t wg,
+                      sr_part* parts, int32_t max_parts);
 
 /* Workgroups the decode kernel launches under this policy. */
 int32_t sr_grid_size(const sr_shape* shape, const sr_launch* launch);

@@ -21,7 +21,7 @@ EXPORTS = (
     "sr_record_sink", "sr_route", "sr_workspace_bytes", "sr_workspace_init",
     "sr_decode_attn", "sr_dense_decode", "sr_splits_for", "sr_grid_size",
     "sr_status_string", "sr_version", "sr_stream_read", "sr_route_decode",
-    "sr_dense_decode_alpha0", "sr_rope_append",
+    "sr_dense_decode_alpha0", "sr_rope_append", "sr_plan_parts",
 )
 
 
@@ -39,6 +39,14 @@ class SrLaunch(ctypes.Structure):
     _fields_ = [
         ("num_splits", ctypes.c_int32), ("kernel", ctypes.c_int32),
         ("wgs_per_cu", ctypes.c_int32), ("waves_per_wg", ctypes.c_int32),
+    ]
+
+
+class SrPart(ctypes.Structure):
+    _fields_ = [
+        ("item", ctypes.c_int32), ("part", ctypes.c_int32), ("parts", ctypes.c_int32),
+        ("lanes", ctypes.c_int32), ("first", ctypes.c_int64), ("end", ctypes.c_int64),
+        ("chunk", ctypes.c_int64),
     ]
 
 
@@ -73,6 +81,7 @@ def _load():
         "sr_status_string": (ctypes.c_char_p, [i32]),
         "sr_version": (i32, []),
         "sr_stream_read": (i32, [P, sz, i32, i32, i32, P, P]),
+        "sr_plan_parts": (i32, [S, Lp, i32, i32, ctypes.POINTER(SrPart), i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -105,8 +105,9 @@ WsLayout ws_layout(const sr_shape& s, const Plan& p) {
     WsLayout w;
     w.tickets = 0;
     w.ml = align256(n_items * sizeof(uint32_t));
-    w.acc = w.ml + align256(static_cast<size_t>(p.grid) * 3 * p.gp * sizeof(float));
-    w.total = w.acc + align256(static_cast<size_t>(p.grid) * p.gp * s.head_dim * sizeof(float));
+    const size_t parts = static_cast<size_t>(p.grid) + n_items;  // slots w + i, w < grid, i < n
+    w.acc = w.ml + align256(parts * 3 * p.gp * sizeof(float));
+    w.total = w.acc + align256(parts * p.gp * s.head_dim * sizeof(float));
     return w;
 }
 
@@ -278,6 +279,36 @@ int32_t sr_splits_for(const sr_shape* shape, const sr_launch* launch, int32_t n_
     Plan p;
     if (make_plan(*shape, launch, p) != SR_OK) return 0;
     return splits_for(p.fixed_splits, p.grid, p.split_cap, n_active);
+}
+
+int32_t sr_plan_parts(const sr_shape* shape, const sr_launch* launch, int32_t n_active, int32_t wg,
+                      sr_part* parts, int32_t max_parts) {
+    if (!parts || max_parts < 2 || check_shape(shape) != SR_OK) return -1;
+    Plan p;
+    if (make_plan(*shape, launch, p) != SR_OK) return -1;
+    const int32_t n_items = shape->batch * shape->num_kv_heads;
+    if (n_active < 0 || n_active > n_items || wg < 0 || wg >= p.grid) return -1;
+    const int32_t chunk = chunk_positions(p.kernel, shape->head_dim, p.gp, p.waves);
+    const SplitPlan sp =
+        make_split_plan(p.fixed_splits, p.grid, p.split_cap, n_active, shape->seq_len, chunk);
+    if (wg >= sp.P) return 0;
+    const int64_t p0 = range_begin(sp, wg), p1 = range_begin(sp, wg + 1);
+    int32_t i_begin, i_end;
+    range_items(sp, wg, i_begin, i_end);
+    int32_t r = 0;
+    for (int32_t i = i_begin; i < i_end && r < 2; ++i, ++r) {
+        int32_t w_lo, n_parts;
+        item_parts(sp, i, w_lo, n_parts);
+        const int64_t x0 = static_cast<int64_t>(i) * sp.C;
+        parts[r].item = i;
+        parts[r].part = wg - w_lo;
+        parts[r].parts = n_parts;
+        parts[r].lanes = sp.S;
+        parts[r].first = p0 > x0 ? p0 - x0 : 0;
+        parts[r].end = p1 - x0 < sp.C ? p1 - x0 : sp.C;
+        parts[r].chunk = chunk;
+    }
+    return r;
 }
 
 int32_t sr_grid_size(const sr_shape* shape, const sr_launch* launch) {

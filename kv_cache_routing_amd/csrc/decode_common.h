@@ -65,29 +65,179 @@ __device__ inline float wave_max(float x) {
     return x;
 }
 
-// What one workgroup owns: split `split` of the item at work-list slot `slot`.
-// The item's positions are dealt to its S splits round-robin in chunks of
-// CHUNK positions: split s takes chunks s, s + S, s + 2S, ...  So at any
-// moment all workgroups of an item stream one window of the cache together
-// (DRAM pages stay open) instead of S distant ranges.
-struct WorkUnit {
-    int32_t slot, split, splits, b, g;
-    int64_t first;   // first position of this split's first chunk
-    int64_t stride;  // positions between this split's consecutive chunks (S * CHUNK)
-    int64_t t1;      // positions [0, t1) exist (t1 = T)
+// The chunks of one item that one workgroup takes (lane-major positions
+// [q0, q1) of the item, see SplitPlan), visited lane by lane from the last
+// lane of the range to the first, each lane with rising step k.  A range that
+// ends at the head of one lane and starts in the tail of the previous one
+// thus reads its head piece first: every workgroup of an item then moves
+// through the steps k together, and the item's workgroups stream one window
+// of the cache (DRAM pages stay open) rather than distant ranges.
+// The walk keeps pos, the first cache position of the current chunk; within
+// a lane it advances by step = S * chunk positions and is recomputed only at
+// a lane change.  A finished walk points at `past` (>= T), where every row a
+// prefetch asks for clamps to the last cached row.  Steps are 32-bit
+// (C < 2^31), so the walk stays in scalar registers (the scalar unit has no
+// 64-bit ordered compare).
+struct ChunkWalk {
+    int64_t pos, step, chunk, past;
+    int32_t k, k_end, k_first;
+    int32_t l, l_first, S, Q, rem;
+    bool done;
+
+    __device__ void next() {
+        if (++k < k_end) {
+            pos += step;
+            return;
+        }
+        if (l == l_first) {
+            done = true;
+            pos = past;
+            return;
+        }
+        --l;
+        k = l == l_first ? k_first : 0;
+        k_end = Q + (l < rem ? 1 : 0);
+        pos = (l + static_cast<int64_t>(k) * S) * chunk;
+    }
 };
 
-// Routing decision and work mapping of one workgroup, then its sink duty.
+__device__ inline ChunkWalk make_walk(const SplitPlan& p, int64_t q0, int64_t q1, int32_t chunk,
+                                      int64_t seq_len) {
+    ChunkWalk c{};
+    c.S = p.S;
+    c.Q = p.Q;
+    c.rem = p.rem;
+    c.chunk = chunk;
+    c.step = static_cast<int64_t>(p.S) * chunk;
+    c.past = seq_len;
+    c.pos = seq_len;
+    c.done = q0 >= q1;
+    if (c.done) return c;
+    int32_t la, lb, ka, kb;
+    lane_of(p, static_cast<int32_t>(q0), la, ka);
+    lane_of(p, static_cast<int32_t>(q1 - 1), lb, kb);
+    // Integer division runs on the vector unit; readfirstlane moves the
+    // (workgroup-uniform) results back to scalar registers for the loop.
+    c.l = __builtin_amdgcn_readfirstlane(lb);
+    c.l_first = __builtin_amdgcn_readfirstlane(la);
+    c.k_first = __builtin_amdgcn_readfirstlane(ka);
+    c.k = c.l == c.l_first ? c.k_first : 0;
+    c.k_end = __builtin_amdgcn_readfirstlane(kb + 1);
+    c.pos = (c.l + static_cast<int64_t>(c.k) * c.S) * chunk;
+    return c;
+}
+
+// One workgroup's part of one item: the item at work-list position `slot`,
+// the chunks to stream, and where its partial result goes.
+struct WorkUnit {
+    int32_t slot;   // list position of the item (index of its ticket)
+    int32_t b, g;
+    int32_t parts;  // workgroups sharing the item (1: this one writes the output)
+    int32_t base;   // partial slot of the item's first part
+    int32_t mine;   // partial slot of this part
+    int64_t t1;     // positions [0, t1) exist (t1 = T)
+    ChunkWalk walk;
+};
+
+// What the merge of an item needs (a workgroup may owe two merges).
+struct MergeJob {
+    int32_t slot, b, g, parts, base;
+};
+
+__device__ inline MergeJob merge_job(const WorkUnit& u) {
+    return MergeJob{u.slot, u.b, u.g, u.parts, u.base};
+}
+
+// A workgroup's share of the launch: the split plan, its range of positions
+// and the items (b * Hkv + g) at list positions i_begin .. i_end - 1.
+struct WorkRange {
+    SplitPlan plan;
+    int64_t p0, p1;
+    int32_t w, i_begin, i_end;
+    int32_t lane;  // lanes mode: the one lane this workgroup streams
+    int32_t item[2];
+};
+
+// Routing decision and work division of one workgroup, then its sink duty.
 // Workgroup w copies v0 into the G output rows of the sink at list position
-// n_active + w (if there is one), then takes split (w mod S) of the active
-// item at list position (w / S), S = splits per item.  Without routing the
-// list is the identity; with sr_route the list and n_active come from device
-// memory; in fused mode every workgroup derives the decisions itself (the
-// same arithmetic as sr_route, so every workgroup agrees) and workgroup 0
-// writes the routing outputs.  Returns false when there is no split to do.
-// A split with no chunk below T (S * CHUNK > T) is empty and still merges.
+// n_active + w (if there is one), then takes its range of the split plan.
+// Without routing the list is the identity; with sr_route the list and
+// n_active come from device memory; in fused mode every workgroup derives
+// the decisions itself (the same arithmetic as sr_route, so every workgroup
+// agrees) and workgroup 0 writes the routing outputs.  Returns false when
+// the workgroup has no part.  In lanes mode a lane with no chunk below T
+// (S > C) is an empty part and still merges.
 template <int D, int NT, int CHUNK>
-__device__ inline bool map_work(const DecodeArgs& a, WorkUnit& u);
+__device__ inline bool map_work(const DecodeArgs& a, WorkRange& r);
+
+// Part i (a list position in [r.i_begin, r.i_end)) of the workgroup's range;
+// chunks of CHUNK positions.
+template <int CHUNK>
+__device__ inline WorkUnit part_of(const DecodeArgs& a, const WorkRange& r, int32_t i) {
+    WorkUnit u;
+    const SplitPlan& p = r.plan;
+    const int32_t item = i == r.i_begin ? r.item[0] : r.item[1];
+    u.slot = i;
+    u.b = item / a.num_kv_heads;
+    u.g = item - u.b * a.num_kv_heads;
+    u.mine = r.w + i;
+    u.t1 = a.seq_len;
+    if (!p.balanced) {  // all of lane r.lane: no division needed
+        u.parts = p.S;
+        u.base = i * p.S + i;
+        ChunkWalk& c = u.walk;
+        c = ChunkWalk{};
+        c.S = p.S;
+        c.Q = p.Q;
+        c.rem = p.rem;
+        c.chunk = CHUNK;
+        c.step = static_cast<int64_t>(p.S) * CHUNK;
+        c.past = a.seq_len;
+        c.l = c.l_first = r.lane;
+        c.k = c.k_first = 0;
+        c.k_end = p.Q + (r.lane < p.rem ? 1 : 0);
+        c.done = c.k_end == 0;
+        c.pos = c.done ? c.past : static_cast<int64_t>(r.lane) * CHUNK;
+        return u;
+    }
+    int32_t w_lo;
+    item_parts(p, i, w_lo, u.parts);
+    u.base = w_lo + i;
+    const int64_t x0 = static_cast<int64_t>(i) * p.C;
+    const int64_t q0 = r.p0 > x0 ? r.p0 - x0 : 0;
+    const int64_t q1 = r.p1 - x0 < p.C ? r.p1 - x0 : p.C;
+    u.walk = make_walk(p, q0, q1, CHUNK, a.seq_len);
+    return u;
+}
+
+// Two-stage register pipeline over a walk: the next tile's loads are in
+// flight while the current tile is computed, also across the lanes of the
+// walk.  This wave's tile of a chunk starts at pos + wave * WT.  issue() must
+// clamp rows past T: the prefetch after the last tile asks for rows at or
+// past T, which costs one row.
+template <int WT, typename Raw, typename Issue, typename Compute>
+__device__ inline void stream_walk(ChunkWalk w, int wave, Raw& ra, Raw& rb, Issue issue,
+                                   Compute compute) {
+    const int64_t wofs = static_cast<int64_t>(wave) * WT;
+    int64_t ta = w.pos + wofs;
+    issue(ra, ta);
+    while (!w.done) {
+        ChunkWalk n1 = w;
+        n1.next();
+        const int64_t tb = n1.pos + wofs;
+        issue(rb, tb);
+        compute(ra, ta);
+        if (n1.done) break;
+        ChunkWalk n2 = n1;
+        n2.next();
+        const int64_t tc = n2.pos + wofs;
+        issue(ra, tc);
+        compute(rb, tb);
+        if (n2.done) break;
+        w = n2;
+        ta = tc;
+    }
+}
 
 // A store that is visible to every XCD once acknowledged (device-scope
 // coherent: it is written through the local L2 instead of staying dirty).
@@ -98,10 +248,10 @@ __device__ inline void store_coherent(float* p, float v) {
 // Weight of position 0 in head h of the item: exp2(z0 - M) / L, with z0 the
 // base-2 logit the kernel computed for position 0 and (M, L) the item's final
 // maximum and sum (Eq. (1): alpha_0).
-__device__ inline void write_alpha0(const DecodeArgs& a, const WorkUnit& u, int h, float z0,
+__device__ inline void write_alpha0(const DecodeArgs& a, int32_t b, int32_t g, int h, float z0,
                                     float M, float L) {
     if (h >= a.group) return;
-    a.alpha0_out[static_cast<int64_t>(u.b) * a.num_q_heads + static_cast<int64_t>(u.g) * a.group +
+    a.alpha0_out[static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(g) * a.group +
                  h] = fast_exp2(z0 - M) / L;
 }
 
@@ -120,7 +270,7 @@ __device__ inline void write_alpha0(const DecodeArgs& a, const WorkUnit& u, int 
 // (m, l) loads while the accumulators stream in.  A merge of up to SP splits
 // costs one memory round trip plus LDS work.
 template <int D, int GP, int NW>
-__device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, float* out_item) {
+__device__ inline void merge_splits(const DecodeArgs& a, const MergeJob& u, float* out_item) {
     constexpr int NT = NW * 64;
     constexpr int NV = GP * D / 4;                 // float4 slots per partial
     constexpr int GROUPS = NV >= NT ? 1 : NT / NV;
@@ -137,10 +287,10 @@ __device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, floa
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int32_t G = a.group;
-    const int32_t S = u.splits;
-    const float* ml0 = a.part_ml + static_cast<int64_t>(u.slot) * S * 3 * GP;
+    const int32_t S = u.parts;
+    const float* ml0 = a.part_ml + static_cast<int64_t>(u.base) * 3 * GP;
     const float4* acc0 =
-        reinterpret_cast<const float4*>(a.part_acc + static_cast<int64_t>(u.slot) * S * GP * D);
+        reinterpret_cast<const float4*>(a.part_acc + static_cast<int64_t>(u.base) * GP * D);
     const int gi = GROUPS > 1 ? t / NV : 0;
     const int v0 = GROUPS > 1 ? t % NV : t;
     const int hm = t % GP, sm = t / GP;  // this thread's (head, split) in every (m, l) pass
@@ -233,7 +383,7 @@ __device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, floa
         __syncthreads();
     }
     head_reduce(lw, false, s_L);
-    if (t < G && a.alpha0_out) write_alpha0(a, u, t, z0, s_M[t], s_L[t]);
+    if (t < G && a.alpha0_out) write_alpha0(a, u.b, u.g, t, z0, s_M[t], s_L[t]);
     if constexpr (GROUPS > 1) {
         s_grp[gi][v0] = acc[0];
         __syncthreads();
@@ -265,21 +415,21 @@ __device__ inline void merge_splits(const DecodeArgs& a, const WorkUnit& u, floa
 }
 
 // Merge the per-wave states held in LDS (s_m/s_l [NW][GP], s_acc [NW][GP][D])
-// into this workgroup's split partial.  With one split per item the partial
-// is final and goes straight to `out`; otherwise it is stored with
-// device-coherent stores, a ticket is taken, and the last workgroup of the item
-// merges all S partials in ascending split order and writes `out`.
+// into this workgroup's partial of the item.  When the workgroup is the
+// item's only part the partial is final and goes straight to `out`;
+// otherwise it is stored at slot u.mine with device-coherent stores and a
+// ticket is taken.  Returns true (in every thread) when this workgroup drew
+// the item's last ticket: it must then merge the item (merge_item), after
+// an acquire that this function has already made.
 template <int D, int GP, int NW>
-__device__ inline void finish_split(const DecodeArgs& a, const WorkUnit& u,
-                                    const float (*s_m)[GP], const float (*s_l)[GP],
-                                    const float (*s_acc)[GP][D], const float* s_z0) {
+__device__ inline bool finish_part(const DecodeArgs& a, const WorkUnit& u,
+                                   const float (*s_m)[GP], const float (*s_l)[GP],
+                                   const float (*s_acc)[GP][D], const float* s_z0) {
     constexpr int NT = NW * 64;
     const int32_t G = a.group;
-    float* out_item = a.out + (static_cast<int64_t>(u.b) * a.num_q_heads +
-                               static_cast<int64_t>(u.g) * G) * D;
-    const int64_t wg = blockIdx.x;
-
-    if (u.splits == 1) {
+    if (u.parts == 1) {
+        float* out_item = a.out + (static_cast<int64_t>(u.b) * a.num_q_heads +
+                                   static_cast<int64_t>(u.g) * G) * D;
         for (int x = threadIdx.x; x < G * D; x += NT) {
             const int h = x / D, i = x - (x / D) * D;
             float M = kNegInf;
@@ -291,13 +441,13 @@ __device__ inline void finish_split(const DecodeArgs& a, const WorkUnit& u,
                 L += wt * s_l[w][h];
             }
             out_item[x] = A / L;
-            if (i == 0 && a.alpha0_out) write_alpha0(a, u, h, s_z0[h], M, L);
+            if (i == 0 && a.alpha0_out) write_alpha0(a, u.b, u.g, h, s_z0[h], M, L);
         }
-        return;
+        return false;
     }
 
-    float* pml = a.part_ml + wg * 3 * GP;
-    float* pacc = a.part_acc + wg * GP * D;
+    float* pml = a.part_ml + static_cast<int64_t>(u.mine) * 3 * GP;
+    float* pacc = a.part_acc + static_cast<int64_t>(u.mine) * GP * D;
     for (int x = threadIdx.x; x < GP * D; x += NT) {
         const int h = x / D, i = x - (x / D) * D;
         float M = kNegInf;
@@ -312,7 +462,7 @@ __device__ inline void finish_split(const DecodeArgs& a, const WorkUnit& u,
         if (i == 0) {
             store_coherent(pml + h, M);
             store_coherent(pml + GP + h, L);
-            store_coherent(pml + 2 * GP + h, s_z0[h]);  // meaningful in the split with position 0
+            store_coherent(pml + 2 * GP + h, s_z0[h]);  // meaningful in the part holding position 0
         }
     }
 
@@ -330,13 +480,21 @@ __device__ inline void finish_split(const DecodeArgs& a, const WorkUnit& u,
     if (threadIdx.x == 0) {
         const uint32_t prev = __hip_atomic_fetch_add(a.tickets + u.slot, 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = prev == static_cast<uint32_t>(u.splits - 1);
+        const bool last = prev == static_cast<uint32_t>(u.parts - 1);
         if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         s_last = last;
     }
     __syncthreads();
-    if (!s_last) return;
+    return __builtin_amdgcn_readfirstlane(s_last) != 0;
+}
 
+// The merge of an item whose last ticket this workgroup drew: all its parts
+// in ascending workgroup order, written to `out`; the ticket is left at zero
+// for the next call.
+template <int D, int GP, int NW>
+__device__ inline void merge_item(const DecodeArgs& a, const MergeJob& u) {
+    float* out_item = a.out + (static_cast<int64_t>(u.b) * a.num_q_heads +
+                               static_cast<int64_t>(u.g) * a.group) * D;
     merge_splits<D, GP, NW>(a, u, out_item);
     if (threadIdx.x == 0) a.tickets[u.slot] = 0u;  // ready for the next call
 }

@@ -54,191 +54,212 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) float s_p[NW][16][16];  // [pos][head]
     __shared__ float s_m[NW][GP], s_l[NW][GP];
     __shared__ float s_acc[NW][GP][D];
-    __shared__ float s_z0[GP];  // logits of position 0 (split 0 only)
+    __shared__ float s_z0[GP];  // logits of position 0 (in the part that holds it)
 
-    WorkUnit u;
-    if (!map_work<D, NW * 64, NW * 16>(a, u)) return;
+    WorkRange wr;
+    if (!map_work<D, NW * 64, NW * 16>(a, wr)) return;
     const int32_t G = a.group;
 
-    // A operands: query row = col, elements d = 32*kb + 8*grp + e
-    bf16x8 qhi[KB], qlo[KB];
-    {
-        const float* qr = a.q + (static_cast<int64_t>(u.b) * a.num_q_heads +
-                                 static_cast<int64_t>(u.g) * G + col) * D;
-        const bool real = col < G;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            uint32_t hw[4], lw[4];
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                float x0 = real ? qr[32 * kb + 8 * grp + e] * a.qscale : 0.f;
-                float x1 = real ? qr[32 * kb + 8 * grp + e + 1] * a.qscale : 0.f;
-                const uint32_t h0 = bf16_rne_bits(x0), h1 = bf16_rne_bits(x1);
-                const uint32_t l0 = bf16_rne_bits(x0 - bf16_bits_to_float(h0));
-                const uint32_t l1 = bf16_rne_bits(x1 - bf16_bits_to_float(h1));
-                hw[e / 2] = h0 | (h1 << 16);
-                lw[e / 2] = l0 | (l1 << 16);
-            }
-            qhi[kb] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-            qlo[kb] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-        }
-    }
+    // One pass per item this workgroup has a part in: one, or two when the
+    // work is balanced across an item boundary, the later item first (the
+    // head of its first lane, read while the item's other workgroups are at
+    // the same steps).  The pass is a lambda called at two sites rather than
+    // a loop body, which keeps the register allocation of the common
+    // one-pass case free of loop-carried state.  Merges that fall to this
+    // workgroup run after the passes, when nothing else holds registers.
+    auto pass = [&](int32_t part, MergeJob& job) -> bool {
+        const WorkUnit u = part_of<NW * 16>(a, wr, part);
 
-    const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + u.b * a.stride_b + u.g * a.stride_h;
-    const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + u.b * a.stride_b + u.g * a.stride_h;
-    const int64_t st = a.stride_t;
-
-    float m[4], lsum[4];  // heads 4*grp + i, uniform across the 16-lane row
+        // A operands: query row = col, elements d = 32*kb + 8*grp + e
+        bf16x8 qhi[KB], qlo[KB];
+        {
+            const float* qr = a.q + (static_cast<int64_t>(u.b) * a.num_q_heads +
+                                     static_cast<int64_t>(u.g) * G + col) * D;
+            const bool real = col < G;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        m[i] = kNegInf;
-        lsum[i] = 0.f;
-    }
-    float acc[GP][8];
+            for (int kb = 0; kb < KB; ++kb) {
+                uint32_t hw[4], lw[4];
 #pragma unroll
-    for (int h = 0; h < GP; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-
-    // One 16-position tile: the raw key and value bytes this lane loads.
-    struct Raw {
-        uint4 k[KB];
-        uint4 v[UPS];
-    };
-    const int64_t last = u.t1 - 1;
-    // Positions past T are clamped to the last row: every lane then reads the
-    // same row, so a prefetch past the end costs one row and no branch.
-    auto issue = [&](Raw& r, int64_t tile) {
-        int64_t tk = tile + col;
-        tk = tk < u.t1 ? tk : last;
-        const uint16_t* kp = kbase + tk * st + 8 * grp;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) r.k[kb] = load_stream(kp + 32 * kb);
-#pragma unroll
-        for (int uu = 0; uu < UPS; ++uu) {
-            int64_t tv = tile + prow + TPI * uu;
-            tv = tv < u.t1 ? tv : last;
-            r.v[uu] = load_stream(vbase + tv * st + pchunk * 8);
-        }
-    };
-    auto compute = [&](const Raw& r, int64_t tile) {
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const bf16x8 kv = __builtin_bit_cast(bf16x8, r.k[kb]);
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi[kb], kv, s, 0, 0, 0);
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qlo[kb], kv, s, 0, 0, 0);
-        }
-        if (tile + col >= u.t1) {  // ragged tail: positions past T weigh nothing
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s[i] = kNegInf;
-        }
-        if (tile == 0 && col == 0) {  // position 0 is column 0 of tile 0
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (4 * grp + i < GP) s_z0[4 * grp + i] = s[i];
-        }
-        bool up = false;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) up = up || (s[i] > m[i]);
-        if (__any(up)) {
-            float alpha[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float mx = group_allreduce_max<16>(s[i]);
-                const float mn = fmaxf(m[i], mx);
-                alpha[i] = mn > m[i] ? fast_exp2(m[i] - mn) : 1.f;
-                m[i] = mn;
-                lsum[i] *= alpha[i];
-            }
-#pragma unroll
-            for (int h = 0; h < GP; ++h) {
-                const float al = readlane_f(alpha[h & 3], 16 * (h >> 2));
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] *= al;
+                for (int e = 0; e < 8; e += 2) {
+                    float x0 = real ? qr[32 * kb + 8 * grp + e] * a.qscale : 0.f;
+                    float x1 = real ? qr[32 * kb + 8 * grp + e + 1] * a.qscale : 0.f;
+                    const uint32_t h0 = bf16_rne_bits(x0), h1 = bf16_rne_bits(x1);
+                    const uint32_t l0 = bf16_rne_bits(x0 - bf16_bits_to_float(h0));
+                    const uint32_t l1 = bf16_rne_bits(x1 - bf16_bits_to_float(h1));
+                    hw[e / 2] = h0 | (h1 << 16);
+                    lw[e / 2] = l0 | (l1 << 16);
+                }
+                qhi[kb] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+                qlo[kb] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
             }
         }
-        float p[4];
+
+        const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + u.b * a.stride_b + u.g * a.stride_h;
+        const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + u.b * a.stride_b + u.g * a.stride_h;
+        const int64_t st = a.stride_t;
+
+        float m[4], lsum[4];  // heads 4*grp + i, uniform across the 16-lane row
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            p[i] = s[i] == kNegInf ? 0.f : fast_exp2(s[i] - m[i]);
-            lsum[i] += p[i];
+            m[i] = kNegInf;
+            lsum[i] = 0.f;
         }
-        *reinterpret_cast<float4*>(&s_p[wave][col][4 * grp]) = make_float4(p[0], p[1], p[2], p[3]);
-        __builtin_amdgcn_wave_barrier();
+        float acc[GP][8];
 #pragma unroll
-        for (int uu = 0; uu < UPS; ++uu) {
-            const int pos = prow + TPI * uu;
-            float pr[GP];
-            if constexpr (GP >= 4) {
+        for (int h = 0; h < GP; ++h)
 #pragma unroll
-                for (int h4 = 0; h4 < GP; h4 += 4) {
-                    const float4 x = *reinterpret_cast<const float4*>(&s_p[wave][pos][h4]);
-                    pr[h4] = x.x;
-                    pr[h4 + 1] = x.y;
-                    pr[h4 + 2] = x.z;
-                    pr[h4 + 3] = x.w;
-                }
-            } else {
+            for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+
+        // One 16-position tile: the raw key and value bytes this lane loads.
+        struct Raw {
+            uint4 k[KB];
+            uint4 v[UPS];
+        };
+        const int64_t last = u.t1 - 1;
+        // Positions past T are clamped to the last row: every lane then reads the
+        // same row, so a prefetch past the end costs one row and no branch.
+        auto issue = [&](Raw& r, int64_t tile) {
+            int64_t tk = tile + col;
+            tk = tk < u.t1 ? tk : last;
+            const uint16_t* kp = kbase + tk * st + 8 * grp;
 #pragma unroll
-                for (int h = 0; h < GP; ++h) pr[h] = s_p[wave][pos][h];
+            for (int kb = 0; kb < KB; ++kb) r.k[kb] = load_stream(kp + 32 * kb);
+#pragma unroll
+            for (int uu = 0; uu < UPS; ++uu) {
+                int64_t tv = tile + prow + TPI * uu;
+                tv = tv < u.t1 ? tv : last;
+                r.v[uu] = load_stream(vbase + tv * st + pchunk * 8);
             }
-            const uint32_t w4[4] = {r.v[uu].x, r.v[uu].y, r.v[uu].z, r.v[uu].w};
-            float vf[8];
+        };
+        auto compute = [&](const Raw& r, int64_t tile) {
+            f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const bf16x8 kv = __builtin_bit_cast(bf16x8, r.k[kb]);
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi[kb], kv, s, 0, 0, 0);
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qlo[kb], kv, s, 0, 0, 0);
+            }
+            if (tile + col >= u.t1) {  // ragged tail: positions past T weigh nothing
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[i] = kNegInf;
+            }
+            if (tile == 0 && col == 0) {  // position 0 is column 0 of tile 0
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * grp + i < GP) s_z0[4 * grp + i] = s[i];
+            }
+            bool up = false;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) up = up || (s[i] > m[i]);
+            if (__any(up)) {
+                float alpha[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float mx = group_allreduce_max<16>(s[i]);
+                    const float mn = fmaxf(m[i], mx);
+                    alpha[i] = mn > m[i] ? fast_exp2(m[i] - mn) : 1.f;
+                    m[i] = mn;
+                    lsum[i] *= alpha[i];
+                }
+#pragma unroll
+                for (int h = 0; h < GP; ++h) {
+                    const float al = readlane_f(alpha[h & 3], 16 * (h >> 2));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[h][e] *= al;
+                }
+            }
+            float p[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                vf[2 * i] = __uint_as_float(w4[i] << 16);
-                vf[2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u);
+                p[i] = s[i] == kNegInf ? 0.f : fast_exp2(s[i] - m[i]);
+                lsum[i] += p[i];
             }
+            *reinterpret_cast<float4*>(&s_p[wave][col][4 * grp]) = make_float4(p[0], p[1], p[2], p[3]);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int uu = 0; uu < UPS; ++uu) {
+                const int pos = prow + TPI * uu;
+                float pr[GP];
+                if constexpr (GP >= 4) {
+#pragma unroll
+                    for (int h4 = 0; h4 < GP; h4 += 4) {
+                        const float4 x = *reinterpret_cast<const float4*>(&s_p[wave][pos][h4]);
+                        pr[h4] = x.x;
+                        pr[h4 + 1] = x.y;
+                        pr[h4 + 2] = x.z;
+                        pr[h4 + 3] = x.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int h = 0; h < GP; ++h) pr[h] = s_p[wave][pos][h];
+                }
+                const uint32_t w4[4] = {r.v[uu].x, r.v[uu].y, r.v[uu].z, r.v[uu].w};
+                float vf[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    vf[2 * i] = __uint_as_float(w4[i] << 16);
+                    vf[2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u);
+                }
+#pragma unroll
+                for (int h = 0; h < GP; ++h)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[h][e] += pr[h] * vf[e];
+            }
+            __builtin_amdgcn_wave_barrier();
+        };
+
+        // Two-stage register pipeline over this part's chunks: the next tile's
+        // loads are in flight while the current tile is computed.
+        Raw ra, rb;
+        stream_walk<16>(u.walk, wave, ra, rb, issue, compute);
+
+        // wave totals: sums over the 16 positions of a row, values over PV rows
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lsum[i] = group_allreduce_sum<16>(lsum[i]);
+#pragma unroll
+        for (int o = LPT; o < 64; o <<= 1)
 #pragma unroll
             for (int h = 0; h < GP; ++h)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] += pr[h] * vf[e];
+                for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], o);
+        if (prow == 0) {
+#pragma unroll
+            for (int h = 0; h < GP; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s_acc[wave][h][pchunk * 8 + e] = acc[h][e];
         }
-        __builtin_amdgcn_wave_barrier();
-    };
-
-    // Two-stage register pipeline: the next tile's loads are in flight while
-    // the current tile is computed.
-    const int64_t step = u.stride;
-    Raw ra, rb;
-    int64_t tile = u.first + static_cast<int64_t>(wave) * 16;
-    if (tile < u.t1) issue(ra, tile);
-    for (; tile < u.t1; tile += 2 * step) {
-        issue(rb, tile + step);
-        compute(ra, tile);
-        if (tile + step >= u.t1) break;
-        issue(ra, tile + 2 * step);
-        compute(rb, tile + step);
-    }
-
-    // wave totals: sums over the 16 positions of a row, values over PV rows
+        if (col == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lsum[i] = group_allreduce_sum<16>(lsum[i]);
-#pragma unroll
-    for (int o = LPT; o < 64; o <<= 1)
-#pragma unroll
-        for (int h = 0; h < GP; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], o);
-    if (prow == 0) {
-#pragma unroll
-        for (int h = 0; h < GP; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s_acc[wave][h][pchunk * 8 + e] = acc[h][e];
-    }
-    if (col == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int h = 4 * grp + i;
-            if (h < GP) {
-                s_m[wave][h] = m[i];
-                s_l[wave][h] = lsum[i];
+            for (int i = 0; i < 4; ++i) {
+                const int h = 4 * grp + i;
+                if (h < GP) {
+                    s_m[wave][h] = m[i];
+                    s_l[wave][h] = lsum[i];
+                }
             }
         }
+        __syncthreads();
+        job = merge_job(u);
+        return finish_part<D, GP, NW>(a, u, s_m, s_l, s_acc, s_z0);
+    };
+    MergeJob job0{}, job1{};
+    const bool owe1 = pass(wr.i_end - 1, job1);
+    bool owe0 = false;
+    if (wr.i_end - wr.i_begin == 2) {
+        __syncthreads();  // the first pass is done with LDS
+        owe0 = pass(wr.i_begin, job0);
     }
-    __syncthreads();
-    finish_split<D, GP, NW>(a, u, s_m, s_l, s_acc, s_z0);
+    for (int j = 0; j < 2; ++j) {
+        if (!(j == 0 ? owe0 : owe1)) continue;
+        __syncthreads();
+        MergeJob job;
+        job.slot = j == 0 ? job0.slot : job1.slot;
+        job.b = j == 0 ? job0.b : job1.b;
+        job.g = j == 0 ? job0.g : job1.g;
+        job.parts = j == 0 ? job0.parts : job1.parts;
+        job.base = j == 0 ? job0.base : job1.base;
+        merge_item<D, GP, NW>(a, job);
+    }
 }
 
 template <int D, int GP, int NW>

@@ -50,172 +50,193 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
 
     __shared__ float s_m[NW][GP], s_l[NW][GP];
     __shared__ float s_acc[NW][GP][D];
-    __shared__ float s_z0[GP];  // logits of position 0 (split 0 only)
+    __shared__ float s_z0[GP];  // logits of position 0 (in the part that holds it)
 
-    WorkUnit u;
-    if (!map_work<D, NW * 64, NW * TILE>(a, u)) return;
+    WorkRange wr;
+    if (!map_work<D, NW * 64, NW * TILE>(a, wr)) return;
     const int32_t G = a.group;
 
-    float qs[GP][E];
-    {
-        const float* qb = a.q + (static_cast<int64_t>(u.b) * a.num_q_heads +
-                                 static_cast<int64_t>(u.g) * G) * D + chunk * E;
-#pragma unroll
-        for (int h = 0; h < GP; ++h) {
-            if (h < G) {
-                const float4 x0 = *reinterpret_cast<const float4*>(qb + h * D);
-                const float4 x1 = *reinterpret_cast<const float4*>(qb + h * D + 4);
-                qs[h][0] = x0.x * a.qscale; qs[h][1] = x0.y * a.qscale;
-                qs[h][2] = x0.z * a.qscale; qs[h][3] = x0.w * a.qscale;
-                qs[h][4] = x1.x * a.qscale; qs[h][5] = x1.y * a.qscale;
-                qs[h][6] = x1.z * a.qscale; qs[h][7] = x1.w * a.qscale;
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e) qs[h][e] = 0.f;
-            }
-        }
-    }
+    // One pass per item this workgroup has a part in: one, or two when the
+    // work is balanced across an item boundary, the later item first (the
+    // head of its first lane, read while the item's other workgroups are at
+    // the same steps).  The pass is a lambda called at two sites rather than
+    // a loop body, which keeps the register allocation of the common
+    // one-pass case free of loop-carried state.  Merges that fall to this
+    // workgroup run after the passes, when nothing else holds registers.
+    auto pass = [&](int32_t part, MergeJob& job) -> bool {
+        const WorkUnit u = part_of<NW * TILE>(a, wr, part);
 
-    const KV* kb = static_cast<const KV*>(a.k) + u.b * a.stride_b + u.g * a.stride_h + chunk * E;
-    const KV* vb = static_cast<const KV*>(a.v) + u.b * a.stride_b + u.g * a.stride_h + chunk * E;
-    const int64_t st = a.stride_t;
-
-    float m[GP], l[GP], acc[GP][E];
-#pragma unroll
-    for (int h = 0; h < GP; ++h) {
-        m[h] = kNegInf;
-        l[h] = 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
-    }
-
-    // One tile of TILE rows: the raw 8-element slices this lane loads.
-    constexpr int W = sizeof(KV) * E / 16;  // 16-byte loads per 8-element slice
-    struct Raw {
-        uint4 k[U][W];
-        uint4 v[U][W];
-    };
-    const int64_t last = u.t1 - 1;
-    // Rows past T are clamped to the last row: every lane then reads the same
-    // row, so a prefetch past the end costs one row and no branch.
-    auto issue = [&](Raw& r, int64_t tile) {
-#pragma unroll
-        for (int v = 0; v < U; ++v) {
-            int64_t t = tile + v * TPI + row;
-            t = t < u.t1 ? t : last;
-            const uint4* kp = reinterpret_cast<const uint4*>(kb + t * st);
-            const uint4* vp = reinterpret_cast<const uint4*>(vb + t * st);
-#pragma unroll
-            for (int w = 0; w < W; ++w) {
-                r.k[v][w] = load_stream(kp + w);
-                r.v[v][w] = load_stream(vp + w);
-            }
-        }
-    };
-    auto compute = [&](const Raw& r, int64_t tile) {
-        float z[U][GP];
-#pragma unroll
-        for (int v = 0; v < U; ++v) {
-            float kf[E];
-            Row8<KV>::unpack(r.k[v], kf);
-            const bool valid = tile + v * TPI + row < u.t1;
+        float qs[GP][E];
+        {
+            const float* qb = a.q + (static_cast<int64_t>(u.b) * a.num_q_heads +
+                                     static_cast<int64_t>(u.g) * G) * D + chunk * E;
 #pragma unroll
             for (int h = 0; h < GP; ++h) {
-                float s = 0.f;
+                if (h < G) {
+                    const float4 x0 = *reinterpret_cast<const float4*>(qb + h * D);
+                    const float4 x1 = *reinterpret_cast<const float4*>(qb + h * D + 4);
+                    qs[h][0] = x0.x * a.qscale; qs[h][1] = x0.y * a.qscale;
+                    qs[h][2] = x0.z * a.qscale; qs[h][3] = x0.w * a.qscale;
+                    qs[h][4] = x1.x * a.qscale; qs[h][5] = x1.y * a.qscale;
+                    qs[h][6] = x1.z * a.qscale; qs[h][7] = x1.w * a.qscale;
+                } else {
 #pragma unroll
-                for (int e = 0; e < E; ++e) s += qs[h][e] * kf[e];
-                s = group_allreduce_sum<LPT>(s);
-                z[v][h] = valid ? s : kNegInf;
+                    for (int e = 0; e < E; ++e) qs[h][e] = 0.f;
+                }
             }
         }
-        if (tile == 0 && row == 0 && chunk == 0) {  // position 0 is row 0 of tile 0
-#pragma unroll
-            for (int h = 0; h < GP; ++h) s_z0[h] = z[0][h];
-        }
-        bool up = false;
-        float zm[GP];
+
+        const KV* kb = static_cast<const KV*>(a.k) + u.b * a.stride_b + u.g * a.stride_h + chunk * E;
+        const KV* vb = static_cast<const KV*>(a.v) + u.b * a.stride_b + u.g * a.stride_h + chunk * E;
+        const int64_t st = a.stride_t;
+
+        float m[GP], l[GP], acc[GP][E];
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
-            zm[h] = z[0][h];
+            m[h] = kNegInf;
+            l[h] = 0.f;
 #pragma unroll
-            for (int v = 1; v < U; ++v) zm[h] = fmaxf(zm[h], z[v][h]);
-            up = up || (zm[h] > m[h]);
+            for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
         }
-        if (__any(up)) {
+
+        // One tile of TILE rows: the raw 8-element slices this lane loads.
+        constexpr int W = sizeof(KV) * E / 16;  // 16-byte loads per 8-element slice
+        struct Raw {
+            uint4 k[U][W];
+            uint4 v[U][W];
+        };
+        const int64_t last = u.t1 - 1;
+        // Rows past T are clamped to the last row: every lane then reads the same
+        // row, so a prefetch past the end costs one row and no branch.
+        auto issue = [&](Raw& r, int64_t tile) {
+#pragma unroll
+            for (int v = 0; v < U; ++v) {
+                int64_t t = tile + v * TPI + row;
+                t = t < u.t1 ? t : last;
+                const uint4* kp = reinterpret_cast<const uint4*>(kb + t * st);
+                const uint4* vp = reinterpret_cast<const uint4*>(vb + t * st);
+#pragma unroll
+                for (int w = 0; w < W; ++w) {
+                    r.k[v][w] = load_stream(kp + w);
+                    r.v[v][w] = load_stream(vp + w);
+                }
+            }
+        };
+        auto compute = [&](const Raw& r, int64_t tile) {
+            float z[U][GP];
+#pragma unroll
+            for (int v = 0; v < U; ++v) {
+                float kf[E];
+                Row8<KV>::unpack(r.k[v], kf);
+                const bool valid = tile + v * TPI + row < u.t1;
+#pragma unroll
+                for (int h = 0; h < GP; ++h) {
+                    float s = 0.f;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) s += qs[h][e] * kf[e];
+                    s = group_allreduce_sum<LPT>(s);
+                    z[v][h] = valid ? s : kNegInf;
+                }
+            }
+            if (tile == 0 && row == 0 && chunk == 0) {  // position 0 is row 0 of tile 0
+#pragma unroll
+                for (int h = 0; h < GP; ++h) s_z0[h] = z[0][h];
+            }
+            bool up = false;
+            float zm[GP];
 #pragma unroll
             for (int h = 0; h < GP; ++h) {
-                const float mn = fmaxf(m[h], zm[h]);
-                const float al = mn > m[h] ? fast_exp2(m[h] - mn) : 1.f;
-                m[h] = mn;
-                l[h] *= al;
+                zm[h] = z[0][h];
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[h][e] *= al;
+                for (int v = 1; v < U; ++v) zm[h] = fmaxf(zm[h], z[v][h]);
+                up = up || (zm[h] > m[h]);
             }
-        }
+            if (__any(up)) {
 #pragma unroll
-        for (int v = 0; v < U; ++v) {
-            float vf[E];
-            Row8<KV>::unpack(r.v[v], vf);
+                for (int h = 0; h < GP; ++h) {
+                    const float mn = fmaxf(m[h], zm[h]);
+                    const float al = mn > m[h] ? fast_exp2(m[h] - mn) : 1.f;
+                    m[h] = mn;
+                    l[h] *= al;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[h][e] *= al;
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < U; ++v) {
+                float vf[E];
+                Row8<KV>::unpack(r.v[v], vf);
+#pragma unroll
+                for (int h = 0; h < GP; ++h) {
+                    const float p = z[v][h] == kNegInf ? 0.f : fast_exp2(z[v][h] - m[h]);
+                    l[h] += p;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[h][e] += p * vf[e];
+                }
+            }
+        };
+
+        // Two-stage register pipeline over this part's chunks: the next tile's
+        // loads are in flight while the current tile is computed.
+        Raw ra, rb;
+        stream_walk<TILE>(u.walk, wave, ra, rb, issue, compute);
+
+        // merge the lane groups of this wave (lanes with the same chunk)
+#pragma unroll
+        for (int o = LPT; o < 64; o <<= 1) {
 #pragma unroll
             for (int h = 0; h < GP; ++h) {
-                const float p = z[v][h] == kNegInf ? 0.f : fast_exp2(z[v][h] - m[h]);
-                l[h] += p;
+                const float mo = __shfl_xor(m[h], o);
+                const float lo = __shfl_xor(l[h], o);
+                const float M = fmaxf(m[h], mo);
+                const float wa = merge_weight(m[h], M), wb = merge_weight(mo, M);
+                l[h] = l[h] * wa + lo * wb;
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[h][e] += p * vf[e];
+                for (int e = 0; e < E; ++e) {
+                    const float ao = __shfl_xor(acc[h][e], o);
+                    acc[h][e] = acc[h][e] * wa + ao * wb;
+                }
+                m[h] = M;
             }
         }
+        if (row == 0) {
+#pragma unroll
+            for (int h = 0; h < GP; ++h) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) s_acc[wave][h][chunk * E + e] = acc[h][e];
+                if (chunk == 0) {
+                    s_m[wave][h] = m[h];
+                    s_l[wave][h] = l[h];
+                }
+            }
+        }
+        __syncthreads();
+        job = merge_job(u);
+        return finish_part<D, GP, NW>(a, u, s_m, s_l, s_acc, s_z0);
     };
-
-    // Two-stage register pipeline: the next tile's loads are in flight while
-    // the current tile is computed.
-    const int64_t step = u.stride;
-    Raw ra, rb;
-    int64_t tile = u.first + static_cast<int64_t>(wave) * TILE;
-    if (tile < u.t1) issue(ra, tile);
-    for (; tile < u.t1; tile += 2 * step) {
-        issue(rb, tile + step);
-        compute(ra, tile);
-        if (tile + step >= u.t1) break;
-        issue(ra, tile + 2 * step);
-        compute(rb, tile + step);
+    MergeJob job0{}, job1{};
+    const bool owe1 = pass(wr.i_end - 1, job1);
+    bool owe0 = false;
+    if (wr.i_end - wr.i_begin == 2) {
+        __syncthreads();  // the first pass is done with LDS
+        owe0 = pass(wr.i_begin, job0);
     }
-
-    // merge the lane groups of this wave (lanes with the same chunk)
-#pragma unroll
-    for (int o = LPT; o < 64; o <<= 1) {
-#pragma unroll
-        for (int h = 0; h < GP; ++h) {
-            const float mo = __shfl_xor(m[h], o);
-            const float lo = __shfl_xor(l[h], o);
-            const float M = fmaxf(m[h], mo);
-            const float wa = merge_weight(m[h], M), wb = merge_weight(mo, M);
-            l[h] = l[h] * wa + lo * wb;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const float ao = __shfl_xor(acc[h][e], o);
-                acc[h][e] = acc[h][e] * wa + ao * wb;
-            }
-            m[h] = M;
-        }
+    for (int j = 0; j < 2; ++j) {
+        if (!(j == 0 ? owe0 : owe1)) continue;
+        __syncthreads();
+        MergeJob job;
+        job.slot = j == 0 ? job0.slot : job1.slot;
+        job.b = j == 0 ? job0.b : job1.b;
+        job.g = j == 0 ? job0.g : job1.g;
+        job.parts = j == 0 ? job0.parts : job1.parts;
+        job.base = j == 0 ? job0.base : job1.base;
+        merge_item<D, GP, NW>(a, job);
     }
-    if (row == 0) {
-#pragma unroll
-        for (int h = 0; h < GP; ++h) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) s_acc[wave][h][chunk * E + e] = acc[h][e];
-            if (chunk == 0) {
-                s_m[wave][h] = m[h];
-                s_l[wave][h] = l[h];
-            }
-        }
-    }
-    __syncthreads();
-    finish_split<D, GP, NW>(a, u, s_m, s_l, s_acc, s_z0);
 }
 
 template <typename KV, int D, int GP, int NW>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
-    constexpr int U = GP >= 16 ? 1 : (GP >= 8 ? 2 : (GP >= 4 ? 8 : 8));
+    constexpr int U = valu_rows_per_lane(GP);
     hipLaunchKernelGGL((k_decode_valu<KV, D, GP, NW, U>), dim3(a.grid), dim3(NW * 64), 0, st, a);
     return hipGetLastError();
 }

@@ -194,48 +194,100 @@ __device__ inline void partition_items(const uint8_t* s_sink, int32_t n_items, i
 
 namespace sr {
 
+// A value every lane holds alike, moved to a scalar register: values read
+// from LDS or memory are otherwise assumed to differ per lane, and the work
+// division derived from them would live in vector registers behind
+// per-lane branches.
+__device__ inline int32_t uniform(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ inline int64_t uniform64(int64_t x) {
+    const uint64_t u = static_cast<uint64_t>(x);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// The plan's fields in scalar registers (integer division runs on the vector
+// unit).
+__device__ inline SplitPlan uniform_plan(SplitPlan p) {
+    p.A = uniform64(p.A);
+    p.e = uniform(p.e);
+    p.C = uniform(p.C);
+    p.n = uniform(p.n);
+    p.S = uniform(p.S);
+    p.P = uniform(p.P);
+    p.Q = uniform(p.Q);
+    p.rem = uniform(p.rem);
+    p.balanced = uniform(p.balanced);
+    return p;
+}
+
 template <int D, int NT, int CHUNK>
-__device__ inline bool map_work(const DecodeArgs& a, WorkUnit& u) {
+__device__ inline bool map_work(const DecodeArgs& a, WorkRange& r) {
     const int32_t n_items = a.batch * a.num_kv_heads;
     const int32_t wg = blockIdx.x;
     const int32_t G = a.group;
-    int32_t n_act, S, slot, item = -1, sink_item = -1;
+    int32_t n_act, sink_item = -1;
+    r.item[0] = r.item[1] = -1;
+    // The plan, this workgroup's range of positions and the list positions
+    // of the items it touches (one in lanes mode, at most two when balanced).
+    auto plan_range = [&](int32_t n) {
+        r.plan = uniform_plan(
+            make_split_plan(a.fixed_splits, a.grid, a.split_cap, n, a.seq_len, CHUNK));
+        r.w = wg;
+        r.i_begin = r.i_end = 0;
+        r.lane = 0;
+        r.p0 = r.p1 = 0;
+        if (wg >= r.plan.P) return;
+        if (!r.plan.balanced) {  // lane wg mod S of item wg / S
+            r.i_begin = uniform(wg / r.plan.S);
+            r.i_end = r.i_begin + 1;
+            r.lane = wg - r.i_begin * r.plan.S;
+            return;
+        }
+        r.p0 = uniform64(range_begin(r.plan, wg));
+        r.p1 = uniform64(range_begin(r.plan, wg + 1));
+        range_items(r.plan, wg, r.i_begin, r.i_end);
+        r.i_begin = uniform(r.i_begin);
+        r.i_end = uniform(r.i_end);
+    };
     if (a.fused) {
         __shared__ uint8_t s_flag[kMaxFusedItems];
         __shared__ int32_t s_wa[NT / 64], s_ws[NT / 64];
-        __shared__ int32_t s_pick[2];
+        __shared__ int32_t s_pick[3];  // items at positions i_begin, i_begin + 1; the sink
         const bool w0 = wg == 0;
-        if (threadIdx.x == 0) s_pick[0] = s_pick[1] = -1;
+        if (threadIdx.x < 3) s_pick[threadIdx.x] = -1;
         route_items<NT, 8>(a.q, a.k0, a.tau, n_items, G, D, s_flag, w0 ? a.scores_out : nullptr,
                            w0 ? a.mask_out : nullptr);
         int32_t* list = w0 ? a.list_out : nullptr;
         if (n_items <= NT) {
             int32_t pos;
-            n_act = partition_one_pass<NT>(s_flag, n_items, s_wa, s_ws, pos);
-            S = splits_for(a.fixed_splits, a.grid, a.split_cap, n_act);
-            slot = wg / S;
+            n_act = uniform(partition_one_pass<NT>(s_flag, n_items, s_wa, s_ws, pos));
+            plan_range(n_act);
             const int32_t j = threadIdx.x;
             if (j < n_items) {
-                if (n_act > 0 && slot < n_act && pos == slot) s_pick[0] = j;
-                if (pos == n_act + wg) s_pick[1] = j;
+                if (pos == r.i_begin && pos < r.i_end) s_pick[0] = j;
+                if (pos == r.i_begin + 1 && pos < r.i_end) s_pick[1] = j;
+                if (pos == n_act + wg) s_pick[2] = j;
                 if (list) list[pos] = j;
             }
             __syncthreads();
         } else {
-            n_act = count_active<NT>(s_flag, n_items, s_wa);
-            S = splits_for(a.fixed_splits, a.grid, a.split_cap, n_act);
-            slot = wg / S;
-            const int32_t want_a = (n_act > 0 && slot < n_act) ? slot : -1;
+            n_act = uniform(count_active<NT>(s_flag, n_items, s_wa));
+            plan_range(n_act);
+            const int32_t ib = r.i_begin, ie = r.i_end;
             const int32_t want_s = n_act + wg < n_items ? n_act + wg : -1;
             partition_items<NT>(s_flag, n_items, n_act, s_wa, s_ws, [&](int32_t pos, int32_t j) {
-                if (pos == want_a) s_pick[0] = j;
-                if (pos == want_s) s_pick[1] = j;
+                if (pos == ib && pos < ie) s_pick[0] = j;
+                if (pos == ib + 1 && pos < ie) s_pick[1] = j;
+                if (pos == want_s) s_pick[2] = j;
                 if (list) list[pos] = j;
             });
         }
         if (w0 && threadIdx.x == 0 && a.n_active_out) a.n_active_out[0] = n_act;
-        item = s_pick[0];
-        sink_item = s_pick[1];
+        r.item[0] = uniform(s_pick[0]);
+        r.item[1] = uniform(s_pick[1]);
+        sink_item = uniform(s_pick[2]);
     } else if (a.routed && n_items <= NT) {
         // one round trip: the whole list and n_active load together
         __shared__ int32_t s_list[NT];
@@ -243,17 +295,18 @@ __device__ inline bool map_work(const DecodeArgs& a, WorkUnit& u) {
         if (static_cast<int32_t>(threadIdx.x) < n_items) s_list[threadIdx.x] = a.work_list[threadIdx.x];
         if (threadIdx.x == 0) s_nact = *a.n_active;
         __syncthreads();
-        n_act = s_nact;
-        S = splits_for(a.fixed_splits, a.grid, a.split_cap, n_act);
-        slot = wg / S;
-        if (n_act + wg < n_items) sink_item = s_list[n_act + wg];
-        if (n_act > 0 && slot < n_act) item = s_list[slot];
+        n_act = uniform(min(max(s_nact, 0), n_items));
+        plan_range(n_act);
+        if (n_act + wg < n_items) sink_item = uniform(s_list[n_act + wg]);
+        if (r.i_begin < r.i_end) r.item[0] = uniform(s_list[r.i_begin]);
+        if (r.i_begin + 1 < r.i_end) r.item[1] = uniform(s_list[r.i_begin + 1]);
     } else {
-        n_act = a.routed ? *a.n_active : n_items;
-        S = splits_for(a.fixed_splits, a.grid, a.split_cap, n_act);
-        slot = wg / S;
-        if (a.routed && n_act + wg < n_items) sink_item = a.work_list[n_act + wg];
-        if (n_act > 0 && slot < n_act) item = a.routed ? a.work_list[slot] : slot;
+        n_act = a.routed ? uniform(min(max(*a.n_active, 0), n_items)) : n_items;
+        plan_range(n_act);
+        if (a.routed && n_act + wg < n_items) sink_item = uniform(a.work_list[n_act + wg]);
+        if (r.i_begin < r.i_end) r.item[0] = a.routed ? uniform(a.work_list[r.i_begin]) : r.i_begin;
+        if (r.i_begin + 1 < r.i_end)
+            r.item[1] = a.routed ? uniform(a.work_list[r.i_begin + 1]) : r.i_begin + 1;
     }
     if (sink_item >= 0) {
         const int32_t b = sink_item / a.num_kv_heads, g = sink_item - b * a.num_kv_heads;
@@ -262,16 +315,7 @@ __device__ inline bool map_work(const DecodeArgs& a, WorkUnit& u) {
             a.out + (static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(g) * G) * D;
         for (int x = threadIdx.x; x < G * D; x += NT) dst[x] = src[x % D];
     }
-    if (item < 0) return false;
-    u.slot = slot;
-    u.split = wg - slot * S;
-    u.splits = S;
-    u.b = item / a.num_kv_heads;
-    u.g = item - u.b * a.num_kv_heads;
-    u.first = static_cast<int64_t>(u.split) * CHUNK;
-    u.stride = static_cast<int64_t>(S) * CHUNK;
-    u.t1 = a.seq_len;
-    return true;
+    return r.i_begin < r.i_end;
 }
 
 }  // namespace sr

@@ -19,8 +19,8 @@ struct DecodeArgs {
     const int32_t* n_active;   // [1]     (routed only)
     float* out;                // [B][Hq][d] fp32
     uint32_t* tickets;         // [B*Hkv] arrival counters, zero between calls
-    float* part_ml;            // [grid][2][GP]   split maxima and sums
-    float* part_acc;           // [grid][GP][d]   split accumulators
+    float* part_ml;            // [grid + B*Hkv][3][GP]  part maxima, sums, position-0 logits
+    float* part_acc;           // [grid + B*Hkv][GP][d]  part accumulators
     int64_t stride_b, stride_h, stride_t;  // elements
     int64_t seq_len;
     int32_t batch, num_q_heads, num_kv_heads, group;
@@ -60,6 +60,137 @@ __host__ __device__ inline int32_t splits_for(int32_t fixed_splits, int32_t grid
     int32_t s = grid / n_act;
     if (s > split_cap) s = split_cap;
     return s < 1 ? 1 : s;
+}
+
+// Work division of a decode launch (the kernels and the host share it).
+//
+// Each active item's cache is cut into C = ceil(T / chunk) chunks of `chunk`
+// positions (one tile per wave).  The chunks of an item are ordered
+// lane-major: lane l (of S lanes) holds chunks l, l + S, l + 2S, ..., and the
+// lanes follow each other; the n active items' sequences are concatenated in
+// work-list order, N = n * C positions in all.  Workgroup w takes the
+// positions [begin(w), begin(w + 1)):
+//
+// * lanes mode (the S lanes of every item fill the grid, a fixed split count
+//   was asked for, or the split cap is reached): exactly lane w mod S of
+//   item w / S, so the workgroups of an item stream one interleaved window;
+// * balanced mode (the lanes leave workgroups over, e.g. 29 items on 256
+//   workgroups): an equal share floor(w N / P) .. floor((w + 1) N / P), so no
+//   CU idles; a share is at most C positions, so it touches at most two items.
+//
+// Workgroup w's work on item i is one "part"; the parts of an item are the
+// workgroups w_lo(i) .. w_hi(i) and their partial results sit at slots
+// w + i, contiguous per item (w + i is injective over the parts).
+struct SplitPlan {
+    int64_t A;         // balanced: floor(N / P), positions per workgroup
+    int32_t C;         // chunks per item (< 2^31)
+    int32_t e;         // balanced: N mod P
+    int32_t n;         // active items
+    int32_t S;         // lanes per item
+    int32_t P;         // workgroups with cache work
+    int32_t Q, rem;    // lane l holds Q + (l < rem) chunks
+    int32_t balanced;
+};
+
+// Balanced mode keeps products like w * n and w * (N mod P) below 2^30.
+constexpr int32_t kMaxBalancedGrid = 1 << 15;
+
+// Everything below runs in 32-bit arithmetic (N = n * C can exceed 2^32,
+// but no 64-bit division is needed): with C = c1 * P + c2,
+// floor(N / P) = n * c1 + floor(n * c2 / P), and n * c2 < 2^30.
+__host__ __device__ inline SplitPlan make_split_plan(int32_t fixed_splits, int32_t grid,
+                                                     int32_t split_cap, int32_t n_act,
+                                                     int64_t seq_len, int32_t chunk) {
+    SplitPlan p{};
+    p.n = n_act > 0 ? n_act : 0;
+    p.C = static_cast<int32_t>((seq_len + chunk - 1) / chunk);
+    p.S = splits_for(fixed_splits, grid, split_cap, n_act);
+    p.Q = p.C / p.S;
+    p.rem = p.C - p.Q * p.S;
+    p.balanced = fixed_splits == 0 && p.n > 0 && p.S < split_cap &&
+                 static_cast<int64_t>(p.n) * p.S < grid && grid <= kMaxBalancedGrid;
+    p.P = p.balanced ? grid : p.n * p.S;
+    if (p.balanced) {
+        const int32_t c1 = p.C / p.P, c2 = p.C - c1 * p.P;
+        const int32_t nc2 = p.n * c2;
+        p.A = static_cast<int64_t>(p.n) * c1 + nc2 / p.P;
+        p.e = nc2 - (nc2 / p.P) * p.P;
+    }
+    return p;
+}
+
+__host__ __device__ inline int32_t lane_start(const SplitPlan& p, int32_t l) {
+    return l * p.Q + (l < p.rem ? l : p.rem);
+}
+
+// Lane and step of lane-major position q (0 <= q < C) of an item.
+__host__ __device__ inline void lane_of(const SplitPlan& p, int32_t q, int32_t& l, int32_t& k) {
+    const int32_t big = p.rem * (p.Q + 1);
+    if (q < big) {
+        l = q / (p.Q + 1);
+        k = q - l * (p.Q + 1);
+    } else {  // here Q >= 1: with Q == 0 every position lies below `big`
+        const int32_t r = q - big;
+        l = p.rem + r / p.Q;
+        k = r - (l - p.rem) * p.Q;
+    }
+}
+
+// First position of workgroup w's range (w <= P; begin(P) = N).
+__host__ __device__ inline int64_t range_begin(const SplitPlan& p, int32_t w) {
+    if (p.balanced) return static_cast<int64_t>(w) * p.A + (w * p.e) / p.P;  // floor(w N / P)
+    return static_cast<int64_t>(w / p.S) * p.C + lane_start(p, w % p.S);
+}
+
+// List positions of the items workgroup w (< P) has parts in: [i_begin, i_end).
+__host__ __device__ inline void range_items(const SplitPlan& p, int32_t w, int32_t& i_begin,
+                                            int32_t& i_end) {
+    if (!p.balanced) {
+        i_begin = w / p.S;
+        i_end = i_begin + 1;
+        return;
+    }
+    i_begin = (w * p.n) / p.P;  // floor(floor(w N / P) / C) = floor(w n / P)
+    // a range is at most C long (P >= n), so it reaches at most one more item
+    i_end = range_begin(p, w + 1) > static_cast<int64_t>(i_begin + 1) * p.C ? i_begin + 2
+                                                                           : i_begin + 1;
+}
+
+// The workgroup holding position x = i * C, the first of item i (i <= n;
+// item n stands for the end, P): the largest w with begin(w) <= x, which is
+// floor(i P / n) or one more.
+__host__ __device__ inline int32_t item_first_wg(const SplitPlan& p, int32_t i) {
+    if (i >= p.n) return p.P;
+    const int32_t m = (i * p.P) / p.n;
+    return range_begin(p, m + 1) <= static_cast<int64_t>(i) * p.C ? m + 1 : m;
+}
+
+// The parts of item i: first workgroup and count.
+__host__ __device__ inline void item_parts(const SplitPlan& p, int32_t i, int32_t& w_lo,
+                                           int32_t& parts) {
+    if (!p.balanced) {
+        w_lo = i * p.S;
+        parts = p.S;
+        return;
+    }
+    w_lo = item_first_wg(p, i);
+    // the last part is the workgroup holding (i + 1) C - 1: the first
+    // workgroup of item i + 1, unless that one starts exactly at its start
+    const int32_t w_next = item_first_wg(p, i + 1);
+    const bool starts_there =
+        w_next >= p.P || range_begin(p, w_next) == static_cast<int64_t>(i + 1) * p.C;
+    parts = (starts_there ? w_next - 1 : w_next) - w_lo + 1;
+}
+
+// Rows of cache per lane and tile of the vector-ALU kernel (U), and the
+// positions per chunk of either kernel.
+__host__ __device__ constexpr int valu_rows_per_lane(int gp) {
+    return gp >= 16 ? 1 : (gp >= 8 ? 2 : 8);
+}
+
+inline int32_t chunk_positions(int32_t kernel, int32_t head_dim, int32_t gp, int32_t waves) {
+    if (kernel == SR_KERNEL_MFMA) return waves * 16;
+    return waves * (64 / (head_dim / 8)) * valu_rows_per_lane(gp);
 }
 
 inline int32_t pad_group(int32_t g) {

@@ -1,10 +1,13 @@
 """Host-side checks of the C ABI: the library loads, exports every function
 include/sinkroute.h declares, and rejects bad arguments before launching
-anything (each case here fails validation, so no kernel is ever enqueued)."""
+anything (each case here fails validation, so no kernel is ever enqueued).
+The work division the decode kernel uses is checked through sr_plan_parts,
+which runs the same arithmetic on the host."""
 import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from kv_cache_routing_amd import _native as N
@@ -174,3 +177,135 @@ def test_fused_route_decode_validation():
     assert fused(s, ws_bytes=16) == N.SR_ERR_INVALID_ARG
     big = shape(B=1024, Hq=8, Hkv=8)            # 8192 items > 4096
     assert fused(big) == N.SR_ERR_UNSUPPORTED
+
+
+# --- work division (host-side model of what the decode kernel streams) ----------
+def plan(s, launch, n_active):
+    """{wg: [sr_part, ...]} over the whole grid."""
+    grid = N.lib.sr_grid_size(ctypes.byref(s), ctypes.byref(launch))
+    buf = (N.SrPart * 2)()
+    out = {}
+    for wg in range(grid):
+        r = N.lib.sr_plan_parts(ctypes.byref(s), ctypes.byref(launch), n_active, wg, buf, 2)
+        assert 0 <= r <= 2, (wg, r)
+        out[wg] = [N.SrPart.from_buffer_copy(buf[i]) for i in range(r)]
+    return grid, out
+
+
+def lane_major_chunks(first, end, C, S):
+    """Chunks of lane-major positions [first, end): lane l holds chunks
+    l, l + S, ... (Q + (l < rem) of them), lanes in order."""
+    Q, rem = divmod(C, S)
+    chunks, q = [], 0
+    for lane in range(S):
+        for k in range(Q + (lane < rem)):
+            if first <= q < end:
+                chunks.append(lane + k * S)
+            q += 1
+    return chunks
+
+
+@pytest.mark.parametrize("kw,n_active,launch", [
+    (dict(B=8, Hq=64, Hkv=8, T=131072), 29, (0, 2, 0, 0)),   # 70B shape, 29 of 64 active
+    (dict(B=1, Hq=32, Hkv=8, T=524288), 4, (0, 2, 0, 0)),    # divides the grid: lanes
+    (dict(B=4, Hq=32, Hkv=8, T=262144), 24, (0, 1, 0, 0)),   # VALU chunking
+    (dict(B=2, Hq=8, Hkv=8, T=40000), 11, (0, 2, 2, 0)),     # 2 workgroups per CU
+    (dict(B=1, Hq=32, Hkv=8, T=3000), 3, (0, 2, 0, 0)),      # split cap binds: lanes
+    (dict(B=1, Hq=8, Hkv=2, T=200), 2, (7, 1, 0, 0)),        # fixed splits
+    (dict(B=1, Hq=8, Hkv=2, T=70), 2, (9, 2, 0, 0)),         # more lanes than chunks
+    (dict(B=40, Hq=8, Hkv=8, T=65536), 257, (0, 2, 0, 8)),   # >256 items, 8 waves
+])
+def test_plan_covers_every_chunk_once(kw, n_active, launch):
+    s = shape(**kw)
+    lau = N.SrLaunch(*launch)
+    grid, parts = plan(s, lau, n_active)
+    seen = {}
+    per_wg, n_parts = [], {}
+    for wg, ps in parts.items():
+        total = 0
+        for p in ps:
+            S, chunk = p.lanes, p.chunk
+            C = -(-kw["T"] // chunk)
+            assert 0 <= p.item < n_active and 0 <= p.first <= p.end <= C
+            n_parts.setdefault(p.item, set()).add((p.part, p.parts, wg))
+            for c in lane_major_chunks(p.first, p.end, C, S):
+                assert (p.item, c) not in seen, ("chunk twice", p.item, c)
+                seen[(p.item, c)] = wg
+            total += p.end - p.first
+        if ps:
+            per_wg.append(total)
+    C = -(-kw["T"] // parts_chunk(parts))
+    assert len(seen) == n_active * C                     # every chunk of every item
+    for item, ps in n_parts.items():
+        (count,) = {pp for _, pp, _ in ps}
+        assert sorted(p for p, _, _ in ps) == list(range(count))
+        wgs = sorted(w for _, _, w in ps)
+        assert wgs == list(range(wgs[0], wgs[0] + count))  # parts are consecutive workgroups
+    S = N.lib.sr_splits_for(ctypes.byref(s), ctypes.byref(lau), n_active)
+    balanced = launch[0] == 0 and n_active * S < grid and S < -(-kw["T"] // 512)
+    if balanced:
+        assert len(per_wg) == grid and max(per_wg) - min(per_wg) <= 1
+    else:  # one lane of one item per workgroup
+        assert all(len(ps) <= 1 for ps in parts.values())
+        assert sum(1 for ps in parts.values() if ps) == n_active * S
+
+
+def parts_chunk(parts):
+    return next(p.chunk for ps in parts.values() for p in ps)
+
+
+def test_plan_parts_rejects_bad_arguments():
+    s = shape()
+    lau = N.SrLaunch(0, 0, 0, 0)
+    buf = (N.SrPart * 2)()
+    grid = N.lib.sr_grid_size(ctypes.byref(s), ctypes.byref(lau))
+    call = lambda n, wg, m=2: N.lib.sr_plan_parts(ctypes.byref(s), ctypes.byref(lau), n, wg, buf, m)
+    assert call(-1, 0) == -1 and call(9, 0) == -1
+    assert call(4, -1) == -1 and call(4, grid) == -1
+    assert call(4, 0, 1) == -1
+    assert call(0, 0) == 0                                  # nothing active: no cache work
+
+
+def test_plan_random_layouts_tile_every_item():
+    """Random shapes, kernels, grids and active counts: each item's parts,
+    in workgroup order, tile its lane-major chunk sequence [0, C) exactly
+    (lane-major positions are one-to-one with chunks), part numbers run
+    0..parts-1, and balanced shares differ by at most one chunk."""
+    rng = np.random.default_rng(2024)
+    buf = (N.SrPart * 2)()
+    for _ in range(150):
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        B = int(rng.integers(1, 9))
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        d = int(rng.choice([64, 128]))
+        T = int(rng.integers(1, 400000))
+        kern = int(rng.choice([1, 2]))
+        waves = int(rng.choice([4, 8]))
+        fixed = int(rng.choice([0, 0, 0, int(rng.integers(1, 40))]))
+        per_cu = int(rng.choice([0, 1, 2, 3]))
+        s = shape(B=B, Hq=Hkv * G, Hkv=Hkv, d=d, T=T)
+        lau = N.SrLaunch(fixed, kern, per_cu, waves)
+        grid = N.lib.sr_grid_size(ctypes.byref(s), ctypes.byref(lau))
+        n_act = int(rng.integers(0, B * Hkv + 1))
+        items, totals = {}, []
+        for wg in range(grid):
+            r = N.lib.sr_plan_parts(ctypes.byref(s), ctypes.byref(lau), n_act, wg, buf, 2)
+            assert 0 <= r <= 2
+            tot = 0
+            for i in range(r):
+                p = N.SrPart.from_buffer_copy(buf[i])
+                items.setdefault(p.item, []).append((wg, p.part, p.parts, p.first, p.end, p.chunk))
+                tot += p.end - p.first
+            if r:
+                totals.append(tot)
+        assert sorted(items) == list(range(n_act))
+        for item, ps in items.items():
+            ps.sort()
+            C = -(-T // ps[0][5])
+            assert [p[1] for p in ps] == list(range(len(ps))) and {p[2] for p in ps} == {len(ps)}
+            assert ps[0][3] == 0 and ps[-1][4] == C
+            for a, b in zip(ps, ps[1:]):
+                assert a[4] == b[3] and b[0] == a[0] + 1
+        S = N.lib.sr_splits_for(ctypes.byref(s), ctypes.byref(lau), n_act)
+        if fixed == 0 and n_act and n_act * S < grid and S < -(-T // 512):
+            assert len(totals) == grid and max(totals) - min(totals) <= 1

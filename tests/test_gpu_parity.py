@@ -400,6 +400,53 @@ def test_route_at_item_envelope_maximum():
     _many_items_check.cache.pop(wl.name)
 
 
+# --- balanced work division ------------------------------------------------------
+# When the active count does not divide the grid, each workgroup takes an
+# equal share of all active items' chunks (a share may span two lanes or two
+# items); these layers are long enough (T / 512 above grid / n_active) for
+# that mode and small enough for the oracle in full.
+BALANCED = [
+    Workload("bal-3of4-g4", 1, 16, 4, 128, 65536, "bf16", seed=151, sink_plan=("count", 1)),
+    Workload("bal-10of16-g2", 2, 16, 8, 128, 32768, "bf16", seed=152, sink_plan=("count", 3)),
+    Workload("bal-7of8-g1-d64", 1, 8, 8, 64, 40000, "bf16", seed=153, sink_plan=("count", 1)),
+]
+
+
+@pytest.mark.parametrize("wl", BALANCED, ids=lambda w: w.name)
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_balanced_division_full_parity(wl, kernel):
+    layer = make_layer(wl)
+    lau = launch(kernel)
+    q, k, v = upload(layer)
+    grid = sr.grid_size(sr.make_shape(q, k, v), lau)
+    n_act = wl.batch * (wl.num_kv_heads - wl.sink_plan[1])
+    S = sr.splits_for(sr.make_shape(q, k, v), lau, n_act)
+    assert n_act * S < grid and S < -(-wl.seq_len // 512), "layer must divide in balanced mode"
+    got = full_check(layer, lau, check_dense=False)
+    k0, v0 = sr.record_sink(k, v)
+    fused, _ = sr.route_decode(q, k, v, k0, v0, wl.tau, launch=lau)
+    assert torch.equal(fused.cpu(), torch.from_numpy(got))
+    routed_all = sr.decode_attn(q, k, v, v0, *_route_all_active(q, k0), launch=lau)
+    assert torch.equal(routed_all, sr.dense_decode(q, k, v, launch=lau))
+
+
+def _route_all_active(q, k0):
+    r = sr.route(q, k0, 2.0)  # tau > 1: every item active, the identity list
+    return r.work_list, r.n_active
+
+
+def test_balanced_dense_alpha0():
+    wl = Workload("bal-dense-6", 1, 12, 6, 128, 40000, "bf16", seed=154)
+    layer = make_layer(wl)
+    q, k, v = upload(layer)
+    out, a0 = sr.dense_decode_alpha0(q, k, v)
+    q_np, k_np, v_np = oracle_inputs(layer)
+    assert_outputs(out.cpu().numpy(), oracle.dense_decode(q_np, k_np, v_np), "balanced dense")
+    ref = oracle.bos_mass(q_np, k_np)
+    rel = np.abs(a0.cpu().numpy().astype(np.float64) - ref) / ref
+    assert rel.max() <= 1e-4
+
+
 # --- attention weight of position 0 (alpha_0) -----------------------------------
 ALPHA_CASES = [
     Workload("a-8b", 1, 32, 8, 128, 9000, "bf16", seed=81, sink_plan=("count", 4)),
