@@ -30,8 +30,8 @@ BF16_KERNELS = ["valu", "mfma"]
 KERNEL_ID = {"valu": 1, "mfma": 2, "auto": 0}
 
 
-def launch(kernel="auto", splits=0, per_cu=0):
-    return sr.make_launch(splits, KERNEL_ID[kernel], per_cu)
+def launch(kernel="auto", splits=0, per_cu=0, waves=0):
+    return sr.make_launch(splits, KERNEL_ID[kernel], per_cu, waves)
 
 
 def run_routed(q, k, v, tau, lau):
@@ -445,6 +445,28 @@ def test_balanced_dense_alpha0():
     ref = oracle.bos_mass(q_np, k_np)
     rel = np.abs(a0.cpu().numpy().astype(np.float64) - ref) / ref
     assert rel.max() <= 1e-4
+
+
+# --- eight-wave workgroups -------------------------------------------------------
+EIGHT_WAVES = [
+    Workload("w8-8b", 1, 32, 8, 128, 12345, "bf16", seed=161, sink_plan=("count", 4)),
+    Workload("w8-g16-d64", 1, 32, 2, 64, 2000, "bf16", seed=162, sink_plan=("count", 1)),
+    Workload("w8-f32", 1, 16, 4, 128, 3333, "f32", seed=163, sink_plan=("count", 2)),
+    Workload("w8-bal-3of4", 1, 16, 4, 128, 65536, "bf16", seed=164, sink_plan=("count", 1)),
+]
+
+
+@pytest.mark.parametrize("wl", EIGHT_WAVES, ids=lambda w: w.name)
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_eight_wave_workgroups(wl, kernel):
+    if wl.kv_dtype == "f32" and kernel == "mfma":
+        pytest.skip("matrix-core kernel takes bf16 caches")
+    layer = make_layer(wl)
+    got = full_check(layer, launch(kernel, waves=8))
+    q, k, v = upload(layer)
+    k0, v0 = sr.record_sink(k, v)
+    fused, _ = sr.route_decode(q, k, v, k0, v0, wl.tau, launch=launch(kernel, waves=8))
+    assert torch.equal(fused.cpu(), torch.from_numpy(got))
 
 
 # --- attention weight of position 0 (alpha_0) -----------------------------------
