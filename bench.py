@@ -204,9 +204,12 @@ def cpu_baseline(layer, n_active_items, budget_s=12.0):
 
     import oracle
     from workloads import as_numpy
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in info) or blas
     except Exception:  # pragma: no cover
         cores = 1
     wl = layer.wl
@@ -239,7 +242,22 @@ def cpu_baseline(layer, n_active_items, budget_s=12.0):
                    f"layer-step takes {step_s * 1e3:.0f} ms"),
         "us_per_layer_step": round(step_s * 1e6, 1),
         "seconds": round(t_total, 2),
+        "cpu_model": _cpu_model(),
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "numpy": np.__version__,
+        "blas": blas,
     }
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
 
 
 def decode_layers_report(sr, torch, args):
@@ -585,6 +603,20 @@ def main():
     ceiling, _ = read_ceiling([t for c in caches for t in c[:2]], stream, grids=(256, 512),
                               unrolls=(8,))
 
+    props = torch.cuda.get_device_properties(dev)
+    device = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+              "compute_units": props.multi_processor_count,
+              "hbm_gib": round(props.total_memory / 2**30, 1), "hip": torch.version.hip,
+              "torch": torch.__version__}
+    grid = sr.grid_size(shape, lau)
+    parts0 = sr.plan_parts(shape, lau, n_active, 0)
+    chunk = parts0[0]["chunk"] if parts0 else 0
+    balanced = n_active * splits < grid and splits < -(-wl.seq_len // 512)
+    launch_info = {"waves_per_wg": lau.waves_per_wg or 4, "grid": grid,
+                   "lanes_per_active_group": splits,
+                   "positions_per_lane": -(-wl.seq_len // splits),
+                   "chunk_positions": chunk, "mode": "balanced" if balanced else "lanes"}
+
     sweep_rows = []
     if not args.no_sweep:
         k, v, k0, v0 = caches[0]
@@ -607,6 +639,10 @@ def main():
                                "active_fraction": round(na / (wl.batch * wl.num_kv_heads), 4),
                                "gbs": round(algorithmic_bytes(wl, na) / (ms * 1e-3) / 1e9, 1)})
             log(f"sweep f={f}: {ms * 1e3:.1f} us (n_active={na})")
+        t0 = sweep_rows[0]["us"]
+        for row in sweep_rows:
+            row["t_over_t0"] = round(row["us"] / t0, 4)
+            row["dev_from_linear"] = round(row["us"] / t0 - (1 - row["sink_fraction"]), 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -646,6 +682,15 @@ def main():
         "decode_kernel_us": round(ms_decode * 1e3, 2),
         "splits_per_active_group": splits,
         "kernel": kernel,
+        "launch": launch_info,
+        "device": device,
+        # the output fields of the pages' efficiency benchmark
+        "pages_fields": {"context_length": wl.seq_len,
+                         "baseline_latency_us": round(ms_dense * 1e3, 2),
+                         "sinkrouter_latency_us": round(ms_step * 1e3, 2),
+                         "throughput": round(1e3 / ms_step, 1),
+                         "sink_ratio": round(1 - n_active / (wl.batch * wl.num_kv_heads), 4),
+                         "speedup": round(ms_dense / ms_step, 4)},
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": kname,
@@ -654,6 +699,8 @@ def main():
                      "frac_of_measured_ceiling": round(dec_gbs / ceiling, 4)},
         "cpu_baseline": cpu,
         "sink_fraction_sweep": sweep_rows,
+        "sink_fraction_sweep_max_dev_from_linear": (
+            max(abs(r["dev_from_linear"]) for r in sweep_rows) if sweep_rows else None),
         "kernel_compare": compare,
         "context": "pages report 2.03x decode speedup at 512K (hardware not stated)",
     }

@@ -25,7 +25,7 @@ from ._native import (SR_KERNEL_AUTO, SR_KERNEL_MFMA, SR_KERNEL_VALU,  # noqa: F
 __all__ = ["record_sink", "route", "decode_attn", "route_decode", "dense_decode",
            "dense_decode_alpha0", "rope_append", "Workspace",
            "make_shape",
-           "make_launch", "splits_for", "grid_size", "SinkRouteError", "Routing",
+           "make_launch", "splits_for", "grid_size", "plan_parts", "SinkRouteError", "Routing",
            "SR_KERNEL_AUTO", "SR_KERNEL_VALU", "SR_KERNEL_MFMA"]
 
 
@@ -73,6 +73,16 @@ def splits_for(shape: N.SrShape, launch: N.SrLaunch | None, n_active: int) -> in
 
 def grid_size(shape: N.SrShape, launch: N.SrLaunch | None) -> int:
     return N.lib.sr_grid_size(ctypes.byref(shape), _lp(launch))
+
+
+def plan_parts(shape: N.SrShape, launch: N.SrLaunch | None, n_active: int, wg: int) -> list:
+    """Workgroup wg's parts of the work division (host-side, no device work):
+    a list of dicts with item, part, parts, lanes, first, end, chunk."""
+    buf = (N.SrPart * 2)()
+    r = N.lib.sr_plan_parts(ctypes.byref(shape), _lp(launch), int(n_active), int(wg), buf, 2)
+    if r < 0:
+        raise SinkRouteError(N.SR_ERR_INVALID_ARG, "sr_plan_parts")
+    return [{f: getattr(buf[i], f) for f, _ in N.SrPart._fields_} for i in range(r)]
 
 
 def _lp(launch):

@@ -309,3 +309,16 @@ def test_plan_random_layouts_tile_every_item():
         S = N.lib.sr_splits_for(ctypes.byref(s), ctypes.byref(lau), n_act)
         if fixed == 0 and n_act and n_act * S < grid and S < -(-T // 512):
             assert len(totals) == grid and max(totals) - min(totals) <= 1
+
+
+def test_binding_plan_parts_matches_the_abi():
+    import kv_cache_routing_amd as sr
+    s = shape(B=8, Hq=64, Hkv=8, T=131072)
+    lau = N.SrLaunch(0, 2, 0, 0)
+    got = sr.plan_parts(s, lau, 29, 7)
+    buf = (N.SrPart * 2)()
+    r = N.lib.sr_plan_parts(ctypes.byref(s), ctypes.byref(lau), 29, 7, buf, 2)
+    assert len(got) == r >= 1
+    assert got[0]["item"] == buf[0].item and got[0]["end"] == buf[0].end
+    with pytest.raises(sr.SinkRouteError):
+        sr.plan_parts(s, lau, 65, 0)
