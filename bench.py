@@ -541,7 +541,8 @@ def main():
         k, v, _, _ = caches[i % R]
         sr.dense_decode(q, k, v, launch=lau, ws=ws, out=out)
 
-    kname = "k_decode_mfma" if (kernel == "mfma" or (kernel == "auto" and wl.group_size > 2)
+    kname = "k_decode_mfma" if (kernel == "mfma" or (kernel == "auto" and (wl.head_dim == 128 or
+                                                                          wl.group_size > 2))
                                 and wl.kv_dtype == "bf16") else "k_decode_valu"
     alg = algorithmic_bytes(wl, n_active)
     if args.read_ceiling:

@@ -65,13 +65,15 @@ sr_status make_plan(const sr_shape& s, const sr_launch* launch, Plan& p) {
     if (l.waves_per_wg != 0 && l.waves_per_wg != 4 && l.waves_per_wg != 8) return SR_ERR_INVALID_ARG;
     p.waves = l.waves_per_wg ? l.waves_per_wg : kDefaultWaves;
     if (l.kernel < SR_KERNEL_AUTO || l.kernel > SR_KERNEL_MFMA) return SR_ERR_INVALID_ARG;
-    // Measured on MI355X (interleaved A/B): the matrix-core kernel is 2.5-4 %
-    // faster at G = 4 and 1.7x faster at G = 8, where QK outgrows the vector
-    // ALUs.  At G <= 2 the vector-ALU kernel's QK work is at most half of its
-    // G = 4 load, and it also serves fp32 caches.
+    // Measured on MI355X (interleaved A/B, non-temporal loads): the matrix-core
+    // kernel leads for every bf16 group size at d = 128 (by 6-7 % at G = 1-2,
+    // 10-20 % at G = 4, 1.8x at G = 8, 5x at G = 16) and at d = 64 from G = 4
+    // on; at d = 64 with G <= 2 the vector-ALU kernel leads by 6-10 %.  fp32
+    // caches take the vector-ALU kernel.
     const int32_t G = s.num_q_heads / s.num_kv_heads;
+    const bool mfma_wins = s.head_dim == 128 || G > 2;
     p.kernel = l.kernel != SR_KERNEL_AUTO ? l.kernel
-               : (s.kv_dtype == SR_KV_BF16 && G > 2 ? SR_KERNEL_MFMA : SR_KERNEL_VALU);
+               : (s.kv_dtype == SR_KV_BF16 && mfma_wins ? SR_KERNEL_MFMA : SR_KERNEL_VALU);
     if (p.kernel == SR_KERNEL_MFMA && s.kv_dtype != SR_KV_BF16) return SR_ERR_UNSUPPORTED;
     const int64_t n_items = static_cast<int64_t>(s.batch) * s.num_kv_heads;
     p.gp = pad_group(s.num_q_heads / s.num_kv_heads);
