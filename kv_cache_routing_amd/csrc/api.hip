@@ -290,7 +290,8 @@ int32_t sr_plan_parts(const sr_shape* shape, const sr_launch* launch, int32_t n_
     if (make_plan(*shape, launch, p) != SR_OK) return -1;
     const int32_t n_items = shape->batch * shape->num_kv_heads;
     if (n_active < 0 || n_active > n_items || wg < 0 || wg >= p.grid) return -1;
-    const int32_t chunk = chunk_positions(p.kernel, shape->head_dim, p.gp, p.waves);
+    const int32_t chunk = chunk_positions(p.kernel, shape->head_dim, p.gp, p.waves,
+                                          shape->kv_dtype == SR_KV_F32 ? 4 : 2);
     const SplitPlan sp =
         make_split_plan(p.fixed_splits, p.grid, p.split_cap, n_active, shape->seq_len, chunk);
     if (wg >= sp.P) return 0;

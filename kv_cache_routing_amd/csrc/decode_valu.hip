@@ -236,7 +236,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
 
 template <typename KV, int D, int GP, int NW>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
-    constexpr int U = valu_rows_per_lane(GP);
+    constexpr int U = valu_rows_per_lane(GP, static_cast<int>(sizeof(KV)));
     hipLaunchKernelGGL((k_decode_valu<KV, D, GP, NW, U>), dim3(a.grid), dim3(NW * 64), 0, st, a);
     return hipGetLastError();
 }

@@ -183,14 +183,17 @@ __host__ __device__ inline void item_parts(const SplitPlan& p, int32_t i, int32_
 }
 
 // Rows of cache per lane and tile of the vector-ALU kernel (U), and the
-// positions per chunk of either kernel.
-__host__ __device__ constexpr int valu_rows_per_lane(int gp) {
-    return gp >= 16 ? 1 : (gp >= 8 ? 2 : 8);
+// positions per chunk of either kernel.  fp32 rows take two 16-byte loads
+// per 8 elements, so they get half the rows (the two tile buffers then fit
+// the register file).
+__host__ __device__ constexpr int valu_rows_per_lane(int gp, int kv_bytes) {
+    return gp >= 16 ? 1 : (gp >= 8 ? 2 : (kv_bytes == 4 ? 4 : 8));
 }
 
-inline int32_t chunk_positions(int32_t kernel, int32_t head_dim, int32_t gp, int32_t waves) {
+inline int32_t chunk_positions(int32_t kernel, int32_t head_dim, int32_t gp, int32_t waves,
+                               int32_t kv_bytes) {
     if (kernel == SR_KERNEL_MFMA) return waves * 16;
-    return waves * (64 / (head_dim / 8)) * valu_rows_per_lane(gp);
+    return waves * (64 / (head_dim / 8)) * valu_rows_per_lane(gp, kv_bytes);
 }
 
 inline int32_t pad_group(int32_t g) {
