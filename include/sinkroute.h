@@ -152,7 +152,8 @@ sr_status sr_rope_append(const sr_shape* shape, const float* q_new, const float*
 
 /* Bytes of scratch the decode calls need for this shape and launch policy:
  * partial results of up to grid + B*Hkv parts (m, l, the position-0 logit
- * and acc, fp32) plus one ticket per item.
+ * and acc, fp32), one ticket per item, and room for a work list and count
+ * (sr_route_decode on large layers).
  * Depends on the current device's CU count in adaptive mode. Returns 0 on an
  * invalid or unsupported shape. */
 size_t sr_workspace_bytes(const sr_shape* shape, const sr_launch* launch);
@@ -180,14 +181,17 @@ sr_status sr_decode_attn(const sr_shape* shape, const sr_launch* launch, const f
                          const int32_t* work_list, const int32_t* n_active, float sm_scale,
                          void* ws, size_t ws_bytes, float* out, void* stream);
 
-/* Routing and decode in one launch (the fused form of sr_route followed by
- * sr_decode_attn, same arguments).  Every workgroup derives the routing
- * decision itself from q and k0 with the arithmetic of sr_route, so the
- * decisions, the work list and the output are bit-identical to the two-call
- * form under the same launch policy; workgroup 0 writes the routing outputs
- * scores / mask / work_list / n_active, each of which may be NULL.  Saves a
- * launch and the routing kernel per layer-step.  Envelope: B*Hkv <= 4096
- * (else SR_ERR_UNSUPPORTED: use the two calls). */
+/* Routing and decode in one call (sr_route followed by sr_decode_attn, same
+ * arguments).  For layers of up to 64 query heads (B*Hq <= 64) it is one
+ * launch: every workgroup derives the routing decision itself from q and k0
+ * with the arithmetic of sr_route, and workgroup 0 writes the routing
+ * outputs.  That saves a launch and the routing kernel per layer-step.
+ * Larger layers run the routing kernel and then the decode on `stream`,
+ * since scoring hundreds of heads in every workgroup costs more than the
+ * extra launch.  Either way the decisions, the work list and the output are
+ * bit-identical to the two-call form under the same launch policy.  scores /
+ * mask / work_list / n_active may each be NULL; the workspace holds the list
+ * and count when they are. */
 sr_status sr_route_decode(const sr_shape* shape, const sr_launch* launch, const float* q,
                           const void* k_cache, const void* v_cache, const float* k0,
                           const float* v0, float tau, float sm_scale, float* scores,

@@ -99,7 +99,7 @@ sr_status make_plan(const sr_shape& s, const sr_launch* launch, Plan& p) {
 constexpr size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct WsLayout {
-    size_t tickets, ml, acc, total;
+    size_t tickets, ml, acc, route, total;
 };
 
 WsLayout ws_layout(const sr_shape& s, const Plan& p) {
@@ -109,7 +109,10 @@ WsLayout ws_layout(const sr_shape& s, const Plan& p) {
     w.ml = align256(n_items * sizeof(uint32_t));
     const size_t parts = static_cast<size_t>(p.grid) + n_items;  // slots w + i, w < grid, i < n
     w.acc = w.ml + align256(parts * 3 * p.gp * sizeof(float));
-    w.total = w.acc + align256(parts * p.gp * s.head_dim * sizeof(float));
+    // work list and n_active of sr_route_decode's two-launch form, for callers
+    // that do not ask for them
+    w.route = w.acc + align256(parts * p.gp * s.head_dim * sizeof(float));
+    w.total = w.route + align256((n_items + 1) * sizeof(int32_t));
     return w;
 }
 
@@ -135,11 +138,8 @@ sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float
         return SR_ERR_INVALID_ARG;
     if (routed && !v0) return SR_ERR_INVALID_ARG;
     if (routed && !fused && (!work_list || !n_active)) return SR_ERR_INVALID_ARG;
-    if (fused) {
-        if (!fused->k0 || !aligned16(fused->k0) || isnan(fused->tau)) return SR_ERR_INVALID_ARG;
-        if (static_cast<int64_t>(s.batch) * s.num_kv_heads > kMaxFusedItems)
-            return SR_ERR_UNSUPPORTED;
-    }
+    if (fused && (!fused->k0 || !aligned16(fused->k0) || isnan(fused->tau)))
+        return SR_ERR_INVALID_ARG;
     Plan p;
     if ((st = make_plan(s, launch, p)) != SR_OK) return st;
     const WsLayout w = ws_layout(s, p);
@@ -183,6 +183,18 @@ sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float
     }
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (fused && static_cast<int64_t>(s.batch) * s.num_q_heads > kMaxFusedHeads) {
+        // large layer: the routing kernel, then the routed decode
+        int32_t* ws_list = reinterpret_cast<int32_t*>(base + w.route);  // [B*Hkv + 1]
+        int32_t* list = fused->work_list ? fused->work_list : ws_list;
+        int32_t* n_act = fused->n_active ? fused->n_active : ws_list + s.batch * s.num_kv_heads;
+        hipError_t e = launch_route(s, q, fused->k0, fused->tau, fused->scores, fused->mask, list,
+                                    n_act, hs);
+        if (e != hipSuccess) return SR_ERR_HIP;
+        a.fused = 0;
+        a.work_list = list;
+        a.n_active = n_act;
+    }
     hipError_t e = p.kernel == SR_KERNEL_MFMA ? launch_decode_mfma(s, a, p.gp, p.waves, hs)
                                                : launch_decode_valu(s, a, p.gp, p.waves, hs);
     return e == hipSuccess ? SR_OK : SR_ERR_HIP;

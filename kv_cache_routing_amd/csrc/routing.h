@@ -252,7 +252,10 @@ __device__ inline bool map_work(const DecodeArgs& a, WorkRange& r) {
         r.i_end = uniform(r.i_end);
     };
     if (a.fused) {
-        __shared__ uint8_t s_flag[kMaxFusedItems];
+        // the host runs fused routing only for n_items <= B*Hq <= kMaxFusedHeads <= NT:
+        // every item has a thread and one ballot pass partitions them
+        static_assert(kMaxFusedHeads <= NT, "one-pass partition needs a thread per item");
+        __shared__ uint8_t s_flag[kMaxFusedHeads];
         __shared__ int32_t s_wa[NT / 64], s_ws[NT / 64];
         __shared__ int32_t s_pick[3];  // items at positions i_begin, i_begin + 1; the sink
         const bool w0 = wg == 0;
@@ -260,30 +263,17 @@ __device__ inline bool map_work(const DecodeArgs& a, WorkRange& r) {
         route_items<NT, 8>(a.q, a.k0, a.tau, n_items, G, D, s_flag, w0 ? a.scores_out : nullptr,
                            w0 ? a.mask_out : nullptr);
         int32_t* list = w0 ? a.list_out : nullptr;
-        if (n_items <= NT) {
-            int32_t pos;
-            n_act = uniform(partition_one_pass<NT>(s_flag, n_items, s_wa, s_ws, pos));
-            plan_range(n_act);
-            const int32_t j = threadIdx.x;
-            if (j < n_items) {
-                if (pos == r.i_begin && pos < r.i_end) s_pick[0] = j;
-                if (pos == r.i_begin + 1 && pos < r.i_end) s_pick[1] = j;
-                if (pos == n_act + wg) s_pick[2] = j;
-                if (list) list[pos] = j;
-            }
-            __syncthreads();
-        } else {
-            n_act = uniform(count_active<NT>(s_flag, n_items, s_wa));
-            plan_range(n_act);
-            const int32_t ib = r.i_begin, ie = r.i_end;
-            const int32_t want_s = n_act + wg < n_items ? n_act + wg : -1;
-            partition_items<NT>(s_flag, n_items, n_act, s_wa, s_ws, [&](int32_t pos, int32_t j) {
-                if (pos == ib && pos < ie) s_pick[0] = j;
-                if (pos == ib + 1 && pos < ie) s_pick[1] = j;
-                if (pos == want_s) s_pick[2] = j;
-                if (list) list[pos] = j;
-            });
+        int32_t pos;
+        n_act = uniform(partition_one_pass<NT>(s_flag, n_items, s_wa, s_ws, pos));
+        plan_range(n_act);
+        const int32_t j = threadIdx.x;
+        if (j < n_items) {
+            if (pos == r.i_begin && pos < r.i_end) s_pick[0] = j;
+            if (pos == r.i_begin + 1 && pos < r.i_end) s_pick[1] = j;
+            if (pos == n_act + wg) s_pick[2] = j;
+            if (list) list[pos] = j;
         }
+        __syncthreads();
         if (w0 && threadIdx.x == 0 && a.n_active_out) a.n_active_out[0] = n_act;
         r.item[0] = uniform(s_pick[0]);
         r.item[1] = uniform(s_pick[1]);

@@ -42,8 +42,13 @@ struct DecodeArgs {
     float* alpha0_out;         // [B][Hq] weight of position 0 per head (optional)
 };
 
-// The fused route+decode prologue keeps one flag per item in LDS.
-constexpr int32_t kMaxFusedItems = 4096;
+// sr_route_decode runs routing inside the decode launch (every workgroup
+// scores every head) only for layers of up to this many query heads; larger
+// layers run the routing kernel and then the decode, which measured faster
+// (a prologue that scores 128 heads per workgroup already costs more than
+// the extra launch).  The fused prologue keeps one flag per item in LDS and
+// partitions the items in one ballot pass, so it needs items <= heads <= 64.
+constexpr int32_t kMaxFusedHeads = 64;
 
 // Adaptive mode never makes a split shorter than this many positions.
 constexpr int64_t kMinSplitLen = 512;

@@ -175,8 +175,9 @@ def test_fused_route_decode_validation():
     assert fused(s, v0=0) == N.SR_ERR_INVALID_ARG
     assert fused(s, tau=float("nan")) == N.SR_ERR_INVALID_ARG
     assert fused(s, ws_bytes=16) == N.SR_ERR_INVALID_ARG
-    big = shape(B=1024, Hq=8, Hkv=8)            # 8192 items > 4096
-    assert fused(big) == N.SR_ERR_UNSUPPORTED
+    big = shape(B=4096, Hq=8, Hkv=8)            # 32768 items: the routing kernel's maximum
+    assert fused(big, ws_bytes=16) == N.SR_ERR_INVALID_ARG  # runs as two launches; ws too small
+    assert fused(shape(B=4097, Hq=8, Hkv=8)) == N.SR_ERR_UNSUPPORTED
 
 
 # --- work division (host-side model of what the decode kernel streams) ----------

@@ -346,6 +346,45 @@ def test_fused_full_size_70b_layer_sampled():
     assert_outputs(out.cpu().numpy()[b, g * G:(g + 1) * G], ref, f"fused 70b item {j}")
 
 
+# --- sr_route_decode picks one launch (<= 64 query heads) or two ----------------
+@pytest.mark.parametrize("wl", [
+    Workload("rd-64-heads", 2, 32, 8, 128, 9000, "bf16", seed=171, sink_plan=("count", 4)),
+    Workload("rd-72-heads", 9, 8, 8, 128, 3000, "bf16", seed=172, sink_plan=("bernoulli", 0.5)),
+], ids=lambda w: w.name)
+def test_route_decode_forms_match_two_calls(wl):
+    layer = make_layer(wl)
+    q, k, v = upload(layer)
+    k0, v0, r, out2 = run_routed(q, k, v, wl.tau, launch("auto"))
+    out1, rf = sr.route_decode(q, k, v, k0, v0, wl.tau)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    for name in ("scores", "mask", "work_list", "n_active"):
+        assert torch.equal(getattr(rf, name), getattr(r, name)), name
+
+
+def test_route_decode_two_launch_form_without_routing_outputs():
+    """Large layer, every routing output NULL: the list and count live in the
+    workspace; the output equals the two calls'."""
+    import ctypes
+    from kv_cache_routing_amd import _native as N
+    wl = Workload("rd-null-128-heads", 4, 32, 8, 128, 5000, "bf16", seed=173,
+                  sink_plan=("count", 4))
+    layer = make_layer(wl)
+    q, k, v = upload(layer)
+    k0, v0, _, ref = run_routed(q, k, v, wl.tau, launch("auto"))
+    shape = sr.make_shape(q, k, v)
+    ws = sr.Workspace(shape, None, q.device)
+    out = torch.empty_like(q)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = N.lib.sr_route_decode(ctypes.byref(shape), None, P(q), P(k), P(v), P(k0), P(v0),
+                               ctypes.c_float(wl.tau), 0.0, None, None, None, None, P(ws.buf),
+                               ws.nbytes, P(out),
+                               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    N.check(st, "sr_route_decode")
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
 # --- many items: every branch of the routing partition ----------------------------
 # The routing partition takes one ballot pass when every item has a thread of
 # its own (up to 256 items in the fused prologue, 1024 in the routing kernel)
