@@ -129,7 +129,11 @@ sr_status sr_record_sink(const sr_shape* shape, const void* k_cache, const void*
  *   mask    out u8 [B][Hkv]: 1 = sink.
  *   work_list out i32 [B*Hkv]: active items ascending, then sinks ascending.
  *   n_active  out i32 [1]: number of active items (stays on the device).
- * Runs as one workgroup; B*Hq heads of 3*d multiply-adds each. */
+ * B*Hq heads of 3*d multiply-adds each, spread over one workgroup per 16
+ * groups (at most 1024 workgroups).  Up to 16 groups that is one launch;
+ * above, a second launch on `stream` partitions the groups, with mask as the
+ * channel between the two.  Scores and decisions are the same bit for bit in
+ * every form. */
 sr_status sr_route(const sr_shape* shape, const float* q, const float* k0, float tau,
                    float* scores, uint8_t* mask, int32_t* work_list, int32_t* n_active,
                    void* stream);
@@ -152,8 +156,9 @@ sr_status sr_rope_append(const sr_shape* shape, const float* q_new, const float*
 
 /* Bytes of scratch the decode calls need for this shape and launch policy:
  * partial results of up to grid + B*Hkv parts (m, l, the position-0 logit
- * and acc, fp32), one ticket per item, and room for a work list and count
- * (sr_route_decode on large layers).
+ * and acc, fp32), one ticket per item, and, for sr_route_decode on large
+ * layers, the routing kernel's ticket and room for a work list, a count and
+ * one flag byte per group.
  * Depends on the current device's CU count in adaptive mode. Returns 0 on an
  * invalid or unsupported shape. */
 size_t sr_workspace_bytes(const sr_shape* shape, const sr_launch* launch);
@@ -188,10 +193,12 @@ sr_status sr_decode_attn(const sr_shape* shape, const sr_launch* launch, const f
  * outputs.  That saves a launch and the routing kernel per layer-step.
  * Larger layers run the routing kernel and then the decode on `stream`,
  * since scoring hundreds of heads in every workgroup costs more than the
- * extra launch.  Either way the decisions, the work list and the output are
+ * extra launch; the routing kernel is then a single launch at any size (the
+ * workgroup that finishes scoring last partitions, through a ticket in the
+ * workspace).  Either way the decisions, the work list and the output are
  * bit-identical to the two-call form under the same launch policy.  scores /
- * mask / work_list / n_active may each be NULL; the workspace holds the list
- * and count when they are. */
+ * mask / work_list / n_active may each be NULL; the workspace holds the
+ * flags, list and count when they are. */
 sr_status sr_route_decode(const sr_shape* shape, const sr_launch* launch, const float* q,
                           const void* k_cache, const void* v_cache, const float* k0,
                           const float* v0, float tau, float sm_scale, float* scores,

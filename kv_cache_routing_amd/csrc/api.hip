@@ -24,7 +24,7 @@ int cu_count() {
     return n;
 }
 
-constexpr int32_t kMaxItems = 32768;  // route kernel keeps one flag per item in LDS
+constexpr int32_t kMaxItems = 32768;  // the supported envelope (tested at the maximum)
 
 size_t elem_size(const sr_shape& s) { return s.kv_dtype == SR_KV_BF16 ? 2 : 4; }
 
@@ -109,10 +109,12 @@ WsLayout ws_layout(const sr_shape& s, const Plan& p) {
     w.ml = align256(n_items * sizeof(uint32_t));
     const size_t parts = static_cast<size_t>(p.grid) + n_items;  // slots w + i, w < grid, i < n
     w.acc = w.ml + align256(parts * 3 * p.gp * sizeof(float));
-    // work list and n_active of sr_route_decode's two-launch form, for callers
-    // that do not ask for them
+    // sr_route_decode's two-launch form: work list, n_active and ticket
+    // [n_items + 2] int32, then one flag byte per item; the routing kernel's
+    // ticket lives here, the rest serves callers that do not ask for the list,
+    // the count or the mask
     w.route = w.acc + align256(parts * p.gp * s.head_dim * sizeof(float));
-    w.total = w.route + align256((n_items + 1) * sizeof(int32_t));
+    w.total = w.route + align256((n_items + 2) * sizeof(int32_t) + n_items);
     return w;
 }
 
@@ -185,11 +187,15 @@ sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (fused && static_cast<int64_t>(s.batch) * s.num_q_heads > kMaxFusedHeads) {
         // large layer: the routing kernel, then the routed decode
-        int32_t* ws_list = reinterpret_cast<int32_t*>(base + w.route);  // [B*Hkv + 1]
+        const int32_t n_items = s.batch * s.num_kv_heads;
+        int32_t* ws_list = reinterpret_cast<int32_t*>(base + w.route);
+        uint32_t* ticket = reinterpret_cast<uint32_t*>(ws_list + n_items + 1);
+        uint8_t* ws_flags = reinterpret_cast<uint8_t*>(ws_list + n_items + 2);
         int32_t* list = fused->work_list ? fused->work_list : ws_list;
-        int32_t* n_act = fused->n_active ? fused->n_active : ws_list + s.batch * s.num_kv_heads;
-        hipError_t e = launch_route(s, q, fused->k0, fused->tau, fused->scores, fused->mask, list,
-                                    n_act, hs);
+        int32_t* n_act = fused->n_active ? fused->n_active : ws_list + n_items;
+        uint8_t* flags = fused->mask ? fused->mask : ws_flags;
+        hipError_t e = launch_route(s, q, fused->k0, fused->tau, fused->scores, flags, list,
+                                    n_act, ticket, hs);
         if (e != hipSuccess) return SR_ERR_HIP;
         a.fused = 0;
         a.work_list = list;
@@ -224,7 +230,7 @@ sr_status sr_route(const sr_shape* shape, const float* q, const float* k0, float
     if (st != SR_OK) return st;
     if (!q || !k0 || !scores || !mask || !work_list || !n_active) return SR_ERR_INVALID_ARG;
     if (isnan(tau)) return SR_ERR_INVALID_ARG;
-    hipError_t e = launch_route(*shape, q, k0, tau, scores, mask, work_list, n_active,
+    hipError_t e = launch_route(*shape, q, k0, tau, scores, mask, work_list, n_active, nullptr,
                                 static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SR_OK : SR_ERR_HIP;
 }

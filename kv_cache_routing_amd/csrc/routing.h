@@ -74,6 +74,141 @@ __device__ inline void head_cosines16(const float* __restrict__ q, const float* 
     }
 }
 
+// Every head of item j (G heads, rows j*G .. j*G + G - 1 of q) against the
+// item's position-0 key, by one aligned 16-lane group; returns, in every lane,
+// whether every head has cos >= tau.  The products, their order and the
+// reduction tree are head_cosines16's, so each score is the one that function
+// gives bit for bit; the key row is loaded and its norm reduced once for all
+// G heads.  Heads go U at a time with every load of a batch issued before its
+// arithmetic; the slots of a short last batch re-read the batch's first head
+// and are not computed (the batch size is the same in every lane).  Lane r of
+// the group writes the batch's r-th score when scores is non-null.  d is 64
+// or 128.  All 64 lanes of the wave must be active.
+template <int U>
+__device__ inline bool score_item16(const float* __restrict__ q, const float* __restrict__ k0,
+                                    int32_t j, int32_t G, int32_t d, int hl, float tau,
+                                    float* scores) {
+    const float* kp = k0 + static_cast<int64_t>(j) * d;
+    float4 xk[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) xk[k] = *reinterpret_cast<const float4*>(kp + 4 * hl + (64 * k < d ? 64 * k : 0));
+    float kk = 0.f;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        if (64 * k < d) {
+            const float4 y = xk[k];
+            kk = fmaf(y.x, y.x, kk);
+            kk = fmaf(y.y, y.y, kk);
+            kk = fmaf(y.z, y.z, kk);
+            kk = fmaf(y.w, y.w, kk);
+        }
+    }
+    const float sk = sqrtf(group_allreduce_sum<16>(kk));
+    bool sink = true;
+    for (int32_t c0 = 0; c0 < G; c0 += U) {
+        const int32_t n_h = G - c0 < U ? G - c0 : U;
+        const float* qb = q + (static_cast<int64_t>(j) * G + c0) * d;
+        float4 xq[U][2];
+#pragma unroll
+        for (int r = 0; r < U; ++r) {
+            const float* qp = qb + static_cast<int64_t>(r < n_h ? r : 0) * d;
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+                xq[r][k] = *reinterpret_cast<const float4*>(qp + 4 * hl + (64 * k < d ? 64 * k : 0));
+        }
+        float mine = 0.f;
+#pragma unroll
+        for (int r = 0; r < U; ++r) {
+            if (r >= n_h) break;
+            float qk = 0.f, qq = 0.f;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                if (64 * k < d) {
+                    const float4 x = xq[r][k], y = xk[k];
+                    qk = fmaf(x.x, y.x, qk);
+                    qk = fmaf(x.y, y.y, qk);
+                    qk = fmaf(x.z, y.z, qk);
+                    qk = fmaf(x.w, y.w, qk);
+                    qq = fmaf(x.x, x.x, qq);
+                    qq = fmaf(x.y, x.y, qq);
+                    qq = fmaf(x.z, x.z, qq);
+                    qq = fmaf(x.w, x.w, qq);
+                }
+            }
+            const float dot = group_allreduce_sum<16>(qk);
+            const float nq = group_allreduce_sum<16>(qq);
+            const float den = sqrtf(nq) * sk;
+            const float c = den > 0.f ? dot / den : 0.f;
+            sink = sink && c >= tau;
+            if (hl == r) mine = c;
+        }
+        if (scores && hl < n_h) scores[static_cast<int64_t>(j) * G + c0 + hl] = mine;
+    }
+    return sink;
+}
+
+// Stable partition of the items from their flags (1 = sink) in global
+// memory, by one workgroup of NT threads: active items in ascending order at
+// list positions [0, n_act), sinks in ascending order after them; *n_active =
+// n_act.  Thread t takes items 4t .. 4t + 3 of each tile of 4*NT and one
+// block-wide scan of packed (sink << 16 | active) counts places them; layers
+// of more than one tile count the active items in a first pass.  Starts and
+// ends with a workgroup barrier.
+template <int NT>
+__device__ inline void partition_flags(const uint8_t* flags, int32_t n_items, int32_t* list,
+                                       int32_t* n_active) {
+    constexpr int NWV = NT / 64, TILE = 4 * NT;
+    static_assert(TILE < 65536, "packed 16-bit counts");
+    __shared__ int32_t s_tot[NWV];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    int32_t n_act = 0;
+    if (n_items > TILE) {
+        int32_t local = 0;
+        for (int32_t j = threadIdx.x; j < n_items; j += NT) local += flags[j] ? 0 : 1;
+        for (int o = 32; o > 0; o >>= 1) local += __shfl_xor(local, o);
+        if (lane == 0) s_tot[wave] = local;
+        __syncthreads();
+        for (int w = 0; w < NWV; ++w) n_act += s_tot[w];
+        __syncthreads();
+    }
+    int32_t base_a = 0, base_s = 0;
+    for (int32_t t0 = 0; t0 < n_items; t0 += TILE) {
+        const int32_t j0 = t0 + 4 * static_cast<int32_t>(threadIdx.x);
+        uint32_t f = 0;  // bit e: item j0 + e is a sink; bit 4 + e: it exists
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (j0 + e < n_items) f |= (flags[j0 + e] ? 1u : 0u) << e | 1u << (4 + e);
+        const int32_t cs = __popc(f & 0xFu), ca = __popc(f >> 4) - cs;
+        const int32_t mine = cs << 16 | ca;
+        int32_t x = mine;  // inclusive scan over the wave
+        for (int o = 1; o < 64; o <<= 1) {
+            const int32_t y = __shfl_up(x, o);
+            if (lane >= o) x += y;
+        }
+        if (lane == 63) s_tot[wave] = x;
+        __syncthreads();
+        int32_t before = 0, tile = 0;
+        for (int w = 0; w < NWV; ++w) {
+            if (w < wave) before += s_tot[w];
+            tile += s_tot[w];
+        }
+        __syncthreads();
+        const int32_t ex = x - mine + before;
+        if (n_items <= TILE) n_act = tile & 0xFFFF;  // one tile: its total is the count
+        int32_t pa = base_a + (ex & 0xFFFF), ps = n_act + base_s + (ex >> 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (!(f >> (4 + e) & 1u)) break;
+            if (f >> e & 1u) list[ps++] = j0 + e;
+            else list[pa++] = j0 + e;
+        }
+        base_a += tile & 0xFFFF;
+        base_s += tile >> 16;
+    }
+    if (threadIdx.x == 0) *n_active = n_act;
+}
+
 // Scores of every head of the layer (B*Hq heads of G per item), computed by
 // NT threads; s_sink[j] ends 1 iff every head of item j has cos >= tau.
 // Heads and items are written to `scores` / `mask` when those are non-null.

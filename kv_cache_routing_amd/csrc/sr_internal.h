@@ -50,6 +50,9 @@ struct DecodeArgs {
 // partitions the items in one ballot pass, so it needs items <= heads <= 64.
 constexpr int32_t kMaxFusedHeads = 64;
 
+// Most workgroups the routing kernel spreads its scoring over.
+constexpr int32_t kRouteMaxWgs = 1024;
+
 // Adaptive mode never makes a split shorter than this many positions.
 constexpr int64_t kMinSplitLen = 512;
 // Launch defaults: wave64s per decode workgroup and workgroups per CU in
@@ -210,9 +213,11 @@ inline int32_t pad_group(int32_t g) {
 // Host launchers, one per translation unit.
 hipError_t launch_record(const sr_shape& s, const void* k, const void* v, float* k0, float* v0,
                          hipStream_t st);
+// ticket: a zeroed counter in device memory, or null (a second launch then
+// partitions large layers).
 hipError_t launch_route(const sr_shape& s, const float* q, const float* k0, float tau,
-                        float* scores, uint8_t* mask, int32_t* work_list, int32_t* n_active,
-                        hipStream_t st);
+                        float* scores, uint8_t* flags, int32_t* work_list, int32_t* n_active,
+                        uint32_t* ticket, hipStream_t st);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_rope_append(const sr_shape& s, const float* q_new, const float* k_new,
                               const float* v_new, const float* inv_freq, int64_t pos,

@@ -80,3 +80,12 @@ def oracle_inputs(layer):
 
 def ticket_region(ws, n_items: int) -> torch.Tensor:
     return ws.buf[: 4 * n_items].view(torch.int32)
+
+
+def route_ticket(ws, n_items: int) -> int:
+    """The routing kernel's ticket in a workspace of exactly sr_workspace_bytes:
+    the last region holds the list, n_active and the ticket ([n_items + 2]
+    int32), then one flag byte per item, padded to 256 bytes."""
+    region = ((n_items + 2) * 4 + n_items + 255) // 256 * 256
+    off = ws.nbytes - region + 4 * (n_items + 1)
+    return int(ws.buf[off:off + 4].view(torch.int32).cpu()[0])

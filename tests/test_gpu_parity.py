@@ -13,8 +13,8 @@ import pytest
 import torch
 
 import oracle
-from parity import (assert_outputs, assert_route, log, oracle_inputs, sink_rows_exact,
-                    ticket_region, upload)
+from parity import (assert_outputs, assert_route, log, oracle_inputs, route_ticket,
+                    sink_rows_exact, ticket_region, upload)
 from workloads import (CONFIGS, L70B_128K_B8, L8B_128K, L8B_256K_B4, L8B_512K, SINK_FRACTIONS,
                        TINY, Workload, as_numpy, make_caches, make_layer, make_layer_bulk,
                        make_queries, sweep)
@@ -362,13 +362,16 @@ def test_route_decode_forms_match_two_calls(wl):
         assert torch.equal(getattr(rf, name), getattr(r, name)), name
 
 
-def test_route_decode_two_launch_form_without_routing_outputs():
-    """Large layer, every routing output NULL: the list and count live in the
-    workspace; the output equals the two calls'."""
+@pytest.mark.parametrize("wl", [
+    Workload("rd-null-128-heads", 4, 32, 8, 128, 5000, "bf16", seed=173, sink_plan=("count", 4)),
+    Workload("rd-null-512-heads", 16, 32, 8, 128, 3000, "bf16", seed=174,
+             sink_plan=("bernoulli", 0.5)),
+], ids=lambda w: w.name)
+def test_route_decode_two_launch_form_without_routing_outputs(wl):
+    """Large layer, every routing output NULL: the list, the count and the
+    flags live in the workspace; the output equals the two calls'."""
     import ctypes
     from kv_cache_routing_amd import _native as N
-    wl = Workload("rd-null-128-heads", 4, 32, 8, 128, 5000, "bf16", seed=173,
-                  sink_plan=("count", 4))
     layer = make_layer(wl)
     q, k, v = upload(layer)
     k0, v0, _, ref = run_routed(q, k, v, wl.tau, launch("auto"))
@@ -386,10 +389,10 @@ def test_route_decode_two_launch_form_without_routing_outputs():
 
 
 # --- many items: every branch of the routing partition ----------------------------
-# The routing partition takes one ballot pass when every item has a thread of
-# its own (up to 256 items in the fused prologue, 1024 in the routing kernel)
-# and a counted multi-pass otherwise; these layers sit on both sides of each
-# limit and at the envelope maxima (4096 items fused, 32768 two-call).
+# Layers of many items through both calls and sr_route_decode (whose large
+# layers take the routing kernel's ticketed form), on both sides of the
+# routing kernel's partition tiles and at the envelope maximum (32768 items,
+# two calls).
 MANY_ITEMS = [
     Workload("items-256", 32, 8, 8, 128, 24, "bf16", seed=141, sink_plan=("bernoulli", 0.5)),
     Workload("items-264-g2", 33, 16, 8, 128, 40, "bf16", seed=142, sink_plan=("bernoulli", 0.5)),
@@ -437,6 +440,52 @@ def test_route_at_item_envelope_maximum():
     _, _, r, out = run_routed(q, k, v, wl.tau, launch("auto"))
     _many_items_check(wl, out.cpu().numpy(), r)
     _many_items_check.cache.pop(wl.name)
+
+
+# --- routing kernel forms --------------------------------------------------------
+# The routing kernel spreads its scoring over one 256-thread workgroup per 16
+# items (at most 1024 workgroups, which then stride).  One workgroup also
+# partitions; with more, the partition runs in a second launch of 1024
+# threads (sr_route) or in the workgroup that draws the last ticket
+# (sr_route_decode's two-launch form).  The partition places 4 items per
+# thread in tiles of 4 x its threads (1024 items in the ticketed workgroup,
+# 4096 in the partition launch).  These layers sit on both sides of each
+# boundary; seq_len is tiny since only the routing is under test.
+ROUTE_FORMS = [
+    Workload("rt-16-items-1wg", 2, 128, 8, 64, 2, "bf16", seed=181, sink_plan=("bernoulli", 0.5)),
+    Workload("rt-17-items-2wg", 17, 16, 1, 64, 2, "bf16", seed=182, sink_plan=("bernoulli", 0.5)),
+    Workload("rt-1024-items", 128, 16, 8, 128, 2, "bf16", seed=183, sink_plan=("bernoulli", 0.5)),
+    Workload("rt-1025-items", 205, 5, 5, 64, 2, "bf16", seed=184, sink_plan=("bernoulli", 0.5)),
+    Workload("rt-4096-items", 512, 8, 8, 64, 2, "bf16", seed=185, sink_plan=("bernoulli", 0.5)),
+    Workload("rt-4097-items", 241, 17, 17, 128, 2, "bf16", seed=186, sink_plan=("bernoulli", 0.5)),
+    Workload("rt-16400-items-strided", 2050, 8, 8, 64, 2, "bf16", seed=187,
+             sink_plan=("bernoulli", 0.5)),
+]
+
+
+@pytest.mark.parametrize("wl", ROUTE_FORMS, ids=lambda w: w.name)
+def test_routing_kernel_forms(wl):
+    """sr_route against the oracle; sr_route_decode's routing outputs equal
+    sr_route's bit for bit, on two different layers in a row through one
+    workspace, and the routing ticket is back at zero after each."""
+    n_items = wl.batch * wl.num_kv_heads
+    log(f"{wl.name}: {n_items} items, {n_items * wl.group_size} heads")
+    ws = None
+    for rep in range(2):
+        layer = make_layer_bulk(wl.with_(seed=wl.seed + 1000 * rep))
+        q_np, k_np, _ = oracle_inputs(layer)
+        q, k, v = upload(layer)
+        k0, v0 = sr.record_sink(k, v)
+        r = sr.route(q, k0, wl.tau)
+        assert_route(r, q_np, k_np[:, :, 0], wl.tau)
+        if ws is None:
+            ws = sr.Workspace(sr.make_shape(q, k, v), None, q.device)
+        out, rf = sr.route_decode(q, k, v, k0, v0, wl.tau, ws=ws)
+        torch.cuda.synchronize()
+        for name in ("scores", "mask", "work_list", "n_active"):
+            assert torch.equal(getattr(rf, name), getattr(r, name)), (rep, name)
+        assert torch.equal(out, sr.decode_attn(q, k, v, v0, r.work_list, r.n_active))
+        assert route_ticket(ws, n_items) == 0
 
 
 # --- balanced work division ------------------------------------------------------
