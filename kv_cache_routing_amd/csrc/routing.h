@@ -10,6 +10,8 @@
 // when every one of its heads has cos >= tau; a zero norm scores 0.
 #pragma once
 
+#include <type_traits>
+
 #include "decode_common.h"
 
 namespace sr {
@@ -209,120 +211,61 @@ __device__ inline void partition_flags(const uint8_t* flags, int32_t n_items, in
     if (threadIdx.x == 0) *n_active = n_act;
 }
 
-// Scores of every head of the layer (B*Hq heads of G per item), computed by
-// NT threads; s_sink[j] ends 1 iff every head of item j has cos >= tau.
-// Heads and items are written to `scores` / `mask` when those are non-null.
-// Ends with a workgroup barrier.
+// The fused prologue's decisions for a layer of at most 64 items (B*Hq
+// heads of G per item), by NT threads: returns the 64-bit mask of sink items
+// (bit j set: every head of item j has cos >= tau), the same in every wave.
+// Each head leaves its pass flag in s_pass[head] (one byte per head, so
+// nothing needs clearing first); after one barrier, lane j of every wave ANDs
+// item j's G flags (all read before the first test) and a ballot gathers
+// them.  Scores are written when `scores` is non-null.
 template <int NT, int U>
-__device__ inline void route_items(const float* __restrict__ q, const float* __restrict__ k0,
-                                   float tau, int32_t n_items, int32_t G, int32_t d,
-                                   uint8_t* s_sink, float* scores, uint8_t* mask) {
+__device__ __attribute__((always_inline)) inline uint64_t fused_sink_mask(const float* __restrict__ q,
+                                           const float* __restrict__ k0, float tau,
+                                           int32_t n_items, int32_t G, int32_t d,
+                                           uint8_t* s_pass, float* scores) {
     constexpr int GROUPS = NT / 16;
-    const int tid = threadIdx.x, hl = tid & 15, hg = tid >> 4;
+    const int tid = threadIdx.x, hl = tid & 15, hg = tid >> 4, lane = tid & 63;
     const int32_t n_heads = n_items * G;
-    for (int32_t j = tid; j < n_items; j += NT) s_sink[j] = 1;
-    __syncthreads();
-    for (int32_t base = 0; base < n_heads; base += GROUPS * U) {
-        float c[U];
-        const int32_t n_live = (n_heads - base + GROUPS - 1) / GROUPS;  // same for every thread
-        head_cosines16<U>(q, k0, base + hg, GROUPS, n_heads, G, d, hl, n_live, c);
+    // Each lane group takes heads hg, hg + GROUPS, ...; a round issues the
+    // loads of only as many head slots as the round has live (1, 2, 4 or U),
+    // since every slot's loads go out unconditionally.
+    auto round = [&](auto slots, int32_t base, int32_t n_live) {
+        constexpr int V = decltype(slots)::value;
+        float c[V];
+        head_cosines16<V>(q, k0, base + hg, GROUPS, n_heads, G, d, hl, n_live, c);
 #pragma unroll
-        for (int r = 0; r < U; ++r) {
+        for (int r = 0; r < V; ++r) {
             const int32_t hh = base + hg + r * GROUPS;
             if (hh < n_heads && hl == 0) {
                 if (scores) scores[hh] = c[r];
-                if (!(c[r] >= tau)) s_sink[hh / G] = 0;  // one dissenting head keeps it active
+                s_pass[hh] = c[r] >= tau ? 1 : 0;  // NaN fails: the head dissents
             }
         }
+    };
+    for (int32_t base = 0; base < n_heads; base += GROUPS * U) {
+        const int32_t n_live = (n_heads - base + GROUPS - 1) / GROUPS;  // same for every thread
+        if (n_live <= 1) round(std::integral_constant<int, 1>{}, base, n_live);
+        else if (n_live <= 2 && U > 2) round(std::integral_constant<int, 2>{}, base, n_live);
+        else if (n_live <= 4 && U > 4) round(std::integral_constant<int, 4>{}, base, n_live);
+        else round(std::integral_constant<int, U>{}, base, n_live);
     }
     __syncthreads();
-    if (mask)
-        for (int32_t j = tid; j < n_items; j += NT) mask[j] = s_sink[j];
+    bool sink = false;
+    if (lane < n_items) {
+        uint8_t f[16];  // G <= 16
+#pragma unroll
+        for (int h = 0; h < 16; ++h) f[h] = s_pass[lane * G + (h < G ? h : 0)];
+        sink = true;
+#pragma unroll
+        for (int h = 0; h < 16; ++h) sink = sink & (f[h] != 0);
+    }
+    return __ballot(sink);
 }
 
-// Number of active items (s_sink[j] == 0), from every thread.
-template <int NT>
-__device__ inline int32_t count_active(const uint8_t* s_sink, int32_t n_items, int32_t* s_tmp) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int32_t local = 0;
-    for (int32_t j = threadIdx.x; j < n_items; j += NT) local += s_sink[j] ? 0 : 1;
-    for (int o = 32; o > 0; o >>= 1) local += __shfl_xor(local, o);
-    if (lane == 0) s_tmp[wave] = local;
-    __syncthreads();
-    int32_t n = 0;
-    for (int w = 0; w < NT / 64; ++w) n += s_tmp[w];
-    __syncthreads();
-    return n;
-}
-
-// Count and stable partition in one pass when every item has its own thread
-// (n_items <= NT): returns n_active; position_of(j) is then this thread's
-// item's list position (active items ascending at [0, n_active), sinks
-// ascending after them), valid when threadIdx.x < n_items.  Ends with a
-// workgroup barrier.
-template <int NT>
-__device__ inline int32_t partition_one_pass(const uint8_t* s_sink, int32_t n_items, int32_t* s_wa,
-                                             int32_t* s_ws, int32_t& pos) {
-    constexpr int NWV = NT / 64;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int32_t j = threadIdx.x;
-    const bool in = j < n_items;
-    const bool is_a = in && !s_sink[j];
-    const uint64_t ba = __ballot(is_a), bs = __ballot(in && !is_a);
-    if (lane == 0) {
-        s_wa[wave] = __popcll(ba);
-        s_ws[wave] = __popcll(bs);
-    }
-    __syncthreads();
-    int32_t n_act = 0, pa = 0, ps = 0;
-    for (int w = 0; w < NWV; ++w) {
-        n_act += s_wa[w];
-        if (w < wave) {
-            pa += s_wa[w];
-            ps += s_ws[w];
-        }
-    }
-    pos = is_a ? pa + __popcll(ba & lt) : n_act + ps + __popcll(bs & lt);
-    return n_act;
-}
-
-// Stable partition of the items: active ones in ascending order at list
-// positions [0, n_act), sinks in ascending order at [n_act, n_items).
-// visit(pos, j) is called once for every item by the thread that owns it.
-template <int NT, typename Visit>
-__device__ inline void partition_items(const uint8_t* s_sink, int32_t n_items, int32_t n_act,
-                                       int32_t* s_wa, int32_t* s_ws, Visit visit) {
-    constexpr int NWV = NT / 64;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int32_t base_a = 0, base_s = n_act;
-    for (int32_t c0 = 0; c0 < n_items; c0 += NT) {
-        const int32_t j = c0 + threadIdx.x;
-        const bool in = j < n_items;
-        const bool is_a = in && !s_sink[j];
-        const bool is_s = in && s_sink[j];
-        const uint64_t ba = __ballot(is_a), bs = __ballot(is_s);
-        if (lane == 0) {
-            s_wa[wave] = __popcll(ba);
-            s_ws[wave] = __popcll(bs);
-        }
-        __syncthreads();
-        int32_t pa = base_a, ps = base_s, ta = 0, ts = 0;
-        for (int w = 0; w < NWV; ++w) {
-            if (w < wave) {
-                pa += s_wa[w];
-                ps += s_ws[w];
-            }
-            ta += s_wa[w];
-            ts += s_ws[w];
-        }
-        if (is_a) visit(pa + __popcll(ba & lt), j);
-        if (is_s) visit(ps + __popcll(bs & lt), j);
-        base_a += ta;
-        base_s += ts;
-        __syncthreads();
-    }
+// Position of the k-th set bit (k = 0 for the lowest) of m, or -1.
+__device__ inline int32_t nth_set_bit(uint64_t m, int32_t k) {
+    for (; k > 0 && m; --k) m &= m - 1;
+    return m ? static_cast<int32_t>(__builtin_ctzll(m)) : -1;
 }
 
 }  // namespace sr
@@ -387,32 +330,33 @@ __device__ inline bool map_work(const DecodeArgs& a, WorkRange& r) {
         r.i_end = uniform(r.i_end);
     };
     if (a.fused) {
-        // the host runs fused routing only for n_items <= B*Hq <= kMaxFusedHeads <= NT:
-        // every item has a thread and one ballot pass partitions them
-        static_assert(kMaxFusedHeads <= NT, "one-pass partition needs a thread per item");
-        __shared__ uint8_t s_flag[kMaxFusedHeads];
-        __shared__ int32_t s_wa[NT / 64], s_ws[NT / 64];
-        __shared__ int32_t s_pick[3];  // items at positions i_begin, i_begin + 1; the sink
+        // the host runs fused routing only for n_items <= B*Hq <= kMaxFusedHeads <= 64:
+        // one ballot holds every item's decision, and the stable partition,
+        // the count and the items this workgroup needs follow from it in
+        // scalar registers, with no further barrier
+        static_assert(kMaxFusedHeads <= 64, "one ballot covers every item");
+        static_assert(kMaxFusedHeads <= 4 * (NT / 16), "one round of at most 4 heads per group");
+        __shared__ uint8_t s_pass[kMaxFusedHeads];
         const bool w0 = wg == 0;
-        if (threadIdx.x < 3) s_pick[threadIdx.x] = -1;
-        route_items<NT, 8>(a.q, a.k0, a.tau, n_items, G, D, s_flag, w0 ? a.scores_out : nullptr,
-                           w0 ? a.mask_out : nullptr);
-        int32_t* list = w0 ? a.list_out : nullptr;
-        int32_t pos;
-        n_act = uniform(partition_one_pass<NT>(s_flag, n_items, s_wa, s_ws, pos));
+        const uint64_t all = n_items >= 64 ? ~0ull : ((1ull << n_items) - 1);
+        const uint64_t sinks =
+            fused_sink_mask<NT, 4>(a.q, a.k0, a.tau, n_items, G, D, s_pass,
+                                   w0 ? a.scores_out : nullptr) & all;
+        const uint64_t act = all & ~sinks;
+        n_act = uniform(__popcll(act));
         plan_range(n_act);
+        if (r.i_begin < r.i_end) r.item[0] = uniform(nth_set_bit(act, r.i_begin));
+        if (r.i_begin + 1 < r.i_end) r.item[1] = uniform(nth_set_bit(act, r.i_begin + 1));
+        if (n_act + wg < n_items) sink_item = uniform(nth_set_bit(sinks, wg));
         const int32_t j = threadIdx.x;
-        if (j < n_items) {
-            if (pos == r.i_begin && pos < r.i_end) s_pick[0] = j;
-            if (pos == r.i_begin + 1 && pos < r.i_end) s_pick[1] = j;
-            if (pos == n_act + wg) s_pick[2] = j;
-            if (list) list[pos] = j;
+        if (w0 && j < n_items) {  // the routing outputs, from workgroup 0
+            const bool is_sink = (sinks >> j) & 1ull;
+            const uint64_t below = (1ull << j) - 1;
+            const int32_t pos = is_sink ? n_act + __popcll(sinks & below) : __popcll(act & below);
+            if (a.mask_out) a.mask_out[j] = is_sink ? 1 : 0;
+            if (a.list_out) a.list_out[pos] = j;
+            if (j == 0 && a.n_active_out) a.n_active_out[0] = n_act;
         }
-        __syncthreads();
-        if (w0 && threadIdx.x == 0 && a.n_active_out) a.n_active_out[0] = n_act;
-        r.item[0] = uniform(s_pick[0]);
-        r.item[1] = uniform(s_pick[1]);
-        sink_item = uniform(s_pick[2]);
     } else if (a.routed && n_items <= NT) {
         // one round trip: the whole list and n_active load together
         __shared__ int32_t s_list[NT];

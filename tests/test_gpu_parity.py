@@ -278,6 +278,10 @@ FUSED_CASES = [
     Workload("f-70b", 2, 64, 8, 128, 6000, "bf16", seed=62, sink_plan=("bernoulli", 0.5)),
     Workload("f-g3", 3, 12, 4, 64, 2100, "bf16", seed=63, sink_plan=("bernoulli", 0.5)),
     Workload("f-f32", 1, 16, 4, 128, 3333, "f32", seed=64, sink_plan=("count", 2)),
+    # the fused decisions are one 64-bit ballot: every bit, one short of it, G = 16
+    Workload("f-64-items-g1", 8, 8, 8, 64, 3000, "bf16", seed=65, sink_plan=("bernoulli", 0.5)),
+    Workload("f-63-items-g1", 9, 7, 7, 64, 2000, "bf16", seed=66, sink_plan=("bernoulli", 0.5)),
+    Workload("f-g16", 4, 16, 1, 128, 2500, "bf16", seed=67, sink_plan=("bernoulli", 0.5)),
 ]
 
 
