@@ -414,17 +414,18 @@ __device__ inline void merge_splits(const DecodeArgs& a, const MergeJob& u, floa
     }
 }
 
-// Merge the per-wave states held in LDS (s_m/s_l [NW][GP], s_acc [NW][GP][D])
+// Merge the per-wave states held in LDS (s_m/s_l [NW][GP], s_acc [NW][GP][DS],
+// rows of D values at a stride of DS)
 // into this workgroup's partial of the item.  When the workgroup is the
 // item's only part the partial is final and goes straight to `out`;
 // otherwise it is stored at slot u.mine with device-coherent stores and a
 // ticket is taken.  Returns true (in every thread) when this workgroup drew
 // the item's last ticket: it must then merge the item (merge_item), after
 // an acquire that this function has already made.
-template <int D, int GP, int NW>
+template <int D, int GP, int NW, int DS = D>
 __device__ inline bool finish_part(const DecodeArgs& a, const WorkUnit& u,
                                    const float (*s_m)[GP], const float (*s_l)[GP],
-                                   const float (*s_acc)[GP][D], const float* s_z0) {
+                                   const float (*s_acc)[GP][DS], const float* s_z0) {
     constexpr int NT = NW * 64;
     const int32_t G = a.group;
     if (u.parts == 1) {

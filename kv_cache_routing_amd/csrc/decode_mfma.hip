@@ -1,21 +1,30 @@
-// Split-K flash-decode of the active groups with QK on the bf16 matrix cores
-// (v_mfma_f32_16x16x32_bf16) and PV on the vector ALUs.  bf16 caches only.
+// Split-K flash-decode of the active groups on the bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16 for QK; PV on the vector ALUs for groups of up to
+// 4 heads, on v_mfma_f32_16x16x16_bf16 for 8 and 16).  bf16 caches only.
 //
-// QK as a 16x16 tile product per 16 cache rows: A = the G query heads padded
-// to 16 rows, B = 16 key rows (column = row of the cache), fp32 result
-// S[head][position].  Lane l feeds key row (l mod 16) with the 8 bf16 at
-// d = 32*kb + 8*(l/16) of k-block kb, so each load instruction takes 64
-// contiguous bytes of 16 rows.  The query is pre-scaled by sm_scale*log2(e)
-// and split exactly enough into hi + lo bf16 terms (two MFMAs per k-block):
-// products with the stored bf16 keys are exact and the logits carry ~2^-16
-// relative error in the query.
+// QK as a 16x16 tile product per 16 cache rows: the G query heads padded to
+// 16 rows against 16 key rows (row of the cache), fp32 logits.  Lane l feeds
+// key row (l mod 16) with the 8 bf16 at d = 32*kb + 8*(l/16) of k-block kb,
+// so each load instruction takes 64 contiguous bytes of 16 rows.  The query
+// is pre-scaled by sm_scale*log2(e) and split exactly enough into hi + lo
+// bf16 terms (two MFMAs per k-block): products with the stored bf16 keys are
+// exact and the logits carry ~2^-16 relative error in the query.
 //
-// Softmax in the MFMA output layout: lane l holds heads 4*(l/16)..+3 of
-// position (l mod 16), so the running maximum of a head is uniform across a
-// 16-lane row and is only recomputed (DPP row max) when some logit exceeds it.
-// The probabilities go through LDS to the PV layout, where lane l owns 8
-// consecutive elements of one value row (16 B, coalesced 1 KiB per wave
+// Groups of up to 4 heads: queries are the A operand, so lane l holds heads
+// 4*(l/16)..+3 of position (l mod 16) and the running maximum of a head is
+// uniform across a 16-lane row (DPP row max, only when some logit exceeds
+// it).  The probabilities go through LDS to the PV layout, where lane l owns
+// 8 consecutive elements of one value row (16 B, coalesced 1 KiB per wave
 // instruction) and accumulates p * V in fp32 for the group's heads.
+//
+// Groups of 8 or 16 heads, where p * V on the vector ALUs would bound the
+// kernel (2*G*d flops per 4*d bytes): the keys are the A operand, so lane l
+// holds head (l mod 16) at positions 4*(l/16)..+3.  That is the B operand
+// layout of the PV product out^T[d][head] += V^T[d][pos] P^T[pos][head] on
+// the 16x16x16 matrix cores, so the probabilities stay in registers (split
+// into hi + lo bf16 terms like the query) and each head's maximum, sum and
+// rescale live in its own lanes.  Only the value tile is transposed, through
+// a padded per-wave LDS tile; the accumulator is D/16 fragments of 4 floats.
 //
 // Method: SinkRouter README (github.com/streamer-AP/SinkRouter), decode-time
 // steps (tiled QK/PV with an online softmax, Split-K, in-kernel merge);
@@ -26,6 +35,7 @@ namespace sr {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short bf16x4;  // bf16 bits, 16x16x16 operands
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 __device__ inline uint32_t bf16_rne_bits(float x) {
@@ -46,6 +56,9 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
     constexpr int TPI = 64 / LPT;     // PV: rows per load instruction
     constexpr int UPS = 16 / TPI;     // PV: load instructions per 16 rows
     static_assert(GP <= 16, "at most 16 heads per group");
+    constexpr bool PVM = GP >= 8;     // PV on the matrix cores
+    constexpr int DS = PVM ? D + 1 : D;  // s_acc row stride (odd: no bank conflicts)
+    constexpr int VS = D + 4;         // s_v row stride in bf16 (264 / 136 B, 8-byte aligned)
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;      // MFMA layout
@@ -53,7 +66,8 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
 
     __shared__ __attribute__((aligned(16))) float s_p[NW][16][16];  // [pos][head]
     __shared__ float s_m[NW][GP], s_l[NW][GP];
-    __shared__ float s_acc[NW][GP][D];
+    __shared__ float s_acc[NW][GP][DS];
+    __shared__ __attribute__((aligned(16))) uint16_t s_v[NW][PVM ? 16 : 1][PVM ? VS : 1];
     __shared__ float s_z0[GP];  // logits of position 0 (in the part that holds it)
 
     WorkRange wr;
@@ -98,17 +112,23 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
         const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + u.b * a.stride_b + u.g * a.stride_h;
         const int64_t st = a.stride_t;
 
-        float m[4], lsum[4];  // heads 4*grp + i, uniform across the 16-lane row
+        // vector-ALU PV: m, lsum of heads 4*grp + i (uniform across the 16-lane
+        // row) and acc[h][e] of value elements 8*pchunk + e.  Matrix-core PV:
+        // m[0], lsum[0] of head col and accm[mb][i] = out^T[16*mb + 4*grp + i][col].
+        float m[4], lsum[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             m[i] = kNegInf;
             lsum[i] = 0.f;
         }
-        float acc[GP][8];
+        float acc[PVM ? 1 : GP][8];
 #pragma unroll
-        for (int h = 0; h < GP; ++h)
+        for (int h = 0; h < (PVM ? 1 : GP); ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+        f32x4 accm[PVM ? D / 16 : 1];
+#pragma unroll
+        for (int mb = 0; mb < (PVM ? D / 16 : 1); ++mb) accm[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         // One 16-position tile: the raw key and value bytes this lane loads.
         struct Raw {
@@ -131,7 +151,58 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
                 r.v[uu] = load_stream(vbase + tv * st + pchunk * 8);
             }
         };
-        auto compute = [&](const Raw& r, int64_t tile) {
+        auto compute_pvm = [&](const Raw& r, int64_t tile) {
+            // logits with the keys as A: s[i] = head col at position tile + 4*grp + i
+            f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const bf16x8 kv = __builtin_bit_cast(bf16x8, r.k[kb]);
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qhi[kb], s, 0, 0, 0);
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qlo[kb], s, 0, 0, 0);
+            }
+            // the tile's value rows into this wave's LDS tile, row-major
+#pragma unroll
+            for (int uu = 0; uu < UPS; ++uu) {
+                uint2* dst = reinterpret_cast<uint2*>(&s_v[wave][prow + TPI * uu][pchunk * 8]);
+                dst[0] = make_uint2(r.v[uu].x, r.v[uu].y);
+                dst[1] = make_uint2(r.v[uu].z, r.v[uu].w);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)  // ragged tail: positions past T weigh nothing
+                if (tile + 4 * grp + i >= u.t1) s[i] = kNegInf;
+            if (tile == 0 && grp == 0 && col < GP) s_z0[col] = s[0];  // position 0
+            float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            if (__any(mx > m[0])) {
+                const float mn = fmaxf(m[0], mx);
+                const float al = mn > m[0] ? fast_exp2(m[0] - mn) : 1.f;
+                m[0] = mn;
+                lsum[0] *= al;
+#pragma unroll
+                for (int mb = 0; mb < D / 16; ++mb) accm[mb] *= al;
+            }
+            bf16x4 phi, plo;  // P^T fragment, hi + lo bf16 terms
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = s[i] == kNegInf ? 0.f : fast_exp2(s[i] - m[0]);
+                lsum[0] += p;
+                const uint32_t h = bf16_rne_bits(p);
+                phi[i] = static_cast<short>(h);
+                plo[i] = static_cast<short>(bf16_rne_bits(p - bf16_bits_to_float(h)));
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int mb = 0; mb < D / 16; ++mb) {
+                bf16x4 vt;  // V^T fragment: d = 16*mb + col at positions 4*grp + j
+#pragma unroll
+                for (int j = 0; j < 4; ++j) vt[j] = static_cast<short>(s_v[wave][4 * grp + j][16 * mb + col]);
+                accm[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, phi, accm[mb], 0, 0, 0);
+                accm[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, plo, accm[mb], 0, 0, 0);
+            }
+            __builtin_amdgcn_wave_barrier();
+        };
+        auto compute_valu = [&](const Raw& r, int64_t tile) {
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
@@ -207,40 +278,60 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
             }
             __builtin_amdgcn_wave_barrier();
         };
+        auto compute = [&](const Raw& r, int64_t tile) {
+            if constexpr (PVM) compute_pvm(r, tile);
+            else compute_valu(r, tile);
+        };
 
         // Two-stage register pipeline over this part's chunks: the next tile's
         // loads are in flight while the current tile is computed.
         Raw ra, rb;
         stream_walk<16>(u.walk, wave, ra, rb, issue, compute);
 
-        // wave totals: sums over the 16 positions of a row, values over PV rows
+        if constexpr (PVM) {
+            // head col's sum over the wave's positions (the four lane rows)
+            lsum[0] += __shfl_xor(lsum[0], 16);
+            lsum[0] += __shfl_xor(lsum[0], 32);
+            if (col < GP) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lsum[i] = group_allreduce_sum<16>(lsum[i]);
+                for (int mb = 0; mb < D / 16; ++mb)
 #pragma unroll
-        for (int o = LPT; o < 64; o <<= 1)
+                    for (int i = 0; i < 4; ++i) s_acc[wave][col][16 * mb + 4 * grp + i] = accm[mb][i];
+                if (grp == 0) {
+                    s_m[wave][col] = m[0];
+                    s_l[wave][col] = lsum[0];
+                }
+            }
+        } else {
+            // wave totals: sums over the 16 positions of a row, values over PV rows
 #pragma unroll
-            for (int h = 0; h < GP; ++h)
+            for (int i = 0; i < 4; ++i) lsum[i] = group_allreduce_sum<16>(lsum[i]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], o);
-        if (prow == 0) {
+            for (int o = LPT; o < 64; o <<= 1)
 #pragma unroll
-            for (int h = 0; h < GP; ++h)
+                for (int h = 0; h < GP; ++h)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) s_acc[wave][h][pchunk * 8 + e] = acc[h][e];
-        }
-        if (col == 0) {
+                    for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], o);
+            if (prow == 0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int h = 4 * grp + i;
-                if (h < GP) {
-                    s_m[wave][h] = m[i];
-                    s_l[wave][h] = lsum[i];
+                for (int h = 0; h < GP; ++h)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) s_acc[wave][h][pchunk * 8 + e] = acc[h][e];
+            }
+            if (col == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int h = 4 * grp + i;
+                    if (h < GP) {
+                        s_m[wave][h] = m[i];
+                        s_l[wave][h] = lsum[i];
+                    }
                 }
             }
         }
         __syncthreads();
         job = merge_job(u);
-        return finish_part<D, GP, NW>(a, u, s_m, s_l, s_acc, s_z0);
+        return finish_part<D, GP, NW, DS>(a, u, s_m, s_l, s_acc, s_z0);
     };
     MergeJob job0{}, job1{};
     const bool owe1 = pass(wr.i_end - 1, job1);

@@ -92,6 +92,26 @@ def test_reduced_layers(wl, kernel):
     full_check(make_layer(wl), launch(kernel))
 
 
+# Groups of 8 and 16 heads take the PV product on the matrix cores (keys as
+# the A operand, value tile transposed through LDS): padded head counts,
+# ragged tails, one and seventeen positions, both head sizes, 4 and 8 waves.
+MFMA_PV = [
+    Workload("pv-g8-d64", 2, 16, 2, 64, 3001, "bf16", seed=31, sink_plan=("count", 1)),
+    Workload("pv-g16-d128", 1, 32, 2, 128, 4099, "bf16", seed=32, sink_plan=("count", 1)),
+    Workload("pv-g5-d128", 2, 10, 2, 128, 2500, "bf16", seed=33, sink_plan=("bernoulli", 0.5)),
+    Workload("pv-g12-d64", 1, 24, 2, 64, 1500, "bf16", seed=34, sink_plan=("count", 1)),
+    Workload("pv-g8-t1", 2, 16, 2, 128, 1, "bf16", seed=35, sink_plan=("none",)),
+    Workload("pv-g16-t17", 2, 16, 1, 64, 17, "bf16", seed=36, sink_plan=("none",)),
+]
+
+
+@pytest.mark.parametrize("wl", MFMA_PV, ids=lambda w: w.name)
+@pytest.mark.parametrize("waves", [4, 8])
+def test_matrix_core_pv_groups(wl, waves):
+    log(f"mfma pv {wl.name} waves={waves}")
+    full_check(make_layer(wl), launch("mfma", waves=waves))
+
+
 @pytest.mark.parametrize("kernel", BF16_KERNELS)
 def test_split_count_sweep(kernel):
     wl = Workload("8b-splits", 1, 32, 8, 128, 8192 + 77, "bf16", seed=21, sink_plan=("count", 4))
