@@ -563,7 +563,7 @@ def main():
         sr.dense_decode(q, k, v, launch=lau, ws=ws, out=out)
 
     kname = "k_decode_mfma" if (kernel == "mfma" or (kernel == "auto" and (wl.head_dim == 128 or
-                                                                          wl.group_size > 2))
+                                                                          wl.group_size > 4))
                                 and wl.kv_dtype == "bf16") else "k_decode_valu"
     alg = algorithmic_bytes(wl, n_active)
     if args.read_ceiling:

@@ -68,7 +68,7 @@ typedef enum { SR_KV_BF16 = 0, SR_KV_F32 = 1 } sr_kv_dtype;
 
 /* Which decode kernel runs the active groups. */
 typedef enum {
-    SR_KERNEL_AUTO = 0,  /* MFMA for bf16 caches with d = 128 or G > 2, VALU otherwise */
+    SR_KERNEL_AUTO = 0,  /* MFMA for bf16 caches with d = 128 or G > 4, VALU otherwise */
     SR_KERNEL_VALU = 1,  /* vector-ALU dot products for QK and PV */
     SR_KERNEL_MFMA = 2   /* bf16 matrix cores for QK (bf16 caches only) */
 } sr_kernel;

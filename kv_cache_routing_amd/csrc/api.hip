@@ -65,13 +65,14 @@ sr_status make_plan(const sr_shape& s, const sr_launch* launch, Plan& p) {
     if (l.waves_per_wg != 0 && l.waves_per_wg != 4 && l.waves_per_wg != 8) return SR_ERR_INVALID_ARG;
     p.waves = l.waves_per_wg ? l.waves_per_wg : kDefaultWaves;
     if (l.kernel < SR_KERNEL_AUTO || l.kernel > SR_KERNEL_MFMA) return SR_ERR_INVALID_ARG;
-    // Measured on MI355X (interleaved A/B, non-temporal loads): the matrix-core
-    // kernel leads for every bf16 group size at d = 128 (by 6-7 % at G = 1-2,
-    // 10-20 % at G = 4, 1.8x at G = 8, 5x at G = 16) and at d = 64 from G = 4
-    // on; at d = 64 with G <= 2 the vector-ALU kernel leads by 6-10 %.  fp32
+    // Measured on MI355X (interleaved A/B, non-temporal loads, dense decode over
+    // ~1 GiB): at d = 128 the matrix-core kernel leads for every bf16 group size
+    // (1-5 % at G = 1-2, 4 % at G = 4, 1.9x at G = 8, 7x at G = 16, PV on the
+    // matrix cores from G = 8); at d = 64 the vector-ALU kernel leads for G <= 4
+    // (7-8 %) and the matrix-core kernel from G = 5 on (1.7x and more).  fp32
     // caches take the vector-ALU kernel.
     const int32_t G = s.num_q_heads / s.num_kv_heads;
-    const bool mfma_wins = s.head_dim == 128 || G > 2;
+    const bool mfma_wins = s.head_dim == 128 || G > 4;
     p.kernel = l.kernel != SR_KERNEL_AUTO ? l.kernel
                : (s.kv_dtype == SR_KV_BF16 && mfma_wins ? SR_KERNEL_MFMA : SR_KERNEL_VALU);
     if (p.kernel == SR_KERNEL_MFMA && s.kv_dtype != SR_KV_BF16) return SR_ERR_UNSUPPORTED;
