@@ -40,14 +40,16 @@ __device__ inline float dpp(float x) {
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
-// Sum over aligned groups of N lanes (N in 4, 8, 16) with DPP; every lane of a
-// group ends with the group's total.  All 64 lanes must be active.
+// Sum over aligned groups of N lanes (N in 4, 8, 16, 32) with DPP (and one
+// lane swap across rows for 32); every lane of a group ends with the group's
+// total.  All 64 lanes must be active.
 template <int N>
 __device__ inline float group_allreduce_sum(float x) {
     x += dpp<0xB1>(x);                          // quad_perm [1,0,3,2]
     x += dpp<0x4E>(x);                          // quad_perm [2,3,0,1]
     if constexpr (N >= 8) x += dpp<0x141>(x);   // row_half_mirror
     if constexpr (N >= 16) x += dpp<0x140>(x);  // row_mirror
+    if constexpr (N >= 32) x += __shfl_xor(x, 16);
     return x;
 }
 

@@ -1,12 +1,14 @@
 // Split-K flash-decode of the active groups with vector-ALU dot products.
 // Handles fp32 and bf16 caches, d in {64, 128}, any group size up to 16.
 //
-// Layout: a wave reads a tile of whole cache rows.  Each lane owns 8
-// consecutive elements of one row (16 B of bf16, 32 B of fp32), so a row is
-// spread over d/8 lanes (a "lane group") and one wave-wide load instruction
-// covers 64/(d/8) consecutive rows: fully coalesced.  QK is an 8-term dot
-// product per lane followed by a DPP all-reduce inside the lane group; PV
-// accumulates p * V for the lane's 8 elements.  Every lane group keeps its own
+// Layout: a wave reads a tile of whole cache rows.  Each lane owns E = 8
+// consecutive elements of one row (16 B of bf16, 32 B of fp32; E = 4, 16 B,
+// for fp32 groups of 16 heads, whose query and accumulator rows would not fit
+// the register file at 8), so a row is spread over d/E lanes (a "lane group")
+// and one wave-wide load instruction covers 64/(d/E) consecutive rows: fully
+// coalesced.  QK is an E-term dot product per lane followed by a DPP
+// all-reduce inside the lane group; PV accumulates p * V for the lane's E
+// elements.  Every lane group keeps its own
 // running maximum, sum and accumulator (online softmax in base 2, rescaled
 // only when a tile raises the maximum); the groups of a wave, then the waves
 // of the workgroup, are merged at the end of the split.
@@ -18,11 +20,13 @@
 namespace sr {
 namespace {
 
-template <typename KV>
-struct Row8;
+// The E elements of one row slice as fp32, from the W = sizeof(KV)*E/16
+// 16-byte loads that read them.
+template <typename KV, int E>
+struct RowSlice;
 
 template <>
-struct Row8<uint16_t> {  // 8 bf16 in one 16-byte load
+struct RowSlice<uint16_t, 8> {  // 8 bf16 in one 16-byte load
     __device__ static inline void unpack(const uint4 (&r)[1], float (&x)[8]) {
         const uint32_t w[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
 #pragma unroll
@@ -34,7 +38,7 @@ struct Row8<uint16_t> {  // 8 bf16 in one 16-byte load
 };
 
 template <>
-struct Row8<float> {  // 8 fp32 in two 16-byte loads
+struct RowSlice<float, 8> {  // 8 fp32 in two 16-byte loads
     __device__ static inline void unpack(const uint4 (&r)[2], float (&x)[8]) {
         const uint32_t w[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
 #pragma unroll
@@ -42,9 +46,19 @@ struct Row8<float> {  // 8 fp32 in two 16-byte loads
     }
 };
 
-template <typename KV, int D, int GP, int NW, int U>
+template <>
+struct RowSlice<float, 4> {  // 4 fp32 in one 16-byte load
+    __device__ static inline void unpack(const uint4 (&r)[1], float (&x)[4]) {
+        x[0] = __uint_as_float(r[0].x);
+        x[1] = __uint_as_float(r[0].y);
+        x[2] = __uint_as_float(r[0].z);
+        x[3] = __uint_as_float(r[0].w);
+    }
+};
+
+template <typename KV, int D, int GP, int NW, int U, int E>
 __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
-    constexpr int E = 8, LPT = D / E, TPI = 64 / LPT, TILE = TPI * U;
+    constexpr int LPT = D / E, TPI = 64 / LPT, TILE = TPI * U;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row = lane / LPT, chunk = lane % LPT;
 
@@ -73,12 +87,14 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
 #pragma unroll
             for (int h = 0; h < GP; ++h) {
                 if (h < G) {
-                    const float4 x0 = *reinterpret_cast<const float4*>(qb + h * D);
-                    const float4 x1 = *reinterpret_cast<const float4*>(qb + h * D + 4);
-                    qs[h][0] = x0.x * a.qscale; qs[h][1] = x0.y * a.qscale;
-                    qs[h][2] = x0.z * a.qscale; qs[h][3] = x0.w * a.qscale;
-                    qs[h][4] = x1.x * a.qscale; qs[h][5] = x1.y * a.qscale;
-                    qs[h][6] = x1.z * a.qscale; qs[h][7] = x1.w * a.qscale;
+#pragma unroll
+                    for (int e4 = 0; e4 < E; e4 += 4) {
+                        const float4 x = *reinterpret_cast<const float4*>(qb + h * D + e4);
+                        qs[h][e4] = x.x * a.qscale;
+                        qs[h][e4 + 1] = x.y * a.qscale;
+                        qs[h][e4 + 2] = x.z * a.qscale;
+                        qs[h][e4 + 3] = x.w * a.qscale;
+                    }
                 } else {
 #pragma unroll
                     for (int e = 0; e < E; ++e) qs[h][e] = 0.f;
@@ -127,7 +143,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
 #pragma unroll
             for (int v = 0; v < U; ++v) {
                 float kf[E];
-                Row8<KV>::unpack(r.k[v], kf);
+                RowSlice<KV, E>::unpack(r.k[v], kf);
                 const bool valid = tile + v * TPI + row < u.t1;
 #pragma unroll
                 for (int h = 0; h < GP; ++h) {
@@ -165,7 +181,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
 #pragma unroll
             for (int v = 0; v < U; ++v) {
                 float vf[E];
-                Row8<KV>::unpack(r.v[v], vf);
+                RowSlice<KV, E>::unpack(r.v[v], vf);
 #pragma unroll
                 for (int h = 0; h < GP; ++h) {
                     const float p = z[v][h] == kNegInf ? 0.f : fast_exp2(z[v][h] - m[h]);
@@ -237,7 +253,8 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
 template <typename KV, int D, int GP, int NW>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
     constexpr int U = valu_rows_per_lane(GP, static_cast<int>(sizeof(KV)));
-    hipLaunchKernelGGL((k_decode_valu<KV, D, GP, NW, U>), dim3(a.grid), dim3(NW * 64), 0, st, a);
+    constexpr int E = valu_elems_per_lane(GP, static_cast<int>(sizeof(KV)));
+    hipLaunchKernelGGL((k_decode_valu<KV, D, GP, NW, U, E>), dim3(a.grid), dim3(NW * 64), 0, st, a);
     return hipGetLastError();
 }
 

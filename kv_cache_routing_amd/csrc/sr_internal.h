@@ -190,18 +190,27 @@ __host__ __device__ inline void item_parts(const SplitPlan& p, int32_t i, int32_
     parts = (starts_there ? w_next - 1 : w_next) - w_lo + 1;
 }
 
-// Rows of cache per lane and tile of the vector-ALU kernel (U), and the
-// positions per chunk of either kernel.  fp32 rows take two 16-byte loads
-// per 8 elements, so they get half the rows (the two tile buffers then fit
-// the register file).
+// Elements of a cache row per lane (E), rows of cache per lane and tile (U)
+// of the vector-ALU kernel, and the positions per chunk of either kernel.
+// fp32 rows take two 16-byte loads per 8 elements, so they get half the rows
+// (the two tile buffers then fit the register file).  fp32 groups of 16 heads
+// take 4 elements per lane: the lane's query and accumulator rows (2 x GP x E
+// floats) would not fit the register file at 8.
+__host__ __device__ constexpr int valu_elems_per_lane(int gp, int kv_bytes) {
+    return gp >= 16 && kv_bytes == 4 ? 4 : 8;
+}
+
 __host__ __device__ constexpr int valu_rows_per_lane(int gp, int kv_bytes) {
-    return gp >= 16 ? 1 : (gp >= 8 ? 2 : (kv_bytes == 4 ? 4 : 8));
+    return valu_elems_per_lane(gp, kv_bytes) == 4
+               ? 4
+               : (gp >= 16 ? 1 : (gp >= 8 ? 2 : (kv_bytes == 4 ? 4 : 8)));
 }
 
 inline int32_t chunk_positions(int32_t kernel, int32_t head_dim, int32_t gp, int32_t waves,
                                int32_t kv_bytes) {
     if (kernel == SR_KERNEL_MFMA) return waves * 16;
-    return waves * (64 / (head_dim / 8)) * valu_rows_per_lane(gp, kv_bytes);
+    return waves * (64 / (head_dim / valu_elems_per_lane(gp, kv_bytes))) *
+           valu_rows_per_lane(gp, kv_bytes);
 }
 
 inline int32_t pad_group(int32_t g) {

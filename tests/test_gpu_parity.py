@@ -80,6 +80,9 @@ REDUCED = [
     Workload("g6-d64", 3, 12, 2, 64, 999, "bf16", seed=17, sink_plan=("bernoulli", 0.5)),
     Workload("f32-d128-g4", 1, 16, 4, 128, 3333, "f32", seed=18, sink_plan=("count", 2)),
     Workload("f32-g8-d64", 2, 16, 2, 64, 700, "f32", seed=19, sink_plan=("count", 1)),
+    # fp32 groups of 16 heads: 4 elements per lane (lane groups of 32 at d = 128)
+    Workload("f32-g16-d128", 1, 32, 2, 128, 2999, "f32", seed=20, sink_plan=("count", 1)),
+    Workload("f32-g16-d64", 2, 16, 1, 64, 1001, "f32", seed=23, sink_plan=("bernoulli", 0.5)),
 ]
 
 
@@ -564,6 +567,7 @@ EIGHT_WAVES = [
     Workload("w8-8b", 1, 32, 8, 128, 12345, "bf16", seed=161, sink_plan=("count", 4)),
     Workload("w8-g16-d64", 1, 32, 2, 64, 2000, "bf16", seed=162, sink_plan=("count", 1)),
     Workload("w8-f32", 1, 16, 4, 128, 3333, "f32", seed=163, sink_plan=("count", 2)),
+    Workload("w8-f32-g16", 1, 32, 2, 128, 1500, "f32", seed=165, sink_plan=("count", 1)),
     Workload("w8-bal-3of4", 1, 16, 4, 128, 65536, "bf16", seed=164, sink_plan=("count", 1)),
 ]
 
