@@ -562,9 +562,9 @@ def main():
         k, v, _, _ = caches[i % R]
         sr.dense_decode(q, k, v, launch=lau, ws=ws, out=out)
 
-    kname = "k_decode_mfma" if (kernel == "mfma" or (kernel == "auto" and (wl.head_dim == 128 or
-                                                                          wl.group_size > 4))
-                                and wl.kv_dtype == "bf16") else "k_decode_valu"
+    auto_mfma = wl.kv_dtype == "f32" or wl.head_dim == 128 or wl.group_size > 4
+    kname = "k_decode_mfma" if kernel == "mfma" or (kernel == "auto" and auto_mfma) \
+        else "k_decode_valu"
     alg = algorithmic_bytes(wl, n_active)
     if args.read_ceiling:
         best, rows = read_ceiling([t for c in caches for t in c[:2]], stream)

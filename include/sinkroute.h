@@ -68,9 +68,11 @@ typedef enum { SR_KV_BF16 = 0, SR_KV_F32 = 1 } sr_kv_dtype;
 
 /* Which decode kernel runs the active groups. */
 typedef enum {
-    SR_KERNEL_AUTO = 0,  /* MFMA for bf16 caches with d = 128 or G > 4, VALU otherwise */
+    SR_KERNEL_AUTO = 0,  /* MFMA for fp32 caches and for bf16 caches with d = 128 or
+                            G > 4; VALU for bf16 caches with d = 64 and G <= 4 */
     SR_KERNEL_VALU = 1,  /* vector-ALU dot products for QK and PV */
-    SR_KERNEL_MFMA = 2   /* bf16 matrix cores for QK (bf16 caches only) */
+    SR_KERNEL_MFMA = 2   /* matrix cores: bf16 caches, QK (and PV for G > 4) in bf16
+                            with fp32 accumulation; fp32 caches, QK and PV in fp32 */
 } sr_kernel;
 
 typedef struct {
@@ -176,9 +178,11 @@ sr_status sr_workspace_init(void* ws, size_t ws_bytes, void* stream);
  *   over t = 0..T-1, fp32 accumulation, split over the context and merged in
  *   ascending split order (bitwise reproducible for a given launch policy).
  *   sm_scale <= 0 means 1/sqrt(d).
- *   For bf16 caches the MFMA kernel splits each scaled query into a sum of
- *   bf16 terms; products with the stored bf16 keys are exact and the logits
- *   carry ~2^-16 relative error in the query, far below the tolerance.
+ *   For bf16 caches the MFMA kernel splits each scaled query (and, for
+ *   groups of more than 4 heads, each probability) into a sum of two bf16
+ *   terms; products with the stored bf16 keys and values are exact and the
+ *   results carry ~2^-16 relative error in those operands, far below the
+ *   tolerance.  For fp32 caches it multiplies in fp32.
  *   ws: at least sr_workspace_bytes(shape, launch) bytes, initialised once
  *   by sr_workspace_init. */
 sr_status sr_decode_attn(const sr_shape* shape, const sr_launch* launch, const float* q,

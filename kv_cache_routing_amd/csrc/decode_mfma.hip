@@ -353,31 +353,203 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
     }
 }
 
+// fp32 caches on the matrix cores: QK and PV on v_mfma_f32_16x16x4_f32, in
+// fp32 throughout.  That instruction takes one value per lane (K = 4 across
+// the four 16-lane rows), so the order in which d is contracted or produced
+// is free, and it is chosen for contiguous 16-byte loads:
+//   QK step kb (d/4 steps): lane (col, grp) feeds key row `col` and query head
+//     `col` at element 16*(kb/4) + 4*grp + kb%4 (per row, the four lane rows
+//     read 64 contiguous bytes per load instruction); the result holds head
+//     `col` at positions 4*grp + i, as in the bf16 kernel's groups of 8 and 16.
+//   PV step (kq, mb): position 4*grp + kq, output element
+//     4*m + 64*(mb/4) + mb%4 of row m = col (16 lanes read a whole 256-byte
+//     stretch of a value row per instruction); the probability is the lane's
+//     own p[kq], so nothing goes through LDS.
+// Every group size pads to 16 heads; partials, merge and work division are
+// the bf16 kernel's.
 template <int D, int GP, int NW>
+__global__ __launch_bounds__(NW * 64) void k_decode_mfma_f32(DecodeArgs a) {
+    constexpr int KD = D / 4;   // QK steps
+    constexpr int DV = D / 16;  // PV output blocks
+    constexpr int DS = D + 1;   // s_acc row stride (odd: no bank conflicts)
+    static_assert(GP <= 16, "at most 16 heads per group");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+
+    __shared__ float s_m[NW][GP], s_l[NW][GP];
+    __shared__ float s_acc[NW][GP][DS];
+    __shared__ float s_z0[GP];
+
+    WorkRange wr;
+    if (!map_work<D, NW * 64, NW * 16>(a, wr)) return;
+    const int32_t G = a.group;
+
+    auto pass = [&](int32_t part, MergeJob& job) -> bool {
+        const WorkUnit u = part_of<NW * 16>(a, wr, part);
+
+        float qv[KD];  // B operand of QK: head col, element 16*(kb/4) + 4*grp + kb%4
+        {
+            const float* qr = a.q + (static_cast<int64_t>(u.b) * a.num_q_heads +
+                                     static_cast<int64_t>(u.g) * G + col) * D + 4 * grp;
+            const bool real = col < G;
+#pragma unroll
+            for (int j = 0; j < KD / 4; ++j) {
+                const float4 x = real ? *reinterpret_cast<const float4*>(qr + 16 * j)
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+                qv[4 * j] = x.x * a.qscale;
+                qv[4 * j + 1] = x.y * a.qscale;
+                qv[4 * j + 2] = x.z * a.qscale;
+                qv[4 * j + 3] = x.w * a.qscale;
+            }
+        }
+        const float* kbase = static_cast<const float*>(a.k) + u.b * a.stride_b + u.g * a.stride_h;
+        const float* vbase = static_cast<const float*>(a.v) + u.b * a.stride_b + u.g * a.stride_h;
+        const int64_t st = a.stride_t;
+
+        float m = kNegInf, lsum = 0.f;  // head col
+        f32x4 accm[DV];                 // out[col][4*(4*grp + i) + 64*(mb/4) + mb%4]
+#pragma unroll
+        for (int mb = 0; mb < DV; ++mb) accm[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        struct Raw {
+            uint4 k[KD / 4];      // key row tile + col, elements 16*j + 4*grp ..
+            uint4 v[4][DV / 4];   // value rows tile + 4*grp + kq, elements 4*col + 64*h ..
+        };
+        const int64_t last = u.t1 - 1;
+        // Rows past T are clamped to the last row: a prefetch past the end costs
+        // one row and no branch.
+        auto issue = [&](Raw& r, int64_t tile) {
+            int64_t tk = tile + col;
+            tk = tk < u.t1 ? tk : last;
+            const float* kp = kbase + tk * st + 4 * grp;
+#pragma unroll
+            for (int j = 0; j < KD / 4; ++j) r.k[j] = load_stream(kp + 16 * j);
+#pragma unroll
+            for (int kq = 0; kq < 4; ++kq) {
+                int64_t tv = tile + 4 * grp + kq;
+                tv = tv < u.t1 ? tv : last;
+                const float* vp = vbase + tv * st + 4 * col;
+#pragma unroll
+                for (int h = 0; h < DV / 4; ++h) r.v[kq][h] = load_stream(vp + 64 * h);
+            }
+        };
+        auto compute = [&](const Raw& r, int64_t tile) {
+            f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < KD / 4; ++j) {
+                const uint4 k = r.k[j];
+                s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.x), qv[4 * j], s, 0, 0, 0);
+                s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.y), qv[4 * j + 1], s, 0, 0, 0);
+                s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.z), qv[4 * j + 2], s, 0, 0, 0);
+                s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.w), qv[4 * j + 3], s, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)  // ragged tail: positions past T weigh nothing
+                if (tile + 4 * grp + i >= u.t1) s[i] = kNegInf;
+            if (tile == 0 && grp == 0 && col < GP) s_z0[col] = s[0];  // position 0
+            float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            if (__any(mx > m)) {
+                const float mn = fmaxf(m, mx);
+                const float al = mn > m ? fast_exp2(m - mn) : 1.f;
+                m = mn;
+                lsum *= al;
+#pragma unroll
+                for (int mb = 0; mb < DV; ++mb) accm[mb] *= al;
+            }
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[i] = s[i] == kNegInf ? 0.f : fast_exp2(s[i] - m);
+                lsum += p[i];
+            }
+#pragma unroll
+            for (int kq = 0; kq < 4; ++kq)
+#pragma unroll
+                for (int h = 0; h < DV / 4; ++h) {
+                    const uint4 v = r.v[kq][h];
+                    accm[4 * h] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.x), p[kq], accm[4 * h], 0, 0, 0);
+                    accm[4 * h + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.y), p[kq], accm[4 * h + 1], 0, 0, 0);
+                    accm[4 * h + 2] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.z), p[kq], accm[4 * h + 2], 0, 0, 0);
+                    accm[4 * h + 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.w), p[kq], accm[4 * h + 3], 0, 0, 0);
+                }
+        };
+
+        Raw ra, rb;
+        stream_walk<16>(u.walk, wave, ra, rb, issue, compute);
+
+        lsum += __shfl_xor(lsum, 16);  // head col's sum over the wave's positions
+        lsum += __shfl_xor(lsum, 32);
+        if (col < GP) {
+#pragma unroll
+            for (int mb = 0; mb < DV; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    s_acc[wave][col][4 * (4 * grp + i) + 64 * (mb >> 2) + (mb & 3)] = accm[mb][i];
+            if (grp == 0) {
+                s_m[wave][col] = m;
+                s_l[wave][col] = lsum;
+            }
+        }
+        __syncthreads();
+        job = merge_job(u);
+        return finish_part<D, GP, NW, DS>(a, u, s_m, s_l, s_acc, s_z0);
+    };
+    MergeJob job0{}, job1{};
+    const bool owe1 = pass(wr.i_end - 1, job1);
+    bool owe0 = false;
+    if (wr.i_end - wr.i_begin == 2) {
+        __syncthreads();  // the first pass is done with LDS
+        owe0 = pass(wr.i_begin, job0);
+    }
+    for (int j = 0; j < 2; ++j) {
+        if (!(j == 0 ? owe0 : owe1)) continue;
+        __syncthreads();
+        MergeJob job;
+        job.slot = j == 0 ? job0.slot : job1.slot;
+        job.b = j == 0 ? job0.b : job1.b;
+        job.g = j == 0 ? job0.g : job1.g;
+        job.parts = j == 0 ? job0.parts : job1.parts;
+        job.base = j == 0 ? job0.base : job1.base;
+        merge_item<D, GP, NW>(a, job);
+    }
+}
+
+template <bool F32, int D, int GP, int NW>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((k_decode_mfma<D, GP, NW>), dim3(a.grid), dim3(NW * 64), 0, st, a);
+    if constexpr (F32)
+        hipLaunchKernelGGL((k_decode_mfma_f32<D, GP, NW>), dim3(a.grid), dim3(NW * 64), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_decode_mfma<D, GP, NW>), dim3(a.grid), dim3(NW * 64), 0, st, a);
     return hipGetLastError();
 }
 
-template <int D, int NW>
+template <bool F32, int D, int NW>
 hipError_t launch_g(const DecodeArgs& a, int gp, hipStream_t st) {
     switch (gp) {
-        case 1: return launch_t<D, 1, NW>(a, st);
-        case 2: return launch_t<D, 2, NW>(a, st);
-        case 4: return launch_t<D, 4, NW>(a, st);
-        case 8: return launch_t<D, 8, NW>(a, st);
-        case 16: return launch_t<D, 16, NW>(a, st);
+        case 1: return launch_t<F32, D, 1, NW>(a, st);
+        case 2: return launch_t<F32, D, 2, NW>(a, st);
+        case 4: return launch_t<F32, D, 4, NW>(a, st);
+        case 8: return launch_t<F32, D, 8, NW>(a, st);
+        case 16: return launch_t<F32, D, 16, NW>(a, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <bool F32>
+hipError_t launch_w(const sr_shape& s, const DecodeArgs& a, int gp, int waves, hipStream_t st) {
+    if (waves == 8)
+        return s.head_dim == 128 ? launch_g<F32, 128, 8>(a, gp, st) : launch_g<F32, 64, 8>(a, gp, st);
+    return s.head_dim == 128 ? launch_g<F32, 128, 4>(a, gp, st) : launch_g<F32, 64, 4>(a, gp, st);
 }
 
 }  // namespace
 
 hipError_t launch_decode_mfma(const sr_shape& s, const DecodeArgs& a, int gp, int waves,
                               hipStream_t st) {
-    if (s.kv_dtype != SR_KV_BF16) return hipErrorInvalidValue;
-    if (waves == 8) return s.head_dim == 128 ? launch_g<128, 8>(a, gp, st) : launch_g<64, 8>(a, gp, st);
-    return s.head_dim == 128 ? launch_g<128, 4>(a, gp, st) : launch_g<64, 4>(a, gp, st);
+    return s.kv_dtype == SR_KV_F32 ? launch_w<true>(s, a, gp, waves, st)
+                                   : launch_w<false>(s, a, gp, waves, st);
 }
 
 }  // namespace sr

@@ -102,8 +102,6 @@ def test_launch_policy_checks():
     assert decode(s, launch=N.SrLaunch(0, 9, 0, 0)) == N.SR_ERR_INVALID_ARG
     assert decode(s, launch=N.SrLaunch(0, 0, 0, 5)) == N.SR_ERR_INVALID_ARG   # 5 waves
     assert decode(s, launch=N.SrLaunch(0, 0, -1, 0)) == N.SR_ERR_INVALID_ARG
-    f32 = shape(dt=N.SR_KV_F32)
-    assert decode(f32, launch=N.SrLaunch(0, N.SR_KERNEL_MFMA, 0, 0)) == N.SR_ERR_UNSUPPORTED
 
 
 def test_split_policy_host_math():

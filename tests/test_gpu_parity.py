@@ -65,9 +65,10 @@ def full_check(layer, lau, tau=None, check_dense=True):
     return got
 
 
-def test_tiny_layer_full_parity():
-    log("tiny")
-    full_check(make_layer(TINY), launch("valu"))
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_tiny_layer_full_parity(kernel):
+    log(f"tiny {kernel}")
+    full_check(make_layer(TINY), launch(kernel))
 
 
 REDUCED = [
@@ -89,8 +90,6 @@ REDUCED = [
 @pytest.mark.parametrize("wl", REDUCED, ids=lambda w: w.name)
 @pytest.mark.parametrize("kernel", ["auto"] + BF16_KERNELS)
 def test_reduced_layers(wl, kernel):
-    if wl.kv_dtype == "f32" and kernel == "mfma":
-        pytest.skip("matrix-core kernel takes bf16 caches")
     log(f"reduced {wl.name} kernel={kernel}")
     full_check(make_layer(wl), launch(kernel))
 
@@ -311,8 +310,6 @@ FUSED_CASES = [
 @pytest.mark.parametrize("wl", FUSED_CASES, ids=lambda w: w.name)
 @pytest.mark.parametrize("kernel", ["auto", "valu", "mfma"])
 def test_fused_route_decode_matches_two_calls_bitwise(wl, kernel):
-    if wl.kv_dtype == "f32" and kernel == "mfma":
-        pytest.skip("matrix-core kernel takes bf16 caches")
     layer = make_layer(wl)
     q, k, v = upload(layer)
     lau = launch(kernel)
@@ -575,8 +572,6 @@ EIGHT_WAVES = [
 @pytest.mark.parametrize("wl", EIGHT_WAVES, ids=lambda w: w.name)
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
 def test_eight_wave_workgroups(wl, kernel):
-    if wl.kv_dtype == "f32" and kernel == "mfma":
-        pytest.skip("matrix-core kernel takes bf16 caches")
     layer = make_layer(wl)
     got = full_check(layer, launch(kernel, waves=8))
     q, k, v = upload(layer)
@@ -598,8 +593,6 @@ ALPHA_CASES = [
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
 @pytest.mark.parametrize("splits", [0, 1, 7])
 def test_dense_alpha0_matches_oracle(wl, kernel, splits):
-    if wl.kv_dtype == "f32" and kernel == "mfma":
-        pytest.skip("matrix-core kernel takes bf16 caches")
     layer = make_layer(wl)
     q, k, v = upload(layer)
     lau = launch(kernel, splits=splits)
