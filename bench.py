@@ -279,6 +279,63 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+def envelope_report(sr, torch, args):
+    """Dense-decode bandwidth over the supported envelope: bf16 and fp32 caches,
+    d = 64 and 128, G = 1..16, B = 1, 8 KV heads, T sized for ~1 GiB of K + V
+    (synthetic normal values).  Each kernel (automatic choice, vector ALU,
+    matrix cores) is timed interleaved with the others after a settling time,
+    as the median of 12 loops of 8 launches."""
+    import statistics
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(5)
+    rows = []
+    for dt in ("bf16", "f32"):
+        for d in (64, 128):
+            for G in (1, 2, 4, 8, 16):
+                Hkv, es = 8, (2 if dt == "bf16" else 4)
+                T = (1 << 30) // (Hkv * d * es * 2)
+                tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+                K = torch.randn((1, Hkv, T, d), generator=gen, device=dev).to(tdt)
+                V = torch.randn((1, Hkv, T, d), generator=gen, device=dev).to(tdt)
+                q = torch.randn((1, Hkv * G, d), generator=gen, device=dev)
+                shape = sr.make_shape(q, K, V)
+                nbytes = 2 * K.numel() * K.element_size()
+                fns = {}
+                for name in ("auto", "valu", "mfma"):
+                    lau = sr.make_launch(0, KERNEL_IDS[name], 0, 0)
+                    ws = sr.Workspace(shape, lau, dev)
+                    out = torch.empty_like(q)
+                    fns[name] = (lambda lau=lau, ws=ws, out=out:
+                                 sr.dense_decode(q, K, V, launch=lau, ws=ws, out=out))
+                t0 = time.time()
+                while time.time() - t0 < args.settle:
+                    for f in fns.values():
+                        f()
+                    torch.cuda.synchronize()
+                res = {n: [] for n in fns}
+                for _ in range(12):
+                    for n, f in fns.items():
+                        a = torch.cuda.Event(enable_timing=True)
+                        b = torch.cuda.Event(enable_timing=True)
+                        a.record()
+                        for _ in range(8):
+                            f()
+                        b.record()
+                        torch.cuda.synchronize()
+                        res[n].append(a.elapsed_time(b) * 1e3 / 8)
+                row = {"dtype": dt, "d": d, "G": G, "T": T, "bytes": nbytes}
+                for n, v in res.items():
+                    us = statistics.median(v)
+                    row[n] = {"us": round(us, 1), "gbs": round(nbytes / us / 1e3, 1)}
+                rows.append(row)
+                log(f"{dt} d={d} G={G}: " + "  ".join(
+                    f"{n} {row[n]['us']} us {row[n]['gbs']} GB/s" for n in res))
+                del K, V
+                torch.cuda.empty_cache()
+    print(json.dumps({"envelope": rows}), flush=True)
+    return 0
+
+
 def decode_layers_report(sr, torch, args):
     """Per-token attention over a stack of layers: each layer rotates the new
     token's q and k and appends k, v (sr_rope_append), then runs routed
@@ -469,6 +526,9 @@ def main():
     ap.add_argument("--tokens", type=int, default=8, help="decode steps of --decode-layers")
     ap.add_argument("--layer-range", type=int, nargs=2, default=None, metavar=("START", "END"),
                     help="layers routed by --decode-layers (inclusive); the rest run dense")
+    ap.add_argument("--envelope", action="store_true",
+                    help="dense-decode bandwidth of every kernel over the envelope "
+                         "(bf16/fp32, d = 64/128, G = 1..16, ~1 GiB each) and exit")
     ap.add_argument("--read-ceiling", action="store_true",
                     help="print the HBM read-probe sweep over the layer caches and exit")
     ap.add_argument("--roofline-only", action="store_true",
@@ -497,6 +557,8 @@ def main():
 
     if args.bos_proxy:
         return bos_proxy_report(sr, torch)
+    if args.envelope:
+        return envelope_report(sr, torch, args)
     if args.decode_layers:
         return decode_layers_report(sr, torch, args)
 
@@ -562,9 +624,7 @@ def main():
         k, v, _, _ = caches[i % R]
         sr.dense_decode(q, k, v, launch=lau, ws=ws, out=out)
 
-    auto_mfma = wl.kv_dtype == "f32" or wl.head_dim == 128 or wl.group_size > 4
-    kname = "k_decode_mfma" if kernel == "mfma" or (kernel == "auto" and auto_mfma) \
-        else "k_decode_valu"
+    kname = "k_decode_valu" if kernel == "valu" else "k_decode_mfma"
     alg = algorithmic_bytes(wl, n_active)
     if args.read_ceiling:
         best, rows = read_ceiling([t for c in caches for t in c[:2]], stream)

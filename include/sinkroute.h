@@ -68,8 +68,7 @@ typedef enum { SR_KV_BF16 = 0, SR_KV_F32 = 1 } sr_kv_dtype;
 
 /* Which decode kernel runs the active groups. */
 typedef enum {
-    SR_KERNEL_AUTO = 0,  /* MFMA for fp32 caches and for bf16 caches with d = 128 or
-                            G > 4; VALU for bf16 caches with d = 64 and G <= 4 */
+    SR_KERNEL_AUTO = 0,  /* MFMA (it leads at every measured shape) */
     SR_KERNEL_VALU = 1,  /* vector-ALU dot products for QK and PV */
     SR_KERNEL_MFMA = 2   /* matrix cores: bf16 caches, QK (and PV for G > 4) in bf16
                             with fp32 accumulation; fp32 caches, QK and PV in fp32 */

@@ -66,16 +66,12 @@ sr_status make_plan(const sr_shape& s, const sr_launch* launch, Plan& p) {
     p.waves = l.waves_per_wg ? l.waves_per_wg : kDefaultWaves;
     if (l.kernel < SR_KERNEL_AUTO || l.kernel > SR_KERNEL_MFMA) return SR_ERR_INVALID_ARG;
     // Measured on MI355X (interleaved A/B, non-temporal loads, dense decode over
-    // ~1 GiB): for bf16 caches at d = 128 the matrix-core kernel leads for every
-    // group size (1-5 % at G = 1-4, 1.9x at G = 8, 7x at G = 16, PV on the matrix
-    // cores from G = 8); at d = 64 the vector-ALU kernel leads for G <= 4 (7-8 %)
-    // and the matrix-core kernel from G = 5 on (1.7x and more).  For fp32 caches
-    // the fp32 matrix-core kernel streams at 6.6-6.95 TB/s for every group size,
-    // against 5.8-6.1 TB/s for the vector-ALU kernel (and ~2 TB/s at G = 16).
-    const int32_t G = s.num_q_heads / s.num_kv_heads;
-    const bool mfma_wins = s.kv_dtype == SR_KV_F32 || s.head_dim == 128 || G > 4;
-    p.kernel = l.kernel != SR_KERNEL_AUTO ? l.kernel
-                                          : (mfma_wins ? SR_KERNEL_MFMA : SR_KERNEL_VALU);
+    // ~1 GiB): the matrix-core kernels lead at every group size and head size.
+    // bf16 at d = 128: by 1-5 % at G = 1-4, 1.9x at G = 8, 7x at G = 16 (PV on
+    // the matrix cores from G = 8); bf16 at d = 64 (two tiles per wave step): by
+    // 3-5 % at G = 1-4 and 2x-7x above; fp32: 6.6-6.95 TB/s against 5.8-6.1 at
+    // G <= 8 and ~2 at G = 16.  The vector-ALU kernel remains on request.
+    p.kernel = l.kernel != SR_KERNEL_AUTO ? l.kernel : SR_KERNEL_MFMA;
     const int64_t n_items = static_cast<int64_t>(s.batch) * s.num_kv_heads;
     p.gp = pad_group(s.num_q_heads / s.num_kv_heads);
     const int64_t cap = (s.seq_len + kMinSplitLen - 1) / kMinSplitLen;

@@ -56,6 +56,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
     constexpr int TPI = 64 / LPT;     // PV: rows per load instruction
     constexpr int UPS = 16 / TPI;     // PV: load instructions per 16 rows
     static_assert(GP <= 16, "at most 16 heads per group");
+    constexpr int SUB = mfma_tiles_per_step(D, 2);  // 16-position tiles per wave step
     constexpr bool PVM = GP >= 8;     // PV on the matrix cores
     constexpr int DS = PVM ? D + 1 : D;  // s_acc row stride (odd: no bank conflicts)
     constexpr int VS = D + 4;         // s_v row stride in bf16 (264 / 136 B, 8-byte aligned)
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
     __shared__ float s_z0[GP];  // logits of position 0 (in the part that holds it)
 
     WorkRange wr;
-    if (!map_work<D, NW * 64, NW * 16>(a, wr)) return;
+    if (!map_work<D, NW * 64, NW * 16 * SUB>(a, wr)) return;
     const int32_t G = a.group;
 
     // One pass per item this workgroup has a part in: one, or two when the
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
     // one-pass case free of loop-carried state.  Merges that fall to this
     // workgroup run after the passes, when nothing else holds registers.
     auto pass = [&](int32_t part, MergeJob& job) -> bool {
-        const WorkUnit u = part_of<NW * 16>(a, wr, part);
+        const WorkUnit u = part_of<NW * 16 * SUB>(a, wr, part);
 
         // A operands: query row = col, elements d = 32*kb + 8*grp + e
         bf16x8 qhi[KB], qlo[KB];
@@ -130,15 +131,19 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
 #pragma unroll
         for (int mb = 0; mb < (PVM ? D / 16 : 1); ++mb) accm[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // One 16-position tile: the raw key and value bytes this lane loads.
-        struct Raw {
+        // One 16-position tile: the raw key and value bytes this lane loads; a
+        // wave step takes SUB of them.
+        struct Tile16 {
             uint4 k[KB];
             uint4 v[UPS];
+        };
+        struct Raw {
+            Tile16 t[SUB];
         };
         const int64_t last = u.t1 - 1;
         // Positions past T are clamped to the last row: every lane then reads the
         // same row, so a prefetch past the end costs one row and no branch.
-        auto issue = [&](Raw& r, int64_t tile) {
+        auto issue16 = [&](Tile16& r, int64_t tile) {
             int64_t tk = tile + col;
             tk = tk < u.t1 ? tk : last;
             const uint16_t* kp = kbase + tk * st + 8 * grp;
@@ -151,7 +156,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
                 r.v[uu] = load_stream(vbase + tv * st + pchunk * 8);
             }
         };
-        auto compute_pvm = [&](const Raw& r, int64_t tile) {
+        auto compute_pvm = [&](const Tile16& r, int64_t tile) {
             // logits with the keys as A: s[i] = head col at position tile + 4*grp + i
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -202,7 +207,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
             }
             __builtin_amdgcn_wave_barrier();
         };
-        auto compute_valu = [&](const Raw& r, int64_t tile) {
+        auto compute_valu = [&](const Tile16& r, int64_t tile) {
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
@@ -278,15 +283,22 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
             }
             __builtin_amdgcn_wave_barrier();
         };
+        auto issue = [&](Raw& r, int64_t tile) {
+#pragma unroll
+            for (int sb = 0; sb < SUB; ++sb) issue16(r.t[sb], tile + 16 * sb);
+        };
         auto compute = [&](const Raw& r, int64_t tile) {
-            if constexpr (PVM) compute_pvm(r, tile);
-            else compute_valu(r, tile);
+#pragma unroll
+            for (int sb = 0; sb < SUB; ++sb) {
+                if constexpr (PVM) compute_pvm(r.t[sb], tile + 16 * sb);
+                else compute_valu(r.t[sb], tile + 16 * sb);
+            }
         };
 
         // Two-stage register pipeline over this part's chunks: the next tile's
         // loads are in flight while the current tile is computed.
         Raw ra, rb;
-        stream_walk<16>(u.walk, wave, ra, rb, issue, compute);
+        stream_walk<16 * SUB>(u.walk, wave, ra, rb, issue, compute);
 
         if constexpr (PVM) {
             // head col's sum over the wave's positions (the four lane rows)

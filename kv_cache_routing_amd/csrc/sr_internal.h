@@ -206,9 +206,16 @@ __host__ __device__ constexpr int valu_rows_per_lane(int gp, int kv_bytes) {
                : (gp >= 16 ? 1 : (gp >= 8 ? 2 : (kv_bytes == 4 ? 4 : 8)));
 }
 
+// 16-position tiles per wave step of the matrix-core kernels: bf16 rows of
+// d = 64 are 256 bytes, and one tile per step left the loads too short to
+// keep HBM busy (two: 5.7 -> 6.7 TB/s at G = 8; at d = 128 one is best).
+__host__ __device__ constexpr int mfma_tiles_per_step(int head_dim, int kv_bytes) {
+    return kv_bytes == 2 && head_dim == 64 ? 2 : 1;
+}
+
 inline int32_t chunk_positions(int32_t kernel, int32_t head_dim, int32_t gp, int32_t waves,
                                int32_t kv_bytes) {
-    if (kernel == SR_KERNEL_MFMA) return waves * 16;
+    if (kernel == SR_KERNEL_MFMA) return waves * 16 * mfma_tiles_per_step(head_dim, kv_bytes);
     return waves * (64 / (head_dim / valu_elems_per_lane(gp, kv_bytes))) *
            valu_rows_per_lane(gp, kv_bytes);
 }
