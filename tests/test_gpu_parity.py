@@ -218,8 +218,16 @@ def test_all_sinks_and_no_sinks():
     assert_outputs(out.cpu().numpy(), oracle.dense_decode(q_np, k_np, v_np), "tau 1.5")
 
 
-def test_strided_cache_views():
-    wl = Workload("strided", 2, 16, 4, 128, 3000, "bf16", seed=51, sink_plan=("count", 2))
+@pytest.mark.parametrize("wl,kernel", [
+    (Workload("strided", 2, 16, 4, 128, 3000, "bf16", seed=51, sink_plan=("count", 2)), "mfma"),
+    (Workload("strided", 2, 16, 4, 128, 3000, "bf16", seed=51, sink_plan=("count", 2)), "valu"),
+    (Workload("strided-d64-g8", 2, 16, 2, 64, 2000, "bf16", seed=52, sink_plan=("count", 1)), "mfma"),
+    (Workload("strided-f32-g16", 1, 32, 2, 128, 1800, "f32", seed=53, sink_plan=("count", 1)), "mfma"),
+    (Workload("strided-f32-g4", 2, 16, 4, 64, 2100, "f32", seed=54, sink_plan=("count", 2)), "valu"),
+], ids=lambda x: x.name if hasattr(x, "name") else x)
+def test_strided_cache_views(wl, kernel):
+    """Caches viewed out of larger buffers (position stride > d): rows past T
+    hold poison that must never be read."""
     layer = make_layer(wl)
     B, Hkv, T, d = layer.k.shape
     big_k = torch.zeros((B, Hkv, T + 333, d), dtype=layer.k.dtype)
@@ -231,11 +239,11 @@ def test_strided_cache_views():
     k = big_k.cuda()[:, :, :T]
     v = big_v.cuda()[:, :, :T]
     q = layer.q.cuda()
-    k0, v0, r, out = run_routed(q, k, v, wl.tau, launch("auto"))
+    k0, v0, r, out = run_routed(q, k, v, wl.tau, launch(kernel))
     q_np, k_np, v_np = oracle_inputs(layer)
     mask = r.mask.cpu().numpy()
     ref = oracle.routed_decode(q_np, k_np, v_np, as_numpy(layer.v[:, :, 0]), mask)
-    assert_outputs(out.cpu().numpy(), ref, "strided routed")
+    assert_outputs(out.cpu().numpy(), ref, f"strided routed {kernel}")
 
 
 # --- full-size layers, sampled outputs ----------------------------------------
