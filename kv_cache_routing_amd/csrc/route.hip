@@ -34,8 +34,8 @@ __global__ void k_record(const void* k, const void* v, float* k0, float* v0, int
 // group scores every head of one item at a time (shared arithmetic in
 // routing.h) and writes its flag; the workgroups stride over the items.
 // Then one workgroup partitions the flags: the only workgroup of a
-// one-workgroup launch, else the one that draws the last ticket (when
-// `ticket` is given; a partition launch follows otherwise).  The ticket starts
+// one-workgroup launch (its flags stay in LDS), else the one that draws the
+// last ticket (when `ticket` is given; a partition launch follows otherwise).  The ticket starts
 // at zero and is left at zero.
 template <int NT>
 __global__ __launch_bounds__(NT) void k_route(
@@ -45,6 +45,18 @@ __global__ __launch_bounds__(NT) void k_route(
     int32_t d) {
     constexpr int GROUPS = NT / 16;
     const int hl = threadIdx.x & 15, hg = threadIdx.x >> 4;
+    if (gridDim.x == 1) {  // at most GROUPS items: flags through LDS, no device-wide publish
+        __shared__ uint8_t s_flag[GROUPS];
+        const bool own = hg < n_items;
+        const int32_t j = own ? hg : n_items - 1;  // idle groups re-score the last item
+        const bool sink = score_item16<8>(q, k0, j, G, d, hl, tau, own ? scores : nullptr);
+        if (own && hl == 0) {
+            flags[j] = sink ? 1 : 0;
+            s_flag[j] = sink ? 1 : 0;
+        }
+        partition_flags<NT>(s_flag, n_items, work_list, n_active);
+        return;
+    }
     const int32_t stride = static_cast<int32_t>(gridDim.x) * GROUPS;
     for (int32_t j0 = static_cast<int32_t>(blockIdx.x) * GROUPS; j0 < n_items; j0 += stride) {
         const bool own = j0 + hg < n_items;
@@ -57,21 +69,19 @@ __global__ __launch_bounds__(NT) void k_route(
         }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's flag stores acknowledged
-    if (gridDim.x > 1) {
-        if (!ticket) return;
-        __shared__ int s_last;
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const uint32_t prev =
-                __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const bool last = prev == gridDim.x - 1;
-            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            s_last = last;
-        }
-        __syncthreads();
-        if (!s_last) return;
-        if (threadIdx.x == 0) *ticket = 0u;  // ready for the next call
+    if (!ticket) return;
+    __shared__ int s_last;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev =
+            __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = prev == gridDim.x - 1;
+        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        s_last = last;
     }
+    __syncthreads();
+    if (!s_last) return;
+    if (threadIdx.x == 0) *ticket = 0u;  // ready for the next call
     partition_flags<NT>(flags, n_items, work_list, n_active);
 }
 
