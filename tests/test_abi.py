@@ -282,7 +282,8 @@ def test_plan_random_layouts_tile_every_item():
         waves = int(rng.choice([4, 8]))
         fixed = int(rng.choice([0, 0, 0, int(rng.integers(1, 40))]))
         per_cu = int(rng.choice([0, 1, 2, 3]))
-        s = shape(B=B, Hq=Hkv * G, Hkv=Hkv, d=d, T=T)
+        dt = int(rng.choice([N.SR_KV_BF16, N.SR_KV_F32]))
+        s = shape(B=B, Hq=Hkv * G, Hkv=Hkv, d=d, T=T, dt=dt)
         lau = N.SrLaunch(fixed, kern, per_cu, waves)
         grid = N.lib.sr_grid_size(ctypes.byref(s), ctypes.byref(lau))
         n_act = int(rng.integers(0, B * Hkv + 1))

@@ -6,6 +6,7 @@ bit-exact v0, active rows within max-abs 1e-2 / mean-abs 1e-3 / per-row
 rel-L2 1e-3 of the oracle (plus a tighter 2e-4 precision check).
 Small layers are checked in full; the full-size layers on sampled items.
 """
+import functools
 import math
 
 import numpy as np
@@ -778,3 +779,48 @@ def test_graph_replay_matches_eager():
         sr.dense_decode(q, k, v, launch=lau, ws=ws)  # eager work between replays
         torch.cuda.synchronize()
     assert int(ticket_region(ws, 8).abs().sum()) == 0
+
+
+# --- randomized layers --------------------------------------------------------------
+@functools.lru_cache(maxsize=None)
+def _random_layers(n, seed):
+    """n seeded random small layers over the whole envelope (any G up to 16,
+    both head sizes and dtypes, ragged lengths, 0-100 % sinks), each with a
+    random kernel, wave count and split policy.  A layer whose generated
+    scores fall within 0.05 of tau is redrawn, so every decision is clear."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.integers(1, 17))
+        B = int(rng.integers(1, 4))
+        d = int(rng.choice([64, 128]))
+        T = int(rng.integers(1, 5000))
+        dt = str(rng.choice(["bf16", "f32"]))
+        frac = float(rng.choice([0.0, 0.3, 0.5, 1.0]))
+        wl = Workload(f"rand{len(out)}", B, Hkv * G, Hkv, d, T, dt, seed=int(rng.integers(1, 1 << 30)),
+                      sink_plan=("bernoulli", frac))
+        kernel = str(rng.choice(["auto", "valu", "mfma"]))
+        waves = int(rng.choice([4, 8]))
+        splits = int(rng.choice([0, 0, int(rng.integers(1, 40))]))
+        layer = make_layer(wl)
+        q_np, k_np, _ = oracle_inputs(layer)
+        scores = oracle.route(q_np, k_np[:, :, 0], wl.tau)[0]
+        if np.abs(scores - wl.tau).min() < 0.05:
+            continue
+        out.append((layer, kernel, waves, splits))
+    return out
+
+
+@pytest.mark.parametrize("i", range(48))
+def test_randomized_layers_against_oracle(i):
+    layer, kernel, waves, splits = _random_layers(48, 7001)[i]
+    wl = layer.wl
+    log(f"{wl.name}: B={wl.batch} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} d={wl.head_dim} "
+        f"T={wl.seq_len} {wl.kv_dtype} {wl.sink_plan} kernel={kernel} waves={waves} splits={splits}")
+    lau = launch(kernel, splits=splits, waves=waves)
+    got = full_check(layer, lau)
+    q, k, v = upload(layer)
+    k0, v0 = sr.record_sink(k, v)
+    fused, _ = sr.route_decode(q, k, v, k0, v0, wl.tau, launch=lau)
+    assert torch.equal(fused.cpu(), torch.from_numpy(got))
