@@ -128,8 +128,13 @@ hipError_t launch_route(const sr_shape& s, const float* q, const float* k0, floa
     hipLaunchKernelGGL(k_route<NT>, dim3(grid), dim3(NT), 0, st, q, k0, tau, scores, flags,
                        work_list, n_active, ticket, n_items, G, s.head_dim);
     if (ticket || grid == 1) return hipGetLastError();
-    hipLaunchKernelGGL(k_partition<1024>, dim3(1), dim3(1024), 0, st, flags, work_list, n_active,
-                       n_items);
+    // one tile of 4 flags per thread: 256 threads up to 1024 groups, 1024 above
+    if (n_items <= 4 * 256)
+        hipLaunchKernelGGL(k_partition<256>, dim3(1), dim3(256), 0, st, flags, work_list,
+                           n_active, n_items);
+    else
+        hipLaunchKernelGGL(k_partition<1024>, dim3(1), dim3(1024), 0, st, flags, work_list,
+                           n_active, n_items);
     return hipGetLastError();
 }
 

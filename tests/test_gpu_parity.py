@@ -478,12 +478,12 @@ def test_route_at_item_envelope_maximum():
 # --- routing kernel forms --------------------------------------------------------
 # The routing kernel spreads its scoring over one 256-thread workgroup per 16
 # items (at most 1024 workgroups, which then stride).  One workgroup also
-# partitions; with more, the partition runs in a second launch of 1024
-# threads (sr_route) or in the workgroup that draws the last ticket
-# (sr_route_decode's two-launch form).  The partition places 4 items per
-# thread in tiles of 4 x its threads (1024 items in the ticketed workgroup,
-# 4096 in the partition launch).  These layers sit on both sides of each
-# boundary; seq_len is tiny since only the routing is under test.
+# partitions; with more, the partition runs in a second launch (sr_route: 256
+# threads up to 1024 items, 1024 above) or in the workgroup that draws the
+# last ticket (sr_route_decode's two-launch form).  The partition places 4
+# items per thread in tiles of 4 x its threads (1024 items for 256 threads,
+# 4096 for 1024).  These layers sit on both sides of each boundary; seq_len
+# is tiny since only the routing is under test.
 ROUTE_FORMS = [
     Workload("rt-16-items-1wg", 2, 128, 8, 64, 2, "bf16", seed=181, sink_plan=("bernoulli", 0.5)),
     Workload("rt-17-items-2wg", 17, 16, 1, 64, 2, "bf16", seed=182, sink_plan=("bernoulli", 0.5)),
