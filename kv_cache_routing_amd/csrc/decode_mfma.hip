@@ -1,6 +1,11 @@
-// Split-K flash-decode of the active groups on the bf16 matrix cores
-// (v_mfma_f32_16x16x32_bf16 for QK; PV on the vector ALUs for groups of up to
-// 4 heads, on v_mfma_f32_16x16x16_bf16 for 8 and 16).  bf16 caches only.
+// Split-K flash-decode of the active groups on the matrix cores.  bf16
+// caches: v_mfma_f32_16x16x32_bf16 for QK; PV on the vector ALUs for groups of
+// up to 4 heads, on v_mfma_f32_16x16x16_bf16 for 8 and 16.  fp32 caches: a
+// second kernel below, QK and PV on v_mfma_f32_16x16x4_f32.
+//
+// A wave step covers one 16-position tile (two at d = 64, where one tile is
+// only 4 KiB of bf16 keys and values: too little per wait to keep HBM busy);
+// the next step's loads are in flight while the current one is computed.
 //
 // QK as a 16x16 tile product per 16 cache rows: the G query heads padded to
 // 16 rows against 16 key rows (row of the cache), fp32 logits.  Lane l feeds
