@@ -31,6 +31,8 @@
  *  so d is contiguous and T_max >= T is allowed.  Element type is bf16 or
  *  fp32 (kv_dtype).  Every row start must be 16-byte aligned.
  *  q, out: fp32 [B][Hq][d] contiguous.  k0, v0: fp32 [B][Hkv][d] contiguous.
+ *  q, out and k0 are read or written 16 bytes at a time and must start
+ *  16-byte aligned; the other arrays need their element's alignment.
  *
  *  Pointers: every data pointer is a device pointer owned by the caller; the
  *  library never allocates, frees or keeps them.  `stream` is a hipStream_t

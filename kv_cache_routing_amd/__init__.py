@@ -43,6 +43,22 @@ def _need_cuda(*ts):
             raise ValueError("libsinkroute takes device tensors")
 
 
+def _expect(t: torch.Tensor, name: str, shape: tuple, dtype: torch.dtype):
+    """The kernels index these arrays densely from the cache shape: anything
+    else would read or write outside them."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}"
+                         f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+
+
+def _expect_q(q: torch.Tensor, k: torch.Tensor):
+    if q.dim() != 3 or k.dim() != 4 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[3]:
+        raise ValueError(f"q must be [B][Hq][d] matching the cache [B][Hkv][T][d]: "
+                         f"q {tuple(q.shape)}, cache {tuple(k.shape)}")
+    _expect(q, "q", q.shape, torch.float32)
+
+
 def make_shape(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None = None) -> N.SrShape:
     """sr_shape from q [B][Hq][d] and a cache view [B][Hkv][T][d]."""
     if k.dim() != 4:
@@ -108,10 +124,14 @@ def rope_append(q_new, k_new, v_new, k_cache, v_cache, pos: int, inv_freq,
                 q_out: torch.Tensor | None = None):
     """Rotate the new token's query/key to `pos`, append key and value to the
     full-capacity caches [B][Hkv][T_max][d] at `pos`; returns the rotated q."""
+    _expect_q(q_new, k_cache)
+    B, Hkv, _, d = k_cache.shape
+    _expect(k_new, "k_new", (B, Hkv, d), torch.float32)
+    _expect(v_new, "v_new", (B, Hkv, d), torch.float32)
+    _expect(inv_freq, "inv_freq", (d // 2,), torch.float32)
+    if q_out is not None:
+        _expect(q_out, "q_out", q_new.shape, torch.float32)
     _need_cuda(q_new, k_new, v_new, k_cache, v_cache, inv_freq)
-    for t in (q_new, k_new, v_new, inv_freq):
-        if t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError("q_new, k_new, v_new, inv_freq are contiguous fp32")
     shape = make_shape(q_new, k_cache, v_cache)
     if q_out is None:
         q_out = torch.empty_like(q_new)
@@ -140,12 +160,24 @@ class Routing:
     n_active: torch.Tensor   # [1] int32 (device)
 
 
+def _expect_routing(r: Routing, B: int, Hq: int, Hkv: int):
+    _expect(r.scores, "scores", (B, Hq), torch.float32)
+    _expect(r.mask, "mask", (B, Hkv), torch.uint8)
+    _expect(r.work_list, "work_list", (B * Hkv,), torch.int32)
+    _expect(r.n_active, "n_active", (1,), torch.int32)
+
+
 def route(q: torch.Tensor, k0: torch.Tensor, tau: float = 0.5, out: Routing | None = None):
-    _need_cuda(q, k0)
+    if k0.dim() != 3 or q.dim() != 3 or q.shape[0] != k0.shape[0] or q.shape[2] != k0.shape[2]:
+        raise ValueError(f"q [B][Hq][d] and k0 [B][Hkv][d] disagree: {tuple(q.shape)}, "
+                         f"{tuple(k0.shape)}")
     B, Hkv, d = k0.shape
     Hq = q.shape[1]
     if q.dtype != torch.float32 or k0.dtype != torch.float32:
         raise ValueError("q and k0 are fp32")
+    if out is not None:
+        _expect_routing(out, B, Hq, Hkv)
+    _need_cuda(q, k0)
     q = q.contiguous()
     k0 = k0.contiguous()
     shape = N.SrShape(B, Hq, Hkv, d, 1, Hkv * d, d, d, N.SR_KV_F32, 0)
@@ -162,9 +194,10 @@ def route(q: torch.Tensor, k0: torch.Tensor, tau: float = 0.5, out: Routing | No
 
 
 def _prep(q, k, v, launch, ws, out):
+    _expect_q(q, k)
+    if out is not None:
+        _expect(out, "out", q.shape, torch.float32)
     _need_cuda(q, k, v)
-    if q.dtype != torch.float32 or not q.is_contiguous():
-        raise ValueError("q must be contiguous fp32 [B][Hq][d]")
     shape = make_shape(q, k, v)
     if ws is None or not ws.fits(shape, launch):
         ws = Workspace(shape, launch, q.device)
@@ -176,6 +209,11 @@ def _prep(q, k, v, launch, ws, out):
 def decode_attn(q, k, v, v0, work_list, n_active, sm_scale: float = 0.0,
                 launch: N.SrLaunch | None = None, ws: Workspace | None = None,
                 out: torch.Tensor | None = None):
+    _expect_q(q, k)
+    B, Hkv, _, d = k.shape
+    _expect(v0, "v0", (B, Hkv, d), torch.float32)
+    _expect(work_list, "work_list", (B * Hkv,), torch.int32)
+    _expect(n_active, "n_active", (1,), torch.int32)
     shape, ws, out = _prep(q, k, v, launch, ws, out)
     N.check(N.lib.sr_decode_attn(ctypes.byref(shape), _lp(launch), _ptr(q), _ptr(k), _ptr(v),
                                  _ptr(v0), _ptr(work_list), _ptr(n_active),
@@ -188,8 +226,13 @@ def route_decode(q, k, v, k0, v0, tau: float = 0.5, sm_scale: float = 0.0,
                  launch: N.SrLaunch | None = None, ws: Workspace | None = None,
                  out: torch.Tensor | None = None, routing: Routing | None = None):
     """Routing and decode in one launch; returns (out, routing outputs)."""
+    _expect_q(q, k)
+    B, Hkv, _, d = k.shape
+    _expect(k0, "k0", (B, Hkv, d), torch.float32)
+    _expect(v0, "v0", (B, Hkv, d), torch.float32)
+    if routing is not None:
+        _expect_routing(routing, B, q.shape[1], Hkv)
     shape, ws, out = _prep(q, k, v, launch, ws, out)
-    B, Hkv, d = k0.shape
     if routing is None:
         dev = q.device
         routing = Routing(torch.empty((B, q.shape[1]), dtype=torch.float32, device=dev),

@@ -226,6 +226,7 @@ sr_status sr_route(const sr_shape* shape, const float* q, const float* k0, float
     sr_status st = check_shape(shape);
     if (st != SR_OK) return st;
     if (!q || !k0 || !scores || !mask || !work_list || !n_active) return SR_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k0)) return SR_ERR_INVALID_ARG;  // read as float4
     if (isnan(tau)) return SR_ERR_INVALID_ARG;
     hipError_t e = launch_route(*shape, q, k0, tau, scores, mask, work_list, n_active, nullptr,
                                 static_cast<hipStream_t>(stream));

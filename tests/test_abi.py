@@ -136,6 +136,10 @@ def test_route_and_record_validation():
     r = N.lib.sr_route(ctypes.byref(s), p(), p(), ctypes.c_float(float("nan")), p(), p(), p(), p(),
                        None)
     assert r == N.SR_ERR_INVALID_ARG
+    for q, k0 in ((FAKE + 4, FAKE), (FAKE, FAKE + 8)):  # q and k0 are read as float4
+        r = N.lib.sr_route(ctypes.byref(s), p(q), p(k0), ctypes.c_float(0.5), p(), p(), p(), p(),
+                           None)
+        assert r == N.SR_ERR_INVALID_ARG
     r = N.lib.sr_record_sink(ctypes.byref(s), p(), p(), p(0), p(), None)
     assert r == N.SR_ERR_INVALID_ARG
     r = N.lib.sr_record_sink(None, p(), p(), p(), p(), None)
