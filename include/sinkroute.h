@@ -113,7 +113,8 @@ typedef struct {
     int32_t num_splits;
     int32_t kernel;        /* sr_kernel */
     int32_t wgs_per_cu;    /* adaptive grid size in workgroups per CU (0 = 1) */
-    int32_t waves_per_wg;  /* 4 or 8 wave64s per workgroup (0 = 4) */
+    int32_t waves_per_wg;  /* 4 or 8 wave64s per workgroup (0 = 4); the vector-ALU
+                            * kernel runs groups of 9-16 heads with 4 */
 } sr_launch;
 
 /* Prefill side (README decode-time steps: the prefill path keeps the key at
@@ -209,6 +210,31 @@ sr_status sr_route_decode(const sr_shape* shape, const sr_launch* launch, const 
                           const float* v0, float tau, float sm_scale, float* scores,
                           uint8_t* mask, int32_t* work_list, int32_t* n_active, void* ws,
                           size_t ws_bytes, float* out, void* stream);
+
+/* One decode step of a layer in one launch: sr_rope_append of the new token
+ * at position T - 1 (T = shape->seq_len, the positions attended after the
+ * append), then sr_route_decode over positions 0 .. T - 1 (README decode-time
+ * steps: rotate the new query, compare it with the position-0 key, route,
+ * attend).  Every workgroup rotates the queries itself; the new key and value
+ * row of each KV group is written by the one workgroup that reads it in this
+ * launch (for a sink group, the one that copies its v0 rows), before it reads.
+ *   q_new, k_new, v_new, inv_freq: as sr_rope_append (unrotated, fp32).
+ *   q_out: the rotated query [B][Hq][d] (may be NULL; must not overlap q_new).
+ *   k_cache, v_cache: caches with room for position T - 1 (strides as usual).
+ *   k0, v0, tau, sm_scale, scores, mask, work_list, n_active, ws, out: as
+ *   sr_route_decode.
+ * Bitwise equal to sr_rope_append at pos = T - 1 followed by sr_route_decode
+ * with seq_len = T: the same q_out, cache rows, routing outputs and out.
+ * Layers of up to 64 query heads only (B*Hq <= 64, else SR_ERR_UNSUPPORTED:
+ * call the two entry points); T >= 2 (position 0 is the recorded sink key).
+ * tau > 1 gives the dense result of the same step. */
+sr_status sr_rope_route_decode(const sr_shape* shape, const sr_launch* launch,
+                               const float* q_new, const float* k_new, const float* v_new,
+                               const float* inv_freq, float* q_out, void* k_cache, void* v_cache,
+                               const float* k0, const float* v0, float tau, float sm_scale,
+                               float* scores, uint8_t* mask, int32_t* work_list,
+                               int32_t* n_active, void* ws, size_t ws_bytes, float* out,
+                               void* stream);
 
 /* Dense baseline: the decode kernel of sr_decode_attn with routing off
  * (identity work list, every item active).  sr_decode_attn with a work list

@@ -23,7 +23,7 @@ from ._native import (SR_KERNEL_AUTO, SR_KERNEL_MFMA, SR_KERNEL_VALU,  # noqa: F
                       SinkRouteError)
 
 __all__ = ["record_sink", "route", "decode_attn", "route_decode", "dense_decode",
-           "dense_decode_alpha0", "rope_append", "Workspace",
+           "dense_decode_alpha0", "rope_append", "rope_route_decode", "Workspace",
            "make_shape",
            "make_launch", "splits_for", "grid_size", "plan_parts", "SinkRouteError", "Routing",
            "SR_KERNEL_AUTO", "SR_KERNEL_VALU", "SR_KERNEL_MFMA"]
@@ -245,6 +245,43 @@ def route_decode(q, k, v, k0, v0, tau: float = 0.5, sm_scale: float = 0.0,
                                   _ptr(routing.work_list), _ptr(routing.n_active), _ptr(ws.buf),
                                   ws.nbytes, _ptr(out), _stream()), "sr_route_decode")
     return out, routing
+
+
+def rope_route_decode(q_new, k_new, v_new, k, v, k0, v0, inv_freq, tau: float = 0.5,
+                      sm_scale: float = 0.0, launch: N.SrLaunch | None = None,
+                      ws: Workspace | None = None, out: torch.Tensor | None = None,
+                      routing: Routing | None = None, q_out: torch.Tensor | None = None):
+    """One decode step in one launch: rotate the new token's query and key to
+    position T - 1 and append its key and value there, then route and attend
+    over positions 0 .. T - 1.  k, v are cache views [B][Hkv][T][d] whose last
+    row is the new token's (their storage must hold it).  Returns (out,
+    routing outputs, rotated q)."""
+    _expect_q(q_new, k)
+    B, Hkv, _, d = k.shape
+    for t, name in ((k_new, "k_new"), (v_new, "v_new"), (k0, "k0"), (v0, "v0")):
+        _expect(t, name, (B, Hkv, d), torch.float32)
+    _expect(inv_freq, "inv_freq", (d // 2,), torch.float32)
+    if q_out is not None:
+        _expect(q_out, "q_out", q_new.shape, torch.float32)
+    if routing is not None:
+        _expect_routing(routing, B, q_new.shape[1], Hkv)
+    shape, ws, out = _prep(q_new, k, v, launch, ws, out)
+    _need_cuda(k_new, v_new, k0, v0, inv_freq)
+    dev = q_new.device
+    if q_out is None:
+        q_out = torch.empty_like(q_new)
+    if routing is None:
+        routing = Routing(torch.empty((B, q_new.shape[1]), dtype=torch.float32, device=dev),
+                          torch.empty((B, Hkv), dtype=torch.uint8, device=dev),
+                          torch.empty((B * Hkv,), dtype=torch.int32, device=dev),
+                          torch.empty((1,), dtype=torch.int32, device=dev))
+    N.check(N.lib.sr_rope_route_decode(
+        ctypes.byref(shape), _lp(launch), _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(inv_freq),
+        _ptr(q_out), _ptr(k), _ptr(v), _ptr(k0), _ptr(v0), ctypes.c_float(tau),
+        ctypes.c_float(sm_scale), _ptr(routing.scores), _ptr(routing.mask),
+        _ptr(routing.work_list), _ptr(routing.n_active), _ptr(ws.buf), ws.nbytes, _ptr(out),
+        _stream()), "sr_rope_route_decode")
+    return out, routing, q_out
 
 
 def dense_decode_alpha0(q, k, v, sm_scale: float = 0.0, launch: N.SrLaunch | None = None,

@@ -21,7 +21,7 @@ EXPORTS = (
     "sr_record_sink", "sr_route", "sr_workspace_bytes", "sr_workspace_init",
     "sr_decode_attn", "sr_dense_decode", "sr_splits_for", "sr_grid_size",
     "sr_status_string", "sr_version", "sr_stream_read", "sr_route_decode",
-    "sr_dense_decode_alpha0", "sr_rope_append", "sr_plan_parts",
+    "sr_dense_decode_alpha0", "sr_rope_append", "sr_plan_parts", "sr_rope_route_decode",
 )
 
 
@@ -76,6 +76,8 @@ def _load():
         "sr_route_decode": (i32, [S, Lp, P, P, P, P, P, f32, f32, P, P, P, P, P, sz, P, P]),
         "sr_dense_decode_alpha0": (i32, [S, Lp, P, P, P, f32, P, sz, P, P, P]),
         "sr_rope_append": (i32, [S, P, P, P, P, ctypes.c_int64, P, P, P, P]),
+        "sr_rope_route_decode": (i32, [S, Lp, P, P, P, P, P, P, P, P, P, f32, f32, P, P, P, P,
+                                       P, sz, P, P]),
         "sr_splits_for": (i32, [S, Lp, i32]),
         "sr_grid_size": (i32, [S, Lp]),
         "sr_status_string": (ctypes.c_char_p, [i32]),

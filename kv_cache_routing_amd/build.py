@@ -28,7 +28,26 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
+    # per-kernel register / scratch report, checked below
+    "-Rpass-analysis=kernel-resource-usage",
 ]
+
+
+def scratch_kernels(remarks: str) -> list:
+    """Kernels the compiler gave per-lane scratch (private memory).  The
+    kernels keep all their state in registers and LDS; scratch appears when
+    a register array or struct is indexed at run time or registers spill,
+    and it slows the streaming loops by whole percents, so it fails the
+    build."""
+    bad, name = [], None
+    for ln in remarks.splitlines():
+        if "Function Name:" in ln:
+            name = ln.split("Function Name:")[1].split("[")[0].strip()
+        elif "ScratchSize [bytes/lane]:" in ln and name:
+            n = int(ln.split("ScratchSize [bytes/lane]:")[1].split("[")[0])
+            if n > 0:
+                bad.append(f"{name} ({n} bytes/lane)")
+    return bad
 
 
 def sources():
@@ -41,8 +60,19 @@ def _compile(src: str) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
-    noise = [ln for ln in (r.stderr or "").splitlines()
-             if "packed-fp32-ops" not in ln and ln.strip()]
+    bad = scratch_kernels(r.stderr or "")
+    if bad:
+        raise RuntimeError(f"{src}: kernels use scratch memory: " + "; ".join(bad))
+    noise, in_remark = [], False
+    for ln in (r.stderr or "").splitlines():
+        if "remark:" in ln:  # the resource report and the source lines it quotes
+            in_remark = True
+            continue
+        if in_remark and (ln.lstrip().startswith("|") or ln.split("|")[0].strip().isdigit()):
+            continue
+        in_remark = False
+        if "packed-fp32-ops" not in ln and ln.strip():
+            noise.append(ln)
     if noise:
         sys.stderr.write("\n".join(noise) + "\n")
     return obj

@@ -74,6 +74,8 @@ sr_status make_plan(const sr_shape& s, const sr_launch* launch, Plan& p) {
     p.kernel = l.kernel != SR_KERNEL_AUTO ? l.kernel : SR_KERNEL_MFMA;
     const int64_t n_items = static_cast<int64_t>(s.batch) * s.num_kv_heads;
     p.gp = pad_group(s.num_q_heads / s.num_kv_heads);
+    // the vector-ALU kernel's 16-head state only fits one wave per SIMD
+    if (p.kernel == SR_KERNEL_VALU && p.gp >= 16) p.waves = 4;
     const int64_t cap = (s.seq_len + kMinSplitLen - 1) / kMinSplitLen;
     if (l.num_splits > 0) {
         const int64_t grid = n_items * l.num_splits;
@@ -124,14 +126,35 @@ struct FusedRoute {
     int32_t* n_active;
 };
 
+struct FusedRope {
+    const float* k_new;
+    const float* v_new;
+    const float* inv_freq;
+    float* q_out;
+};
+
+bool overlaps(const void* a, const void* b, size_t bytes) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + bytes && y < x + bytes;
+}
+
 sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float* q,
                      const void* k, const void* v, const float* v0, const int32_t* work_list,
                      const int32_t* n_active, float sm_scale, void* ws, size_t ws_bytes,
                      float* out, void* stream, bool routed, const FusedRoute* fused = nullptr,
-                     float* alpha0 = nullptr) {
+                     float* alpha0 = nullptr, const FusedRope* rope = nullptr) {
     sr_status st = check_shape(shape);
     if (st != SR_OK) return st;
     const sr_shape& s = *shape;
+    if (rope) {  // rotary inside the fused-routing launch only
+        if (static_cast<int64_t>(s.batch) * s.num_q_heads > kMaxFusedHeads)
+            return SR_ERR_UNSUPPORTED;
+        if (s.seq_len < 2 || !rope->k_new || !rope->v_new || !rope->inv_freq)
+            return SR_ERR_INVALID_ARG;
+        const size_t q_bytes =
+            static_cast<size_t>(s.batch) * s.num_q_heads * s.head_dim * sizeof(float);
+        if (rope->q_out && overlaps(rope->q_out, q, q_bytes)) return SR_ERR_INVALID_ARG;
+    }
     if ((st = check_caches(s, k, v)) != SR_OK) return st;
     if (!q || !out || !ws || !aligned16(q) || !aligned16(out) || !aligned16(ws))
         return SR_ERR_INVALID_ARG;
@@ -171,6 +194,14 @@ sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float
     a.split_cap = p.split_cap;
     a.routed = routed ? 1 : 0;
     a.alpha0_out = alpha0;
+    a.kv_f32 = s.kv_dtype == SR_KV_F32 ? 1 : 0;
+    if (rope) {
+        a.rope = 1;
+        a.k_new = rope->k_new;
+        a.v_new = rope->v_new;
+        a.inv_freq = rope->inv_freq;
+        a.q_out = rope->q_out;
+    }
     if (fused) {
         a.fused = 1;
         a.k0 = fused->k0;
@@ -275,6 +306,19 @@ sr_status sr_route_decode(const sr_shape* shape, const sr_launch* launch, const 
     const FusedRoute f{k0, tau, scores, mask, work_list, n_active};
     return run_decode(shape, launch, q, k_cache, v_cache, v0, nullptr, nullptr, sm_scale, ws,
                       ws_bytes, out, stream, true, &f);
+}
+
+sr_status sr_rope_route_decode(const sr_shape* shape, const sr_launch* launch,
+                               const float* q_new, const float* k_new, const float* v_new,
+                               const float* inv_freq, float* q_out, void* k_cache, void* v_cache,
+                               const float* k0, const float* v0, float tau, float sm_scale,
+                               float* scores, uint8_t* mask, int32_t* work_list,
+                               int32_t* n_active, void* ws, size_t ws_bytes, float* out,
+                               void* stream) {
+    const FusedRoute f{k0, tau, scores, mask, work_list, n_active};
+    const FusedRope r{k_new, v_new, inv_freq, q_out};
+    return run_decode(shape, launch, q_new, k_cache, v_cache, v0, nullptr, nullptr, sm_scale, ws,
+                      ws_bytes, out, stream, true, &f, nullptr, &r);
 }
 
 sr_status sr_dense_decode(const sr_shape* shape, const sr_launch* launch, const float* q,

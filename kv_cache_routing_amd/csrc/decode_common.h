@@ -28,6 +28,13 @@ __device__ inline uint4 load_stream(const void* p) {
     return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+// The same for 8 bytes.
+__device__ inline uint2 load_stream8(const void* p) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 t = __builtin_nontemporal_load(static_cast<const u32x2*>(p));
+    return make_uint2(t.x, t.y);
+}
+
 // exp2(m - M) as a merge weight; a state that saw no position (m = -inf)
 // weighs nothing, even when M is -inf as well.
 __device__ inline float merge_weight(float m, float M) {
@@ -158,6 +165,7 @@ struct WorkRange {
     int32_t w, i_begin, i_end;
     int32_t lane;  // lanes mode: the one lane this workgroup streams
     int32_t item[2];
+    const float* q;  // the queries the passes read (a.q, or rotated in LDS)
 };
 
 // Routing decision and work division of one workgroup, then its sink duty.

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
         // A operands: query row = col, elements d = 32*kb + 8*grp + e
         bf16x8 qhi[KB], qlo[KB];
         {
-            const float* qr = a.q + (static_cast<int64_t>(u.b) * a.num_q_heads +
+            const float* qr = wr.q + (static_cast<int64_t>(u.b) * a.num_q_heads +
                                      static_cast<int64_t>(u.g) * G + col) * D;
             const bool real = col < G;
 #pragma unroll
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma_f32(DecodeArgs a) {
 
         float qv[KD];  // B operand of QK: head col, element 16*(kb/4) + 4*grp + kb%4
         {
-            const float* qr = a.q + (static_cast<int64_t>(u.b) * a.num_q_heads +
+            const float* qr = wr.q + (static_cast<int64_t>(u.b) * a.num_q_heads +
                                      static_cast<int64_t>(u.g) * G + col) * D + 4 * grp;
             const bool real = col < G;
 #pragma unroll
@@ -535,10 +535,11 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma_f32(DecodeArgs a) {
 
 template <bool F32, int D, int GP, int NW>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
+    const size_t lds = a.rope ? rope_lds_bytes(a.batch * a.num_q_heads, D) : 0;
     if constexpr (F32)
-        hipLaunchKernelGGL((k_decode_mfma_f32<D, GP, NW>), dim3(a.grid), dim3(NW * 64), 0, st, a);
+        hipLaunchKernelGGL((k_decode_mfma_f32<D, GP, NW>), dim3(a.grid), dim3(NW * 64), lds, st, a);
     else
-        hipLaunchKernelGGL((k_decode_mfma<D, GP, NW>), dim3(a.grid), dim3(NW * 64), 0, st, a);
+        hipLaunchKernelGGL((k_decode_mfma<D, GP, NW>), dim3(a.grid), dim3(NW * 64), lds, st, a);
     return hipGetLastError();
 }
 

@@ -2,9 +2,10 @@
 // Handles fp32 and bf16 caches, d in {64, 128}, any group size up to 16.
 //
 // Layout: a wave reads a tile of whole cache rows.  Each lane owns E = 8
-// consecutive elements of one row (16 B of bf16, 32 B of fp32; E = 4, 16 B,
-// for fp32 groups of 16 heads, whose query and accumulator rows would not fit
-// the register file at 8), so a row is spread over d/E lanes (a "lane group")
+// consecutive elements of one row (16 B of bf16, 32 B of fp32; E = 4, 8 B of
+// bf16 or 16 B of fp32, for groups of 16 heads, whose query and accumulator
+// rows would not fit the register file at 8), so a row is spread over d/E
+// lanes (a "lane group")
 // and one wave-wide load instruction covers 64/(d/E) consecutive rows: fully
 // coalesced.  QK is an E-term dot product per lane followed by a DPP
 // all-reduce inside the lane group; PV accumulates p * V for the lane's E
@@ -20,14 +21,17 @@
 namespace sr {
 namespace {
 
-// The E elements of one row slice as fp32, from the W = sizeof(KV)*E/16
-// 16-byte loads that read them.
+// One lane's slice of a cache row: E consecutive elements, read with W
+// non-temporal loads of type T and widened to fp32.
 template <typename KV, int E>
 struct RowSlice;
 
 template <>
 struct RowSlice<uint16_t, 8> {  // 8 bf16 in one 16-byte load
-    __device__ static inline void unpack(const uint4 (&r)[1], float (&x)[8]) {
+    using T = uint4;
+    static constexpr int W = 1;
+    __device__ static inline void load(T (&r)[W], const uint16_t* p) { r[0] = load_stream(p); }
+    __device__ static inline void unpack(const T (&r)[W], float (&x)[8]) {
         const uint32_t w[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -38,8 +42,27 @@ struct RowSlice<uint16_t, 8> {  // 8 bf16 in one 16-byte load
 };
 
 template <>
+struct RowSlice<uint16_t, 4> {  // 4 bf16 in one 8-byte load
+    using T = uint2;
+    static constexpr int W = 1;
+    __device__ static inline void load(T (&r)[W], const uint16_t* p) { r[0] = load_stream8(p); }
+    __device__ static inline void unpack(const T (&r)[W], float (&x)[4]) {
+        x[0] = __uint_as_float(r[0].x << 16);
+        x[1] = __uint_as_float(r[0].x & 0xffff0000u);
+        x[2] = __uint_as_float(r[0].y << 16);
+        x[3] = __uint_as_float(r[0].y & 0xffff0000u);
+    }
+};
+
+template <>
 struct RowSlice<float, 8> {  // 8 fp32 in two 16-byte loads
-    __device__ static inline void unpack(const uint4 (&r)[2], float (&x)[8]) {
+    using T = uint4;
+    static constexpr int W = 2;
+    __device__ static inline void load(T (&r)[W], const float* p) {
+        r[0] = load_stream(p);
+        r[1] = load_stream(p + 4);
+    }
+    __device__ static inline void unpack(const T (&r)[W], float (&x)[8]) {
         const uint32_t w[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = __uint_as_float(w[i]);
@@ -48,7 +71,10 @@ struct RowSlice<float, 8> {  // 8 fp32 in two 16-byte loads
 
 template <>
 struct RowSlice<float, 4> {  // 4 fp32 in one 16-byte load
-    __device__ static inline void unpack(const uint4 (&r)[1], float (&x)[4]) {
+    using T = uint4;
+    static constexpr int W = 1;
+    __device__ static inline void load(T (&r)[W], const float* p) { r[0] = load_stream(p); }
+    __device__ static inline void unpack(const T (&r)[W], float (&x)[4]) {
         x[0] = __uint_as_float(r[0].x);
         x[1] = __uint_as_float(r[0].y);
         x[2] = __uint_as_float(r[0].z);
@@ -82,7 +108,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
 
         float qs[GP][E];
         {
-            const float* qb = a.q + (static_cast<int64_t>(u.b) * a.num_q_heads +
+            const float* qb = wr.q + (static_cast<int64_t>(u.b) * a.num_q_heads +
                                      static_cast<int64_t>(u.g) * G) * D + chunk * E;
 #pragma unroll
             for (int h = 0; h < GP; ++h) {
@@ -115,11 +141,11 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
             for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
         }
 
-        // One tile of TILE rows: the raw 8-element slices this lane loads.
-        constexpr int W = sizeof(KV) * E / 16;  // 16-byte loads per 8-element slice
+        // One tile of TILE rows: the raw E-element slices this lane loads.
+        using Slice = RowSlice<KV, E>;
         struct Raw {
-            uint4 k[U][W];
-            uint4 v[U][W];
+            typename Slice::T k[U][Slice::W];
+            typename Slice::T v[U][Slice::W];
         };
         const int64_t last = u.t1 - 1;
         // Rows past T are clamped to the last row: every lane then reads the same
@@ -129,13 +155,8 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
             for (int v = 0; v < U; ++v) {
                 int64_t t = tile + v * TPI + row;
                 t = t < u.t1 ? t : last;
-                const uint4* kp = reinterpret_cast<const uint4*>(kb + t * st);
-                const uint4* vp = reinterpret_cast<const uint4*>(vb + t * st);
-#pragma unroll
-                for (int w = 0; w < W; ++w) {
-                    r.k[v][w] = load_stream(kp + w);
-                    r.v[v][w] = load_stream(vp + w);
-                }
+                Slice::load(r.k[v], kb + t * st);
+                Slice::load(r.v[v], vb + t * st);
             }
         };
         auto compute = [&](const Raw& r, int64_t tile) {
@@ -143,7 +164,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
 #pragma unroll
             for (int v = 0; v < U; ++v) {
                 float kf[E];
-                RowSlice<KV, E>::unpack(r.k[v], kf);
+                Slice::unpack(r.k[v], kf);
                 const bool valid = tile + v * TPI + row < u.t1;
 #pragma unroll
                 for (int h = 0; h < GP; ++h) {
@@ -181,7 +202,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
 #pragma unroll
             for (int v = 0; v < U; ++v) {
                 float vf[E];
-                RowSlice<KV, E>::unpack(r.v[v], vf);
+                Slice::unpack(r.v[v], vf);
 #pragma unroll
                 for (int h = 0; h < GP; ++h) {
                     const float p = z[v][h] == kNegInf ? 0.f : fast_exp2(z[v][h] - m[h]);
@@ -252,9 +273,11 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
 
 template <typename KV, int D, int GP, int NW>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
-    constexpr int U = valu_rows_per_lane(GP, static_cast<int>(sizeof(KV)));
+    constexpr int U = valu_rows_per_lane(GP, static_cast<int>(sizeof(KV)), NW);
     constexpr int E = valu_elems_per_lane(GP, static_cast<int>(sizeof(KV)));
-    hipLaunchKernelGGL((k_decode_valu<KV, D, GP, NW, U, E>), dim3(a.grid), dim3(NW * 64), 0, st, a);
+    const size_t lds = a.rope ? rope_lds_bytes(a.batch * a.num_q_heads, D) : 0;
+    hipLaunchKernelGGL((k_decode_valu<KV, D, GP, NW, U, E>), dim3(a.grid), dim3(NW * 64), lds, st,
+                       a);
     return hipGetLastError();
 }
 
@@ -265,7 +288,9 @@ hipError_t launch_g(const DecodeArgs& a, int gp, hipStream_t st) {
         case 2: return launch_t<KV, D, 2, NW>(a, st);
         case 4: return launch_t<KV, D, 4, NW>(a, st);
         case 8: return launch_t<KV, D, 8, NW>(a, st);
-        case 16: return launch_t<KV, D, 16, NW>(a, st);
+        case 16:  // four-wave workgroups only (make_plan)
+            if constexpr (NW == 4) return launch_t<KV, D, 16, NW>(a, st);
+            return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }

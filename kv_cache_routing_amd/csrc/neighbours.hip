@@ -7,26 +7,10 @@
 // appends the new key/value; position 0 itself is never rotated (angle 0).
 // Rotary form (not printed on the pages; Hugging Face Llama convention):
 // element i is paired with element i + d/2 and both turn by pos * inv_freq[i].
-#include "sr_internal.h"
+#include "rope.h"
 
 namespace sr {
 namespace {
-
-// fp64 -> bf16 with one rounding to nearest even: truncate to fp32 and keep a
-// sticky bit (round to odd, 24 >= 8 + 2 bits), then round the fp32 bits.
-__device__ inline uint16_t bf16_from_double(double x) {
-    const float f = __double2float_rz(x);
-    uint32_t u = __float_as_uint(f);
-    if (static_cast<double>(f) != x) u |= 1u;
-    return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
-
-__device__ inline void store_elem(void* base, int64_t idx, double x, int32_t dtype) {
-    if (dtype == SR_KV_F32)
-        static_cast<float*>(base)[idx] = static_cast<float>(x);
-    else
-        static_cast<uint16_t*>(base)[idx] = bf16_from_double(x);
-}
 
 // One thread per pair (i, i + d/2) of every query row, key row and value row.
 __global__ void k_rope_append(const float* __restrict__ q_new, const float* __restrict__ k_new,
@@ -55,10 +39,9 @@ __global__ void k_rope_append(const float* __restrict__ q_new, const float* __re
     const double x0 = src[row * d + i], x1 = src[row * d + i + half];
     double r0 = x0, r1 = x1;
     if (kind != 2) {
-        double s, c;
-        sincos(static_cast<double>(pos) * static_cast<double>(inv_freq[i]), &s, &c);
-        r0 = x0 * c - x1 * s;
-        r1 = x1 * c + x0 * s;
+        double c, s;
+        rope_angle(pos, inv_freq, i, c, s);
+        rope_turn(x0, x1, c, s, r0, r1);
     }
     if (kind == 0) {
         q_out[row * d + i] = static_cast<float>(r0);

@@ -13,6 +13,7 @@
 #include <type_traits>
 
 #include "decode_common.h"
+#include "rope.h"
 
 namespace sr {
 
@@ -300,6 +301,61 @@ __device__ inline SplitPlan uniform_plan(SplitPlan p) {
     return p;
 }
 
+// Fused rotary, first step: every workgroup turns all B*Hq new queries to
+// position T - 1 (the new token's) in LDS; workgroup 0 also writes them out.
+// The angles' cosines and sines stay in LDS for the key rows.
+template <int D, int NT>
+__device__ inline const float* rope_queries(const DecodeArgs& a, double*& s_c, double*& s_s) {
+    extern __shared__ float4 s_rope[];  // rope_lds_bytes(B * Hq, D)
+    constexpr int HALF = D / 2;
+    s_c = reinterpret_cast<double*>(s_rope);
+    s_s = s_c + HALF;
+    float* s_q = reinterpret_cast<float*>(s_s + HALF);
+    const int64_t pos = a.seq_len - 1;
+    for (int i = threadIdx.x; i < HALF; i += NT) rope_angle(pos, a.inv_freq, i, s_c[i], s_s[i]);
+    __syncthreads();
+    const int32_t n = a.batch * a.num_q_heads * HALF;
+    const bool out = blockIdx.x == 0 && a.q_out;
+    for (int32_t e = threadIdx.x; e < n; e += NT) {
+        const int32_t row = e / HALF, i = e - row * HALF;
+        const float* x = a.q + static_cast<int64_t>(row) * D;
+        double r0, r1;
+        rope_turn(x[i], x[i + HALF], s_c[i], s_s[i], r0, r1);
+        const float f0 = static_cast<float>(r0), f1 = static_cast<float>(r1);
+        s_q[row * D + i] = f0;
+        s_q[row * D + i + HALF] = f1;
+        if (out) {
+            a.q_out[static_cast<int64_t>(row) * D + i] = f0;
+            a.q_out[static_cast<int64_t>(row) * D + i + HALF] = f1;
+        }
+    }
+    __syncthreads();
+    return s_q;
+}
+
+// Fused rotary, second step: the new key (turned) and value of item j go to
+// row T - 1 of the caches, rounded as by the standalone rotary kernel.
+template <int D, int NT>
+__device__ inline void append_row(const DecodeArgs& a, int32_t j, const double* s_c,
+                                  const double* s_s) {
+    constexpr int HALF = D / 2;
+    const int32_t b = j / a.num_kv_heads, g = j - b * a.num_kv_heads;
+    const int64_t at = b * a.stride_b + g * a.stride_h + (a.seq_len - 1) * a.stride_t;
+    const int32_t dtype = a.kv_f32 ? SR_KV_F32 : SR_KV_BF16;
+    void* kc = const_cast<void*>(a.k);
+    void* vc = const_cast<void*>(a.v);
+    const float* kn = a.k_new + static_cast<int64_t>(j) * D;
+    const float* vn = a.v_new + static_cast<int64_t>(j) * D;
+    for (int i = threadIdx.x; i < HALF; i += NT) {
+        double r0, r1;
+        rope_turn(kn[i], kn[i + HALF], s_c[i], s_s[i], r0, r1);
+        store_elem(kc, at + i, r0, dtype);
+        store_elem(kc, at + i + HALF, r1, dtype);
+        store_elem(vc, at + i, vn[i], dtype);
+        store_elem(vc, at + i + HALF, vn[i + HALF], dtype);
+    }
+}
+
 template <int D, int NT, int CHUNK>
 __device__ inline bool map_work(const DecodeArgs& a, WorkRange& r) {
     const int32_t n_items = a.batch * a.num_kv_heads;
@@ -307,6 +363,7 @@ __device__ inline bool map_work(const DecodeArgs& a, WorkRange& r) {
     const int32_t G = a.group;
     int32_t n_act, sink_item = -1;
     r.item[0] = r.item[1] = -1;
+    r.q = a.q;
     // The plan, this workgroup's range of positions and the list positions
     // of the items it touches (one in lanes mode, at most two when balanced).
     auto plan_range = [&](int32_t n) {
@@ -338,9 +395,11 @@ __device__ inline bool map_work(const DecodeArgs& a, WorkRange& r) {
         static_assert(kMaxFusedHeads <= 4 * (NT / 16), "one round of at most 4 heads per group");
         __shared__ uint8_t s_pass[kMaxFusedHeads];
         const bool w0 = wg == 0;
+        double *s_c = nullptr, *s_s = nullptr;
+        if (a.rope) r.q = rope_queries<D, NT>(a, s_c, s_s);
         const uint64_t all = n_items >= 64 ? ~0ull : ((1ull << n_items) - 1);
         const uint64_t sinks =
-            fused_sink_mask<NT, 4>(a.q, a.k0, a.tau, n_items, G, D, s_pass,
+            fused_sink_mask<NT, 4>(r.q, a.k0, a.tau, n_items, G, D, s_pass,
                                    w0 ? a.scores_out : nullptr) & all;
         const uint64_t act = all & ~sinks;
         n_act = uniform(__popcll(act));
@@ -356,6 +415,24 @@ __device__ inline bool map_work(const DecodeArgs& a, WorkRange& r) {
             if (a.mask_out) a.mask_out[j] = is_sink ? 1 : 0;
             if (a.list_out) a.list_out[pos] = j;
             if (j == 0 && a.n_active_out) a.n_active_out[0] = n_act;
+        }
+        if (a.rope) {
+            // Row T - 1 of every item is written by exactly one workgroup:
+            // for a sink, the one that copies its v0 rows; for an active
+            // item, the one whose part holds the chunk with T - 1 (the only
+            // reader of that row in this launch).  It writes before it
+            // streams, and its own loads then see the row.
+            const SplitPlan& p = r.plan;
+            const int32_t c = static_cast<int32_t>((a.seq_len - 1) / CHUNK);
+            const int32_t l = c % p.S, k = c / p.S;  // lane and step of that chunk
+            if (sink_item >= 0) append_row<D, NT>(a, sink_item, s_c, s_s);
+            for (int32_t i = r.i_begin; i < r.i_end; ++i) {
+                const int64_t x = static_cast<int64_t>(i) * p.C + lane_start(p, l) + k;
+                const bool owner = p.balanced ? (r.p0 <= x && x < r.p1) : l == r.lane;
+                if (owner) append_row<D, NT>(a, i == r.i_begin ? r.item[0] : r.item[1], s_c, s_s);
+            }
+            __builtin_amdgcn_s_waitcnt(0);  // the rows are in this XCD's L2
+            __syncthreads();
         }
     } else if (a.routed && n_items <= NT) {
         // one round trip: the whole list and n_active load together

@@ -40,7 +40,24 @@ struct DecodeArgs {
     int32_t* list_out;         // [B*Hkv]   (fused, optional)
     int32_t* n_active_out;     // [1]       (fused, optional)
     float* alpha0_out;         // [B][Hq] weight of position 0 per head (optional)
+    // Fused rotary + append (sr_rope_route_decode, fused routing only): q is
+    // the unrotated new query; every workgroup rotates all queries to
+    // position T - 1 into dynamic LDS (rope_lds_bytes), and the key and value
+    // rows at T - 1 are written by the one workgroup that reads them.
+    int32_t rope;
+    int32_t kv_f32;            // cache elements are fp32 (else bf16)
+    const float* k_new;        // [B][Hkv][d] fp32, unrotated (rope only)
+    const float* v_new;        // [B][Hkv][d] fp32 (rope only)
+    const float* inv_freq;     // [d/2] (rope only)
+    float* q_out;              // [B][Hq][d] rotated query (rope, optional)
 };
+
+// Dynamic LDS of a fused rotary launch: cos and sin of the d/2 angles (fp64),
+// then the rotated queries [B*Hq][d] fp32 (16-byte aligned).
+__host__ __device__ constexpr size_t rope_lds_bytes(int32_t q_rows, int32_t d) {
+    return static_cast<size_t>(d / 2) * 2 * sizeof(double) +
+           static_cast<size_t>(q_rows) * d * sizeof(float);
+}
 
 // sr_route_decode runs routing inside the decode launch (every workgroup
 // scores every head) only for layers of up to this many query heads; larger
@@ -192,18 +209,22 @@ __host__ __device__ inline void item_parts(const SplitPlan& p, int32_t i, int32_
 
 // Elements of a cache row per lane (E), rows of cache per lane and tile (U)
 // of the vector-ALU kernel, and the positions per chunk of either kernel.
-// fp32 rows take two 16-byte loads per 8 elements, so they get half the rows
-// (the two tile buffers then fit the register file).  fp32 groups of 16 heads
-// take 4 elements per lane: the lane's query and accumulator rows (2 x GP x E
-// floats) would not fit the register file at 8.
+// Sized so that nothing spills: a lane holds its query and accumulator rows
+// (2 x GP x E floats) and two tiles of U slices of K and V.  fp32 rows take
+// two 16-byte loads per 8 elements, so they get half the rows.  Groups of 16
+// heads take 4 elements per lane (8-byte bf16 slices) and always run in
+// four-wave workgroups (make_plan): with two waves per SIMD, 256 registers
+// each, their state does not fit at any tile size.  Eight-wave workgroups of
+// 4-head bf16 groups take half the rows.
 __host__ __device__ constexpr int valu_elems_per_lane(int gp, int kv_bytes) {
-    return gp >= 16 && kv_bytes == 4 ? 4 : 8;
+    return gp >= 16 ? 4 : 8;
 }
 
-__host__ __device__ constexpr int valu_rows_per_lane(int gp, int kv_bytes) {
-    return valu_elems_per_lane(gp, kv_bytes) == 4
-               ? 4
-               : (gp >= 16 ? 1 : (gp >= 8 ? 2 : (kv_bytes == 4 ? 4 : 8)));
+__host__ __device__ constexpr int valu_rows_per_lane(int gp, int kv_bytes, int waves) {
+    const int u = valu_elems_per_lane(gp, kv_bytes) == 4
+                      ? 4
+                      : (gp >= 8 ? 2 : (kv_bytes == 4 ? 4 : 8));
+    return waves == 8 && gp == 4 && kv_bytes == 2 ? u / 2 : u;
 }
 
 // 16-position tiles per wave step of the matrix-core kernels: bf16 rows of
@@ -217,7 +238,7 @@ inline int32_t chunk_positions(int32_t kernel, int32_t head_dim, int32_t gp, int
                                int32_t kv_bytes) {
     if (kernel == SR_KERNEL_MFMA) return waves * 16 * mfma_tiles_per_step(head_dim, kv_bytes);
     return waves * (64 / (head_dim / valu_elems_per_lane(gp, kv_bytes))) *
-           valu_rows_per_lane(gp, kv_bytes);
+           valu_rows_per_lane(gp, kv_bytes, waves);
 }
 
 inline int32_t pad_group(int32_t g) {

@@ -182,6 +182,20 @@ def test_fused_route_decode_validation():
     assert fused(shape(B=4097, Hq=8, Hkv=8)) == N.SR_ERR_UNSUPPORTED
 
 
+def test_rope_route_decode_validation():
+    def call(s, kn=FAKE, vn=FAKE, f=FAKE, q_out=0, q=FAKE):
+        return N.lib.sr_rope_route_decode(ctypes.byref(s), None, p(q), p(kn), p(vn), p(f),
+                                          p(q_out), p(), p(), p(), p(), ctypes.c_float(0.5), 0.0,
+                                          p(0), p(0), p(0), p(0), p(), 1 << 30, p(), None)
+    s = shape()
+    assert call(s, kn=0) == N.SR_ERR_INVALID_ARG
+    assert call(s, vn=0) == N.SR_ERR_INVALID_ARG
+    assert call(s, f=0) == N.SR_ERR_INVALID_ARG
+    assert call(shape(T=1)) == N.SR_ERR_INVALID_ARG            # position 0 is the sink key
+    assert call(s, q_out=FAKE + 4096) == N.SR_ERR_INVALID_ARG  # overlaps q_new
+    assert call(shape(B=3, Hq=32, Hkv=8)) == N.SR_ERR_UNSUPPORTED  # 96 query heads
+
+
 # --- work division (host-side model of what the decode kernel streams) ----------
 def plan(s, launch, n_active):
     """{wg: [sr_part, ...]} over the whole grid."""
@@ -326,3 +340,15 @@ def test_binding_plan_parts_matches_the_abi():
     assert got[0]["item"] == buf[0].item and got[0]["end"] == buf[0].end
     with pytest.raises(sr.SinkRouteError):
         sr.plan_parts(s, lau, 65, 0)
+
+
+def test_build_rejects_kernels_with_scratch():
+    from kv_cache_routing_amd.build import scratch_kernels
+    report = "\n".join([
+        "a.hip:1:1: remark: Function Name: k_good [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark: Function Name: k_spills [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark:     ScratchSize [bytes/lane]: 96 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert scratch_kernels(report) == ["k_spills (96 bytes/lane)"]
+    assert scratch_kernels("") == []

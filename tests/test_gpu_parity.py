@@ -741,6 +741,90 @@ def test_decode_steps_with_append_match_oracle():
         assert_outputs(out.cpu().numpy(), ref, f"step {step} T={T}")
 
 
+# (name, B, Hq, Hkv, d, dtype, T, sink groups per sequence, tau, kernel, waves, splits)
+ROPE_FUSED = [
+    ("8b-lanes", 1, 32, 8, 128, "bf16", 4097, 4, 0.5, "auto", 0, 0),
+    ("8b-balanced", 1, 32, 8, 128, "bf16", 100000, 5, 0.5, "auto", 0, 0),
+    ("8b-last-row-valu", 1, 32, 8, 128, "bf16", 4096, 4, 0.5, "valu", 0, 0),
+    ("d64-b2", 2, 8, 4, 64, "bf16", 3001, 1, 0.5, "auto", 0, 0),
+    ("f32-g8", 1, 16, 2, 128, "f32", 5000, 1, 0.5, "auto", 0, 0),
+    ("g16-64-heads", 1, 64, 4, 128, "bf16", 2049, 2, 0.5, "auto", 0, 0),
+    ("mha", 1, 8, 8, 128, "bf16", 1500, 3, 0.5, "auto", 0, 0),
+    ("dense-tau-above-one", 1, 32, 8, 128, "bf16", 4097, 0, 2.0, "auto", 0, 0),
+    ("all-sinks", 1, 32, 8, 128, "bf16", 4097, 8, -2.0, "auto", 0, 0),
+    ("fixed-splits", 1, 32, 8, 128, "bf16", 20000, 4, 0.5, "mfma", 0, 7),
+    ("waves8-f32-d64", 1, 32, 8, 64, "f32", 3000, 2, 0.5, "auto", 8, 0),
+    ("valu-f32-g16", 1, 32, 2, 64, "f32", 2500, 1, 0.5, "valu", 0, 0),
+    ("two-positions", 1, 32, 8, 128, "bf16", 2, 4, 0.5, "auto", 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", ROPE_FUSED, ids=[c[0] for c in ROPE_FUSED])
+def test_rope_route_decode_matches_append_then_route_decode(case):
+    # One launch (rotate + append + route + decode) against sr_rope_append
+    # followed by sr_route_decode on a copy of the caches: every output, the
+    # rotated query and the whole cache storage bitwise equal; the output
+    # also against the oracle on the appended cache.
+    name, B, Hq, Hkv, d, dtype, T, n_sink, tau, kernel, waves, splits = case
+    G = Hq // Hkv
+    pos, cap = T - 1, T + 5
+    gen = torch.Generator().manual_seed(170 + T + Hq)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kc = torch.randn((B, Hkv, cap, d), generator=gen).to(tdt)
+    vc = torch.randn((B, Hkv, cap, d), generator=gen).to(tdt)
+    kc[:, :, pos:] = 7.0  # rows from T - 1 on: only the append may change them
+    vc[:, :, pos:] = 7.0
+    k0 = kc[:, :, 0].float()
+    f = rope_inv_freq(d)
+    kn, vn = (torch.randn((B, Hkv, d), generator=gen) for _ in range(2))
+    # sinks: the rotated query of every head in the first n_sink groups lies
+    # near k0 (planted by turning the target back by the new position)
+    target = torch.randn((B, Hq, d), generator=gen, dtype=torch.float64)
+    for b in range(B):
+        for g in range(n_sink):
+            u = k0[b, g].double() / k0[b, g].double().norm()
+            for h in range(g * G, (g + 1) * G):
+                target[b, h] = 0.9 * u * target[b, h].norm() + 0.05 * target[b, h]
+    qn = torch.from_numpy(oracle.rope(target.numpy(), -pos, f.numpy())).float()
+    lau = launch(kernel, splits=splits, waves=waves)
+    kA, vA = kc.cuda(), vc.cuda()
+    kB, vB = kc.cuda(), vc.cuda()
+    k0d, v0d = sr.record_sink(kA[:, :, :T], vA[:, :, :T])
+    qn_d, kn_d, vn_d, f_d = qn.cuda(), kn.cuda(), vn.cuda(), f.cuda()
+
+    q_rot = sr.rope_append(qn_d, kn_d, vn_d, kA, vA, pos, f_d)
+    out_a, r_a = sr.route_decode(q_rot, kA[:, :, :T], vA[:, :, :T], k0d, v0d, tau, launch=lau)
+    ws = sr.Workspace(sr.make_shape(qn_d, kB[:, :, :T], vB[:, :, :T]), lau, qn_d.device)
+    for rep in range(2):  # the second call reuses the workspace and rewrites the same row
+        out_b, r_b, q_b = sr.rope_route_decode(qn_d, kn_d, vn_d, kB[:, :, :T], vB[:, :, :T],
+                                               k0d, v0d, f_d, tau, launch=lau, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(q_b, q_rot), f"{name}: rotated query"
+        assert torch.equal(out_b, out_a), f"{name}: output (call {rep})"
+        for fld in ("scores", "mask", "work_list", "n_active"):
+            assert torch.equal(getattr(r_b, fld), getattr(r_a, fld)), f"{name}: {fld}"
+        assert torch.equal(kB, kA) and torch.equal(vB, vA), f"{name}: caches"
+    n_active = int(r_b.n_active.item())
+    expect = B * Hkv if tau > 1 else (0 if tau < -1 else B * (Hkv - n_sink))
+    assert n_active == expect, f"{name}: planted routing gave {n_active} active"
+    shape = sr.make_shape(qn_d, kB[:, :, :T], vB[:, :, :T])
+    grid, lanes = sr.grid_size(shape, lau), sr.splits_for(shape, lau, n_active)
+    balanced = splits == 0 and n_active * lanes < grid and lanes < -(-T // 512)
+    log(f"{name}: n_active={n_active} grid={grid} lanes={lanes} balanced={balanced}")
+    if name == "8b-balanced":
+        assert balanced  # the appended row's owner found from the workgroup's range
+    if name == "8b-lanes":
+        assert not balanced and n_active > 0  # found from the workgroup's lane
+
+    k_dev = as_numpy(kB[:, :, :T].cpu()).astype(np.float64)
+    v_dev = as_numpy(vB[:, :, :T].cpu()).astype(np.float64)
+    q_dev = q_b.cpu().numpy().astype(np.float64)
+    _, mask, _, _ = oracle.route(q_dev, k_dev[:, :, 0], tau)
+    assert np.array_equal(r_b.mask.cpu().numpy(), mask)
+    ref = oracle.routed_decode(q_dev, k_dev, v_dev, v_dev[:, :, 0], mask)
+    assert_outputs(out_b.cpu().numpy(), ref, f"{name} T={T}")
+
+
 def test_graph_replay_matches_eager():
     # The decode calls allocate nothing and never wait for the host, so they
     # can be captured; replay several times with eager work in between and
