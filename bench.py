@@ -340,7 +340,8 @@ def decode_layers_report(sr, torch, args):
     """Per-token attention over a stack of layers: each layer rotates the new
     token's q and k and appends k, v (sr_rope_append), then runs routed
     attention (sr_route_decode) inside the gated layer range and dense
-    attention (sr_dense_decode) outside it.  Caches come from the seeded GPU
+    attention (sr_dense_decode) outside it; timed again with each layer as
+    one sr_rope_route_decode launch.  Caches come from the seeded GPU
     generator (timing only; every kernel's parity is tested elsewhere).  Sink
     groups' queries are built in the rotated frame (0.9 k0/|k0| + 0.05 noise)
     and turned back by -pos on the host, so the routing sees planted sinks."""
@@ -399,12 +400,19 @@ def decode_layers_report(sr, torch, args):
 
     q_rots = [[torch.empty_like(out) for _ in range(L)] for _ in range(N)]
 
-    def token(t, routed=True, attend=True, append=True):
+    def token(t, routed=True, attend=True, append=True, fused=False):
         pos = T0 + t
         for layer in range(L):
             k, v = caches[layer]
             qp, kn, vn = plans[t][layer]
             q_rot = q_rots[t][layer]
+            if fused:  # one launch per layer; tau > 1 gives the dense result
+                k0, v0 = k0v0[layer]
+                tau = 0.5 if routed and start <= layer <= end else 2.0
+                sr.rope_route_decode(qp, kn, vn, k[:, :, :pos + 1], v[:, :, :pos + 1], k0, v0,
+                                     freq, tau, launch=lau, ws=ws, out=out,
+                                     routing=routing[layer], q_out=q_rot)
+                continue
             if append:
                 sr.rope_append(qp, kn, vn, k, v, pos, freq, q_out=q_rot)
             if not attend:
@@ -455,6 +463,8 @@ def decode_layers_report(sr, torch, args):
     append_only = run(graphs(attend=False))
     attend_routed = run(graphs(routed=True, append=False))
     attend_dense = run(graphs(routed=False, append=False))
+    routed_one = run(graphs(routed=True, fused=True))
+    dense_one = run(graphs(routed=False, fused=True))
     gated = sum(1 for layer in range(L) if start <= layer <= end)
     rep = {"decode_layers": {
         "layers": L, "context": T0, "tokens": N, "routed_layers": [start, end],
@@ -466,6 +476,10 @@ def decode_layers_report(sr, torch, args):
         "composition_us_per_token": {"rope_append": round(append_only, 1),
                                      "attention_routed": round(attend_routed, 1),
                                      "attention_dense": round(attend_dense, 1)},
+        "one_launch_per_layer": {  # sr_rope_route_decode (dense layers at tau > 1)
+            "us_per_token_routed": round(routed_one, 1),
+            "us_per_token_dense": round(dense_one, 1),
+            "speedup": round(dense_one / routed_one, 4)},
         "kv_gib_per_token_dense": round(L * 2 * B * Hkv * T0 * d * 2 / 2 ** 30, 2)}}
     print(json.dumps(rep), flush=True)
     return 0

@@ -45,18 +45,21 @@ def _need_cuda(*ts):
 
 def _expect(t: torch.Tensor, name: str, shape: tuple, dtype: torch.dtype):
     """The kernels index these arrays densely from the cache shape: anything
-    else would read or write outside them."""
-    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+    else would read or write outside them.  (Kept cheap: it runs on every
+    call, and launch-bound steps pay for it.)"""
+    if t.shape != shape or t.dtype != dtype or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}, "
                          f"got {t.dtype} {tuple(t.shape)}"
                          f"{'' if t.is_contiguous() else ' (not contiguous)'}")
 
 
 def _expect_q(q: torch.Tensor, k: torch.Tensor):
-    if q.dim() != 3 or k.dim() != 4 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[3]:
+    qs, ks = q.shape, k.shape
+    if len(qs) != 3 or len(ks) != 4 or qs[0] != ks[0] or qs[2] != ks[3]:
         raise ValueError(f"q must be [B][Hq][d] matching the cache [B][Hkv][T][d]: "
-                         f"q {tuple(q.shape)}, cache {tuple(k.shape)}")
-    _expect(q, "q", q.shape, torch.float32)
+                         f"q {tuple(qs)}, cache {tuple(ks)}")
+    if q.dtype != torch.float32 or not q.is_contiguous():
+        _expect(q, "q", qs, torch.float32)
 
 
 def make_shape(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None = None) -> N.SrShape:

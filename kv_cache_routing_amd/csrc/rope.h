@@ -11,6 +11,7 @@
 // dtype for the key.
 #pragma once
 
+#include "angle.h"
 #include "sr_internal.h"
 
 namespace sr {
@@ -31,10 +32,10 @@ __device__ inline void store_elem(void* base, int64_t idx, double x, int32_t dty
         static_cast<uint16_t*>(base)[idx] = bf16_from_double(x);
 }
 
-// cos and sin of pos * inv_freq[i].
+// cos and sin of the angle pos * inv_freq[i] (the product rounded once in fp64).
 __device__ inline void rope_angle(int64_t pos, const float* inv_freq, int32_t i, double& c,
                                   double& s) {
-    sincos(static_cast<double>(pos) * static_cast<double>(inv_freq[i]), &s, &c);
+    angle_sincos(static_cast<double>(pos) * static_cast<double>(inv_freq[i]), s, c);
 }
 
 // The pair (x0, x1) turned by the angle with cosine c and sine s; the fused

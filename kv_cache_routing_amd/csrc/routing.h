@@ -303,24 +303,39 @@ __device__ inline SplitPlan uniform_plan(SplitPlan p) {
 
 // Fused rotary, first step: every workgroup turns all B*Hq new queries to
 // position T - 1 (the new token's) in LDS; workgroup 0 also writes them out.
-// The angles' cosines and sines stay in LDS for the key rows.
+// Each thread loads its query pairs first, so that their loads are in
+// flight while the angles are computed.  The angles' cosines and sines stay
+// in LDS for the key rows.  (Copying k0 to LDS here as well, to save the
+// scores' own load, measured slower: the scores are bound by their
+// arithmetic, and the rotation then waits for more loads.)
 template <int D, int NT>
 __device__ inline const float* rope_queries(const DecodeArgs& a, double*& s_c, double*& s_s) {
     extern __shared__ float4 s_rope[];  // rope_lds_bytes(B * Hq, D)
     constexpr int HALF = D / 2;
+    constexpr int MAXP = (kMaxFusedHeads * HALF + NT - 1) / NT;  // pairs per thread
     s_c = reinterpret_cast<double*>(s_rope);
     s_s = s_c + HALF;
     float* s_q = reinterpret_cast<float*>(s_s + HALF);
+    const int32_t n = a.batch * a.num_q_heads * HALF;
+    float x0[MAXP], x1[MAXP];
+#pragma unroll
+    for (int j = 0; j < MAXP; ++j) {  // pairs past n read pair 0 and go unused
+        const int32_t e = threadIdx.x + j * NT < n ? threadIdx.x + j * NT : 0;
+        const int32_t row = e / HALF, i = e - row * HALF;
+        x0[j] = a.q[static_cast<int64_t>(row) * D + i];
+        x1[j] = a.q[static_cast<int64_t>(row) * D + i + HALF];
+    }
     const int64_t pos = a.seq_len - 1;
     for (int i = threadIdx.x; i < HALF; i += NT) rope_angle(pos, a.inv_freq, i, s_c[i], s_s[i]);
     __syncthreads();
-    const int32_t n = a.batch * a.num_q_heads * HALF;
     const bool out = blockIdx.x == 0 && a.q_out;
-    for (int32_t e = threadIdx.x; e < n; e += NT) {
+#pragma unroll
+    for (int j = 0; j < MAXP; ++j) {
+        const int32_t e = threadIdx.x + j * NT;
+        if (e >= n) break;
         const int32_t row = e / HALF, i = e - row * HALF;
-        const float* x = a.q + static_cast<int64_t>(row) * D;
         double r0, r1;
-        rope_turn(x[i], x[i + HALF], s_c[i], s_s[i], r0, r1);
+        rope_turn(x0[j], x1[j], s_c[i], s_s[i], r0, r1);
         const float f0 = static_cast<float>(r0), f1 = static_cast<float>(r1);
         s_q[row * D + i] = f0;
         s_q[row * D + i + HALF] = f1;

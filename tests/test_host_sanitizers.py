@@ -29,3 +29,23 @@ def test_plan_arithmetic_under_sanitizers(tmp_path):
     r = subprocess.run([exe, "200000"], capture_output=True, text=True, timeout=300, env=env)
     assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-4000:])
     assert "200000 layouts ok" in r.stdout
+
+
+def test_rotary_angle_sincos_matches_the_c_library(tmp_path):
+    # sr::angle_sincos (the rotary angles' sine and cosine, shared by host and
+    # device code) against glibc's sin and cos over rotary angles, random
+    # arguments and quadrant boundaries, under the undefined-behaviour
+    # sanitizer: largest absolute error at most 4e-16.
+    gxx = shutil.which("g++")
+    if gxx is None or not os.path.isdir(os.path.join(ROCM_INCLUDE, "hip")):
+        pytest.skip("needs g++ and the HIP headers")
+    exe = str(tmp_path / "angle_check")
+    src = os.path.join(ROOT, "tests", "angle_check.cpp")
+    build = [gxx, "-std=c++17", "-O2", "-D__HIP_PLATFORM_AMD__", f"-I{ROCM_INCLUDE}",
+             f"-I{os.path.join(ROOT, 'kv_cache_routing_amd', 'csrc')}",
+             "-fsanitize=undefined", "-fno-sanitize-recover=undefined", src, "-o", exe]
+    r = subprocess.run(build, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-4000:]
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-4000:])
+    assert "max abs error" in r.stdout
