@@ -865,6 +865,47 @@ def test_graph_replay_matches_eager():
     assert int(ticket_region(ws, 8).abs().sum()) == 0
 
 
+def test_rope_step_graph_replay_matches_eager():
+    # A captured one-launch decode step, replayed with the new row of the
+    # caches reset by eager work in between: every replay writes the row
+    # again and reproduces the eager output, rotated query and caches.
+    B, Hq, Hkv, d, T = 1, 32, 8, 128, 9000
+    gen = torch.Generator().manual_seed(190)
+    kc = torch.randn((B, Hkv, T + 3, d), generator=gen).to(torch.bfloat16)
+    vc = torch.randn((B, Hkv, T + 3, d), generator=gen).to(torch.bfloat16)
+    qn, kn, vn = (torch.randn((B, H, d), generator=gen).cuda() for H in (Hq, Hkv, Hkv))
+    f = rope_inv_freq(d).cuda()
+    lau = launch("auto")
+    kA, vA, kB, vB = kc.cuda(), vc.cuda(), kc.cuda(), vc.cuda()
+    k0, v0 = sr.record_sink(kA[:, :, :T], vA[:, :, :T])
+    ws = sr.Workspace(sr.make_shape(qn, kA[:, :, :T], vA[:, :, :T]), lau, qn.device)
+    out_e, r_e, q_e = sr.rope_route_decode(qn, kn, vn, kA[:, :, :T], vA[:, :, :T], k0, v0, f,
+                                           0.0, launch=lau, ws=ws)
+    out_e, q_e = out_e.clone(), q_e.clone()
+    out_g, q_g = torch.empty_like(qn), torch.empty_like(qn)
+    r_g = sr.Routing(torch.empty_like(r_e.scores), torch.empty_like(r_e.mask),
+                     torch.empty_like(r_e.work_list), torch.empty_like(r_e.n_active))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sr.rope_route_decode(qn, kn, vn, kB[:, :, :T], vB[:, :, :T], k0, v0, f, 0.0,
+                             launch=lau, ws=ws, out=out_g, routing=r_g, q_out=q_g)
+    for it in range(5):
+        out_g.zero_()
+        q_g.zero_()
+        kB[:, :, T - 1] = 7.0
+        vB[:, :, T - 1] = 7.0
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e) and torch.equal(q_g, q_e), it
+        assert torch.equal(r_g.work_list, r_e.work_list), it
+        assert torch.equal(kB, kA) and torch.equal(vB, vA), it
+        sr.dense_decode(q_e, kA[:, :, :T], vA[:, :, :T], launch=lau, ws=ws)  # eager work
+        torch.cuda.synchronize()
+    assert int(r_e.n_active.item()) > 0  # tau = 0: planted nothing, some groups active
+    assert int(ticket_region(ws, B * Hkv).abs().sum()) == 0
+
+
 # --- randomized layers --------------------------------------------------------------
 @functools.lru_cache(maxsize=None)
 def _random_layers(n, seed):
