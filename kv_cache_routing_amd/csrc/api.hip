@@ -67,10 +67,11 @@ sr_status make_plan(const sr_shape& s, const sr_launch* launch, Plan& p) {
     if (l.kernel < SR_KERNEL_AUTO || l.kernel > SR_KERNEL_MFMA) return SR_ERR_INVALID_ARG;
     // Measured on MI355X (interleaved A/B, non-temporal loads, dense decode over
     // ~1 GiB): the matrix-core kernels lead at every group size and head size.
-    // bf16 at d = 128: by 1-5 % at G = 1-4, 1.9x at G = 8, 7x at G = 16 (PV on
+    // bf16 at d = 128: by 0-7 % at G = 1-4, 1.9x at G = 8, 6.6x at G = 16 (PV on
     // the matrix cores from G = 8); bf16 at d = 64 (two tiles per wave step): by
-    // 3-5 % at G = 1-4 and 2x-7x above; fp32: 6.6-6.95 TB/s against 5.8-6.1 at
-    // G <= 8 and ~2 at G = 16.  The vector-ALU kernel remains on request.
+    // 4-7 % at G = 1-4, 2x at G = 8 and 5x at G = 16; fp32: 6.6-6.9 TB/s against
+    // 5.9-6.0 at G <= 8 and ~2 at G = 16.  The vector-ALU kernel remains on
+    // request.
     p.kernel = l.kernel != SR_KERNEL_AUTO ? l.kernel : SR_KERNEL_MFMA;
     const int64_t n_items = static_cast<int64_t>(s.batch) * s.num_kv_heads;
     p.gp = pad_group(s.num_q_heads / s.num_kv_heads);
