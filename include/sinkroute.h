@@ -173,7 +173,9 @@ size_t sr_workspace_bytes(const sr_shape* shape, const sr_launch* launch);
 sr_status sr_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Routed decode (README decode-time steps; paper Eq. (1)).
- *   work_list, n_active: device outputs of sr_route.  Items at positions
+ *   work_list, n_active: device outputs of sr_route (the kernels clamp
+ *   n_active to [0, B*Hkv] and list entries to [0, B*Hkv), so another list
+ *   gives undefined results but no access outside the buffers).  Items at positions
  *   [n_active, B*Hkv) of the list are sinks: their G output rows get v0
  *   (bit-exact) and their caches are never read.  Items before are active:
  *     out[b,h,:] = sum_t softmax_t(sm_scale * <q[b,h], K[b,g,t]>) V[b,g,t,:]

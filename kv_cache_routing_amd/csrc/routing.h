@@ -453,7 +453,10 @@ __device__ inline bool map_work(const DecodeArgs& a, WorkRange& r) {
         // one round trip: the whole list and n_active load together
         __shared__ int32_t s_list[NT];
         __shared__ int32_t s_nact;
-        if (static_cast<int32_t>(threadIdx.x) < n_items) s_list[threadIdx.x] = a.work_list[threadIdx.x];
+        // entries outside [0, B*Hkv) (a list not made by sr_route) are clamped
+        // into range: wrong results, but no access outside the buffers
+        if (static_cast<int32_t>(threadIdx.x) < n_items)
+            s_list[threadIdx.x] = min(max(a.work_list[threadIdx.x], 0), n_items - 1);
         if (threadIdx.x == 0) s_nact = *a.n_active;
         __syncthreads();
         n_act = uniform(min(max(s_nact, 0), n_items));
@@ -464,10 +467,13 @@ __device__ inline bool map_work(const DecodeArgs& a, WorkRange& r) {
     } else {
         n_act = a.routed ? uniform(min(max(*a.n_active, 0), n_items)) : n_items;
         plan_range(n_act);
-        if (a.routed && n_act + wg < n_items) sink_item = uniform(a.work_list[n_act + wg]);
-        if (r.i_begin < r.i_end) r.item[0] = a.routed ? uniform(a.work_list[r.i_begin]) : r.i_begin;
+        auto listed = [&](int32_t i) {  // clamped as above
+            return uniform(min(max(a.work_list[i], 0), n_items - 1));
+        };
+        if (a.routed && n_act + wg < n_items) sink_item = listed(n_act + wg);
+        if (r.i_begin < r.i_end) r.item[0] = a.routed ? listed(r.i_begin) : r.i_begin;
         if (r.i_begin + 1 < r.i_end)
-            r.item[1] = a.routed ? uniform(a.work_list[r.i_begin + 1]) : r.i_begin + 1;
+            r.item[1] = a.routed ? listed(r.i_begin + 1) : r.i_begin + 1;
     }
     if (sink_item >= 0) {
         const int32_t b = sink_item / a.num_kv_heads, g = sink_item - b * a.num_kv_heads;

@@ -865,6 +865,32 @@ def test_graph_replay_matches_eager():
     assert int(ticket_region(ws, 8).abs().sum()) == 0
 
 
+@pytest.mark.parametrize("n_active", [3, 99, -4])
+def test_foreign_work_list_stays_inside_the_buffers(n_active):
+    # A work list not made by sr_route, with entries and counts out of range:
+    # the kernels clamp them, so every access stays inside the buffers (the
+    # output's guard region is untouched) and group 0, which appears only as
+    # an active item, still gets exact attention.
+    wl = Workload("foreign-list", 1, 32, 8, 128, 3000, "bf16", seed=195)
+    layer = make_layer(wl)
+    q, k, v = upload(layer)
+    k0, v0 = sr.record_sink(k, v)
+    n = q.numel()
+    big = torch.full((n + 8192,), 123.0, device=q.device)
+    out = big[:n].view(q.shape)
+    wl_dev = torch.tensor([5, 100, -5, 1000000, 3, 3, 6, 6], dtype=torch.int32, device=q.device)
+    na = torch.tensor([n_active], dtype=torch.int32, device=q.device)
+    for kernel in ("mfma", "valu"):
+        sr.decode_attn(q, k, v, v0, wl_dev, na, launch=launch(kernel), out=out)
+        torch.cuda.synchronize()
+        assert torch.all(big[n:] == 123.0), kernel
+        assert torch.isfinite(out).all(), kernel
+        if n_active == 3:  # group 0 comes from the clamped -5, active only
+            q_np, k_np, v_np = oracle_inputs(layer)
+            ref = oracle.dense_decode(q_np, k_np, v_np)
+            assert_outputs(out.cpu().numpy()[:, :4], ref[:, :4], f"group 0 {kernel}")
+
+
 def test_rope_step_graph_replay_matches_eager():
     # A captured one-launch decode step, replayed with the new row of the
     # caches reset by eager work in between: every replay writes the row
