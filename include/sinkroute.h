@@ -32,7 +32,9 @@
  *  fp32 (kv_dtype).  Every row start must be 16-byte aligned.
  *  q, out: fp32 [B][Hq][d] contiguous.  k0, v0: fp32 [B][Hkv][d] contiguous.
  *  q, out and k0 are read or written 16 bytes at a time and must start
- *  16-byte aligned; the other arrays need their element's alignment.
+ *  16-byte aligned; the other arrays need their element's alignment.  out
+ *  must not overlap q (SR_ERR_INVALID_ARG): workgroups still read q while
+ *  others write their rows of out.
  *
  *  Pointers: every data pointer is a device pointer owned by the caller; the
  *  library never allocates, frees or keeps them.  `stream` is a hipStream_t
@@ -221,7 +223,8 @@ sr_status sr_route_decode(const sr_shape* shape, const sr_launch* launch, const 
  * row of each KV group is written by the one workgroup that reads it in this
  * launch (for a sink group, the one that copies its v0 rows), before it reads.
  *   q_new, k_new, v_new, inv_freq: as sr_rope_append (unrotated, fp32).
- *   q_out: the rotated query [B][Hq][d] (may be NULL; must not overlap q_new).
+ *   q_out: the rotated query [B][Hq][d] (may be NULL; must not overlap q_new
+ *   or out).
  *   k_cache, v_cache: caches with room for position T - 1 (strides as usual).
  *   k0, v0, tau, sm_scale, scores, mask, work_list, n_active, ws, out: as
  *   sr_route_decode.

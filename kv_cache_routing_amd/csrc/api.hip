@@ -154,11 +154,15 @@ sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float
             return SR_ERR_INVALID_ARG;
         const size_t q_bytes =
             static_cast<size_t>(s.batch) * s.num_q_heads * s.head_dim * sizeof(float);
-        if (rope->q_out && overlaps(rope->q_out, q, q_bytes)) return SR_ERR_INVALID_ARG;
+        if (rope->q_out && (overlaps(rope->q_out, q, q_bytes) || overlaps(rope->q_out, out, q_bytes)))
+            return SR_ERR_INVALID_ARG;
     }
     if ((st = check_caches(s, k, v)) != SR_OK) return st;
     if (!q || !out || !ws || !aligned16(q) || !aligned16(out) || !aligned16(ws))
         return SR_ERR_INVALID_ARG;
+    // every workgroup reads q (all of it when it routes) while others write out
+    const size_t q_bytes = static_cast<size_t>(s.batch) * s.num_q_heads * s.head_dim * sizeof(float);
+    if (overlaps(out, q, q_bytes)) return SR_ERR_INVALID_ARG;
     if (routed && !v0) return SR_ERR_INVALID_ARG;
     if (routed && !fused && (!work_list || !n_active)) return SR_ERR_INVALID_ARG;
     if (fused && (!fused->k0 || !aligned16(fused->k0) || isnan(fused->tau)))

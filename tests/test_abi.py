@@ -14,6 +14,7 @@ from kv_cache_routing_amd import _native as N
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation
+OUT = 0x40000000  # a different fake for out, which must not overlap q
 
 
 def header_functions():
@@ -46,7 +47,7 @@ def p(x=FAKE):
     return ctypes.c_void_p(x)
 
 
-def decode(s, launch=None, ws_bytes=1 << 30, q=FAKE, k=FAKE, v=FAKE, out=FAKE, ws=FAKE,
+def decode(s, launch=None, ws_bytes=1 << 30, q=FAKE, k=FAKE, v=FAKE, out=OUT, ws=FAKE,
            v0=FAKE, wl=FAKE, na=FAKE):
     lp = None if launch is None else ctypes.byref(launch)
     return N.lib.sr_decode_attn(ctypes.byref(s), lp, p(q), p(k), p(v), p(v0), p(wl), p(na), 0.0,
@@ -76,6 +77,7 @@ def test_stride_and_alignment_checks():
     assert decode(s) == N.SR_ERR_INVALID_ARG
     assert decode(shape(), k=FAKE + 8) == N.SR_ERR_INVALID_ARG
     assert decode(shape(), q=FAKE + 4) == N.SR_ERR_INVALID_ARG
+    assert decode(shape(), out=FAKE + 4096) == N.SR_ERR_INVALID_ARG  # out overlaps q
 
 
 @pytest.mark.parametrize("which", ["q", "k", "v", "out", "ws", "v0", "wl", "na"])
@@ -85,7 +87,8 @@ def test_null_pointers(which):
 
 def test_dense_needs_no_routing_pointers_but_checks_the_rest():
     s = shape()
-    r = N.lib.sr_dense_decode(ctypes.byref(s), None, p(), p(0), p(), 0.0, p(), 1 << 30, p(), None)
+    r = N.lib.sr_dense_decode(ctypes.byref(s), None, p(), p(0), p(), 0.0, p(), 1 << 30, p(OUT),
+                              None)
     assert r == N.SR_ERR_INVALID_ARG
 
 
@@ -172,7 +175,7 @@ def test_fused_route_decode_validation():
     def fused(s, k0=FAKE, v0=FAKE, tau=0.5, ws_bytes=1 << 30):
         return N.lib.sr_route_decode(ctypes.byref(s), None, p(), p(), p(), p(k0), p(v0),
                                      ctypes.c_float(tau), 0.0, p(0), p(0), p(0), p(0), p(),
-                                     ws_bytes, p(), None)
+                                     ws_bytes, p(OUT), None)
     assert fused(s, k0=0) == N.SR_ERR_INVALID_ARG
     assert fused(s, v0=0) == N.SR_ERR_INVALID_ARG
     assert fused(s, tau=float("nan")) == N.SR_ERR_INVALID_ARG
@@ -186,13 +189,14 @@ def test_rope_route_decode_validation():
     def call(s, kn=FAKE, vn=FAKE, f=FAKE, q_out=0, q=FAKE):
         return N.lib.sr_rope_route_decode(ctypes.byref(s), None, p(q), p(kn), p(vn), p(f),
                                           p(q_out), p(), p(), p(), p(), ctypes.c_float(0.5), 0.0,
-                                          p(0), p(0), p(0), p(0), p(), 1 << 30, p(), None)
+                                          p(0), p(0), p(0), p(0), p(), 1 << 30, p(OUT), None)
     s = shape()
     assert call(s, kn=0) == N.SR_ERR_INVALID_ARG
     assert call(s, vn=0) == N.SR_ERR_INVALID_ARG
     assert call(s, f=0) == N.SR_ERR_INVALID_ARG
     assert call(shape(T=1)) == N.SR_ERR_INVALID_ARG            # position 0 is the sink key
     assert call(s, q_out=FAKE + 4096) == N.SR_ERR_INVALID_ARG  # overlaps q_new
+    assert call(s, q_out=OUT + 64) == N.SR_ERR_INVALID_ARG     # overlaps out
     assert call(shape(B=3, Hq=32, Hkv=8)) == N.SR_ERR_UNSUPPORTED  # 96 query heads
 
 
