@@ -400,18 +400,52 @@ def decode_layers_report(sr, torch, args):
 
     q_rots = [[torch.empty_like(out) for _ in range(L)] for _ in range(N)]
 
-    def token(t, routed=True, attend=True, append=True, fused=False):
+    # --model-step: the rest of a Llama-3.1-8B decoder layer around the
+    # attention, with random-init bf16 weights (timing only): QKV projection,
+    # O projection and SwiGLU MLP as library M = 1 products, the residual adds
+    # folded into them.  Each weight is stored in the layout whose product
+    # streamed faster on MI355X (QKV and down as [out][in], O and gate/up as
+    # [in][out]).  RMSNorm is left out (two vector ops per layer, fused in a
+    # serving engine).  The new key and value come from the projection; the
+    # attention keeps the planted rotated-frame queries, so that half of the
+    # groups still route as sinks (a projected random query would make every
+    # group active).
+    Hd, Ff = Hq * d, 14336
+    wts, hid = [], None
+    if args.model_step:
+        wgen = torch.Generator(device=dev).manual_seed(9002)
+
+        def weight(rows, cols, fan_in):
+            return (torch.randn((rows, cols), generator=wgen, device=dev)
+                    * fan_in ** -0.5).to(torch.bfloat16)
+        for _ in range(L):
+            wts.append({"qkv": weight(Hd + 2 * Hkv * d, Hd, Hd), "o": weight(Hd, Hd, Hd),
+                        "gu": weight(Hd, 2 * Ff, Hd), "down": weight(Hd, Ff, Ff)})
+        hid = torch.randn((1, Hd), generator=wgen, device=dev).to(torch.bfloat16)
+
+    def token(t, routed=True, attend=True, append=True, fused=False, model=False):
         pos = T0 + t
         for layer in range(L):
             k, v = caches[layer]
             qp, kn, vn = plans[t][layer]
             q_rot = q_rots[t][layer]
+            if model:
+                kvn = torch.nn.functional.linear(hid, wts[layer]["qkv"])[:, Hd:].float()
+                kn = kvn[:, :Hkv * d].view(B, Hkv, d)
+                vn = kvn[:, Hkv * d:].view(B, Hkv, d)
             if fused:  # one launch per layer; tau > 1 gives the dense result
                 k0, v0 = k0v0[layer]
                 tau = 0.5 if routed and start <= layer <= end else 2.0
-                sr.rope_route_decode(qp, kn, vn, k[:, :, :pos + 1], v[:, :, :pos + 1], k0, v0,
-                                     freq, tau, launch=lau, ws=ws, out=out,
-                                     routing=routing[layer], q_out=q_rot)
+                if attend:
+                    sr.rope_route_decode(qp, kn, vn, k[:, :, :pos + 1], v[:, :, :pos + 1], k0,
+                                         v0, freq, tau, launch=lau, ws=ws, out=out,
+                                         routing=routing[layer], q_out=q_rot)
+                if model:
+                    w = wts[layer]
+                    hid.addmm_(out.view(1, Hd).to(torch.bfloat16), w["o"])
+                    gu = hid @ w["gu"]
+                    act = torch.nn.functional.silu(gu[:, :Ff]) * gu[:, Ff:]
+                    hid.addmm_(act, w["down"].t())
                 continue
             if append:
                 sr.rope_append(qp, kn, vn, k, v, pos, freq, q_out=q_rot)
@@ -465,6 +499,25 @@ def decode_layers_report(sr, torch, args):
     attend_dense = run(graphs(routed=False, append=False))
     routed_one = run(graphs(routed=True, fused=True))
     dense_one = run(graphs(routed=False, fused=True))
+    model_rep = None
+    if args.model_step:
+        for kw in (dict(routed=True), dict(routed=False), dict(attend=False)):
+            token(0, fused=True, model=True, **kw)  # eager first: library handles, workspaces
+        torch.cuda.synchronize()
+        full_routed = run(graphs(routed=True, fused=True, model=True))
+        full_dense = run(graphs(routed=False, fused=True, model=True))
+        rest = run(graphs(attend=False, fused=True, model=True))
+        model_rep = {
+            "layer": "Llama-3.1-8B decoder layer, random-init bf16 weights "
+                     f"({sum(x.numel() for w in wts for x in w.values()) * 2 / 2 ** 30:.1f} GiB "
+                     "for all layers): QKV, attention (one launch), O, SwiGLU MLP as library "
+                     "M = 1 products, residual adds folded in, RMSNorm left out",
+            "us_per_token_routed": round(full_routed, 1),
+            "us_per_token_dense": round(full_dense, 1),
+            "speedup": round(full_dense / full_routed, 4),
+            "composition_us_per_token": {"projections_mlp": round(rest, 1),
+                                         "attention_routed": round(full_routed - rest, 1),
+                                         "attention_dense": round(full_dense - rest, 1)}}
     gated = sum(1 for layer in range(L) if start <= layer <= end)
     rep = {"decode_layers": {
         "layers": L, "context": T0, "tokens": N, "routed_layers": [start, end],
@@ -480,6 +533,7 @@ def decode_layers_report(sr, torch, args):
             "us_per_token_routed": round(routed_one, 1),
             "us_per_token_dense": round(dense_one, 1),
             "speedup": round(dense_one / routed_one, 4)},
+        **({"model_step": model_rep} if model_rep else {}),
         "kv_gib_per_token_dense": round(L * 2 * B * Hkv * T0 * d * 2 / 2 ** 30, 2)}}
     print(json.dumps(rep), flush=True)
     return 0
@@ -538,6 +592,9 @@ def main():
                          "dense attention per layer) and exit")
     ap.add_argument("--context", type=int, default=131072, help="context of --decode-layers")
     ap.add_argument("--tokens", type=int, default=8, help="decode steps of --decode-layers")
+    ap.add_argument("--model-step", action="store_true",
+                    help="--decode-layers also runs each layer's projections and MLP "
+                         "(random-init Llama-3.1-8B weights) around the attention")
     ap.add_argument("--layer-range", type=int, nargs=2, default=None, metavar=("START", "END"),
                     help="layers routed by --decode-layers (inclusive); the rest run dense")
     ap.add_argument("--envelope", action="store_true",
