@@ -756,6 +756,10 @@ ROPE_FUSED = [
     ("waves8-f32-d64", 1, 32, 8, 64, "f32", 3000, 2, 0.5, "auto", 8, 0),
     ("valu-f32-g16", 1, 32, 2, 64, "f32", 2500, 1, 0.5, "valu", 0, 0),
     ("two-positions", 1, 32, 8, 128, "bf16", 2, 4, 0.5, "auto", 0, 0),
+    ("g3-ragged", 1, 24, 8, 128, "bf16", 7777, 3, 0.5, "auto", 0, 0),
+    ("g6-b2-d64", 2, 24, 4, 64, "bf16", 5001, 1, 0.5, "auto", 0, 0),
+    ("g12-f32-valu", 1, 48, 4, 128, "f32", 3333, 2, 0.5, "valu", 0, 0),
+    ("g5-waves8", 1, 40, 8, 128, "bf16", 6000, 5, 0.5, "mfma", 8, 0),
 ]
 
 
