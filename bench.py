@@ -62,10 +62,12 @@ def decode_sources_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_record(kernel_name: str, workload: str):
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def traffic_record(kernel_name: str, workload: str, path: str = TRAFFIC_JSON):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel sources; otherwise None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -91,7 +93,7 @@ def _pmc_rows(path, counter):
     return rows
 
 
-def summarize_counters(fetch_csv, write_csv):
+def summarize_counters(fetch_csv, write_csv, out_path: str = TRAFFIC_JSON):
     """HBM bytes per decode launch = counter (KiB) x 1024 x (COPY_BYTES / the
     same counter's reading on the plain COPY_BYTES copy that `--calibrate-copy`
     runs first).  Both runs execute the same program, so dispatch ids match;
@@ -121,10 +123,10 @@ def summarize_counters(fetch_csv, write_csv):
                 "hbm_bytes_per_launch": round(rec["FETCH_SIZE"]["bytes_per_dispatch"]
                                               + rec["WRITE_SIZE"]["bytes_per_dispatch"]),
                 "fetch": rec["FETCH_SIZE"], "write": rec["WRITE_SIZE"]}
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    with open(path, "w") as f:
+    with open(out_path, "w") as f:
         json.dump(recs, f, indent=1, sort_keys=True)
     print(json.dumps(recs, indent=1))
+    return recs
 
 
 def algorithmic_bytes(wl, n_active: int) -> int:
