@@ -230,9 +230,12 @@ sr_status sr_route_decode(const sr_shape* shape, const sr_launch* launch, const 
  *   sr_route_decode.
  * Bitwise equal to sr_rope_append at pos = T - 1 followed by sr_route_decode
  * with seq_len = T: the same q_out, cache rows, routing outputs and out.
- * Layers of up to 64 query heads only (B*Hq <= 64, else SR_ERR_UNSUPPORTED:
- * call the two entry points); T >= 2 (position 0 is the recorded sink key).
- * tau > 1 gives the dense result of the same step. */
+ * Above 64 query heads (B*Hq > 64) it is two launches, like sr_route_decode:
+ * the routing kernel's workgroup that scores a KV group first turns that
+ * group's queries into q_out and appends its row, then the decode reads
+ * q_out, which is therefore required there (NULL: SR_ERR_INVALID_ARG).
+ * T >= 2 (position 0 is the recorded sink key).  tau > 1 gives the dense
+ * result of the same step. */
 sr_status sr_rope_route_decode(const sr_shape* shape, const sr_launch* launch,
                                const float* q_new, const float* k_new, const float* v_new,
                                const float* inv_freq, float* q_out, void* k_cache, void* v_cache,

@@ -147,9 +147,11 @@ sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float
     sr_status st = check_shape(shape);
     if (st != SR_OK) return st;
     const sr_shape& s = *shape;
-    if (rope) {  // rotary inside the fused-routing launch only
-        if (static_cast<int64_t>(s.batch) * s.num_q_heads > kMaxFusedHeads)
-            return SR_ERR_UNSUPPORTED;
+    if (rope) {
+        // above kMaxFusedHeads the routing kernel rotates the queries into
+        // q_out, which the decode launch then reads
+        if (static_cast<int64_t>(s.batch) * s.num_q_heads > kMaxFusedHeads && !rope->q_out)
+            return SR_ERR_INVALID_ARG;
         if (s.seq_len < 2 || !rope->k_new || !rope->v_new || !rope->inv_freq)
             return SR_ERR_INVALID_ARG;
         const size_t q_bytes =
@@ -227,8 +229,16 @@ sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float
         int32_t* list = fused->work_list ? fused->work_list : ws_list;
         int32_t* n_act = fused->n_active ? fused->n_active : ws_list + n_items;
         uint8_t* flags = fused->mask ? fused->mask : ws_flags;
+        RouteRope rr{};
+        if (rope) {
+            rr = RouteRope{q, rope->k_new, rope->v_new, rope->inv_freq, rope->q_out,
+                           const_cast<void*>(k), const_cast<void*>(v), s.stride_b, s.stride_h,
+                           s.stride_t, s.seq_len - 1, s.kv_dtype == SR_KV_F32 ? 1 : 0};
+            a.rope = 0;          // done by the routing kernel
+            a.q = rope->q_out;   // the decode reads the rotated queries
+        }
         hipError_t e = launch_route(s, q, fused->k0, fused->tau, fused->scores, flags, list,
-                                    n_act, ticket, hs);
+                                    n_act, ticket, hs, rr);
         if (e != hipSuccess) return SR_ERR_HIP;
         a.fused = 0;
         a.work_list = list;

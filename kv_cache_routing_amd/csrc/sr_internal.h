@@ -252,9 +252,26 @@ hipError_t launch_record(const sr_shape& s, const void* k, const void* v, float*
                          hipStream_t st);
 // ticket: a zeroed counter in device memory, or null (a second launch then
 // partitions large layers).
+// The rotary step done by the routing kernel (sr_rope_route_decode on layers
+// above kMaxFusedHeads query heads): the workgroup that scores an item first
+// turns its heads' new queries to position pos into q_out and appends its
+// new key and value row there; the scores are then taken from q_out.
+// q_new == nullptr: no rotary step (q is already rotated).
+struct RouteRope {
+    const float* q_new;     // [B][Hq][d] unrotated
+    const float* k_new;     // [B][Hkv][d] unrotated
+    const float* v_new;     // [B][Hkv][d]
+    const float* inv_freq;  // [d/2]
+    float* q_out;           // [B][Hq][d] rotated (required)
+    void* k_cache;
+    void* v_cache;
+    int64_t stride_b, stride_h, stride_t, pos;
+    int32_t kv_f32;
+};
+
 hipError_t launch_route(const sr_shape& s, const float* q, const float* k0, float tau,
                         float* scores, uint8_t* flags, int32_t* work_list, int32_t* n_active,
-                        uint32_t* ticket, hipStream_t st);
+                        uint32_t* ticket, hipStream_t st, const RouteRope& rope = RouteRope{});
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_rope_append(const sr_shape& s, const float* q_new, const float* k_new,
                               const float* v_new, const float* inv_freq, int64_t pos,

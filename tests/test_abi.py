@@ -197,7 +197,7 @@ def test_rope_route_decode_validation():
     assert call(shape(T=1)) == N.SR_ERR_INVALID_ARG            # position 0 is the sink key
     assert call(s, q_out=FAKE + 4096) == N.SR_ERR_INVALID_ARG  # overlaps q_new
     assert call(s, q_out=OUT + 64) == N.SR_ERR_INVALID_ARG     # overlaps out
-    assert call(shape(B=3, Hq=32, Hkv=8)) == N.SR_ERR_UNSUPPORTED  # 96 query heads
+    assert call(shape(B=3, Hq=32, Hkv=8)) == N.SR_ERR_INVALID_ARG  # 96 heads need q_out
 
 
 # --- work division (host-side model of what the decode kernel streams) ----------

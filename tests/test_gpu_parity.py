@@ -761,6 +761,12 @@ ROPE_FUSED = [
     ("g6-b2-d64", 2, 24, 4, 64, "bf16", 5001, 1, 0.5, "auto", 0, 0),
     ("g12-f32-valu", 1, 48, 4, 128, "f32", 3333, 2, 0.5, "valu", 0, 0),
     ("g5-waves8", 1, 40, 8, 128, "bf16", 6000, 5, 0.5, "mfma", 8, 0),
+    # above 64 query heads: the routing kernel rotates and appends, then the decode
+    ("128-heads", 2, 64, 8, 128, "bf16", 9000, 4, 0.5, "auto", 0, 0),
+    ("70b-shape-512-heads", 8, 64, 8, 128, "bf16", 3000, 4, 0.5, "auto", 0, 0),
+    ("g16-f32-256-heads", 4, 64, 4, 64, "f32", 2000, 2, 0.5, "valu", 0, 0),
+    ("1024-items", 128, 8, 8, 64, "bf16", 700, 3, 0.5, "mfma", 0, 0),
+    ("large-dense", 4, 32, 8, 128, "bf16", 4097, 0, 2.0, "auto", 0, 0),
 ]
 
 
@@ -996,15 +1002,16 @@ def test_randomized_layers_against_oracle(i):
 
 @functools.lru_cache(maxsize=None)
 def _random_rope_steps(n, seed):
-    """n seeded random one-launch decode steps: up to 64 query heads, any G up
-    to 16, both head sizes and dtypes, T from 2 to 20000, any number of
+    """n seeded random one-call decode steps: up to 512 query heads (one launch
+    up to 64, two above), any G up to 16, both head sizes and dtypes, T from 2
+    to 20000, any number of
     planted sink groups, routed, dense (tau > 1) or all-sink (tau < -1), every
     kernel, wave count and split policy."""
     rng = np.random.default_rng(seed)
     out = []
     while len(out) < n:
-        Hkv, G, B = int(rng.choice([1, 2, 4, 8])), int(rng.integers(1, 17)), int(rng.integers(1, 4))
-        if B * Hkv * G > 64:
+        Hkv, G, B = int(rng.choice([1, 2, 4, 8])), int(rng.integers(1, 17)), int(rng.integers(1, 9))
+        if B * Hkv * G > 512:
             continue
         out.append((f"step{len(out)}", B, Hkv * G, Hkv, int(rng.choice([64, 128])),
                     str(rng.choice(["bf16", "f32"])), int(rng.integers(2, 20000)),
