@@ -150,6 +150,7 @@ __global__ __launch_bounds__(NT) void k_route(
         if (rope) rope_round<NT>(rr, s_c, s_s, 0, n_items, G, d, Hkv, hs, L);
         const bool own = hg < n_items;
         const int32_t j = own ? hg : n_items - 1;  // idle groups re-score the last item
+        // (one round only: with the rotary step its rows are written by now)
         const bool sink = score_item16<8>(qs, k0, j, G, d, hl, tau, own ? scores : nullptr);
         if (own && hl == 0) {
             flags[j] = sink ? 1 : 0;
@@ -165,7 +166,11 @@ __global__ __launch_bounds__(NT) void k_route(
             rope_round<NT>(rr, s_c, s_s, j0, count(j0), G, d, Hkv, hs, L);
         }
         const bool own = hg < ipw && j0 + hg < n_items;
-        const int32_t j = own ? j0 + hg : n_items - 1;  // idle groups re-score the last item
+        // idle groups re-score an item: without the rotary step the last; with
+        // it the round's first, whose rotated rows are already written (an
+        // earlier look at rows written in a later round could leave stale lines
+        // in this CU's cache)
+        const int32_t j = own ? j0 + hg : (rope ? j0 : n_items - 1);
         const bool sink = score_item16<8>(qs, k0, j, G, d, hl, tau, own ? scores : nullptr);
         if (own && hl == 0) {
             const uint8_t f = sink ? 1 : 0;

@@ -767,6 +767,9 @@ ROPE_FUSED = [
     ("g16-f32-256-heads", 4, 64, 4, 64, "f32", 2000, 2, 0.5, "valu", 0, 0),
     ("1024-items", 128, 8, 8, 64, "bf16", 700, 3, 0.5, "mfma", 0, 0),
     ("large-dense", 4, 32, 8, 128, "bf16", 4097, 0, 2.0, "auto", 0, 0),
+    # 4800 groups: more than 1024 routing workgroups of 4, so a workgroup rotates
+    # and scores several rounds
+    ("multi-round-4800-groups", 600, 8, 8, 128, "bf16", 40, 3, 0.5, "auto", 0, 0),
 ]
 
 
