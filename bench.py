@@ -828,7 +828,7 @@ def main():
         "us_per_layer_step_two_calls": round(ms_routed * 1e3, 2),
         "us_per_layer_step_dense": round(ms_dense * 1e3, 2),
         "speedup_vs_dense": round(ms_dense / ms_step, 4),
-        "step": ("sr_route_decode (routing + decode in one launch)" if fused_wins else
+        "step": ("sr_route_decode (routing + decode in one call)" if fused_wins else
                  "sr_route + sr_decode_attn (two launches)") + ", the faster of the two forms",
         "sink_ratio": round(1 - n_active / (wl.batch * wl.num_kv_heads), 4),
         "dense_gbs": round(dense_gbs, 1),

@@ -228,7 +228,8 @@ def decode_attn(q, k, v, v0, work_list, n_active, sm_scale: float = 0.0,
 def route_decode(q, k, v, k0, v0, tau: float = 0.5, sm_scale: float = 0.0,
                  launch: N.SrLaunch | None = None, ws: Workspace | None = None,
                  out: torch.Tensor | None = None, routing: Routing | None = None):
-    """Routing and decode in one launch; returns (out, routing outputs)."""
+    """Routing and decode in one call (one launch up to 64 query heads, the
+    routing kernel and then the decode above); returns (out, routing outputs)."""
     _expect_q(q, k)
     B, Hkv, _, d = k.shape
     _expect(k0, "k0", (B, Hkv, d), torch.float32)
@@ -254,9 +255,10 @@ def rope_route_decode(q_new, k_new, v_new, k, v, k0, v0, inv_freq, tau: float = 
                       sm_scale: float = 0.0, launch: N.SrLaunch | None = None,
                       ws: Workspace | None = None, out: torch.Tensor | None = None,
                       routing: Routing | None = None, q_out: torch.Tensor | None = None):
-    """One decode step in one launch: rotate the new token's query and key to
-    position T - 1 and append its key and value there, then route and attend
-    over positions 0 .. T - 1.  k, v are cache views [B][Hkv][T][d] whose last
+    """One decode step in one call (one launch up to 64 query heads, two
+    above; q_out carries the rotated queries between them): rotate the new
+    token's query and key to position T - 1 and append its key and value
+    there, then route and attend over positions 0 .. T - 1.  k, v are cache views [B][Hkv][T][d] whose last
     row is the new token's (their storage must hold it).  Returns (out,
     routing outputs, rotated q)."""
     _expect_q(q_new, k)
