@@ -911,6 +911,33 @@ def test_foreign_work_list_stays_inside_the_buffers(n_active):
             assert_outputs(out.cpu().numpy()[:, :4], ref[:, :4], f"group 0 {kernel}")
 
 
+@pytest.mark.parametrize("dtype,Hq", [("bf16", 32), ("f32", 128)])
+def test_rope_step_on_padded_cache_rows(dtype, Hq):
+    # Cache rows d + 8 elements apart (views of padded storage): the one-call
+    # step equals the two calls bitwise and never writes the padding.
+    B, Hkv, d, T = 1, 8, 128, 3001
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    gen = torch.Generator().manual_seed(200 + Hq)
+    store = torch.randn((B, Hkv, T + 2, d + 8), generator=gen).to(tdt)
+    store[..., d:] = -3.0  # the padding
+    vstore = torch.randn((B, Hkv, T + 2, d + 8), generator=gen).to(tdt)
+    vstore[..., d:] = -3.0
+    qn, kn, vn = (torch.randn((B, H, d), generator=gen).cuda() for H in (Hq, Hkv, Hkv))
+    f = rope_inv_freq(d).cuda()
+    kA, vA, kB, vB = store.cuda(), vstore.cuda(), store.cuda(), vstore.cuda()
+    view = lambda t: t[:, :, :T, :d]
+    assert view(kA).stride(2) == d + 8
+    k0, v0 = sr.record_sink(view(kA), view(vA))
+    q_rot = sr.rope_append(qn, kn, vn, kA[..., :d], vA[..., :d], T - 1, f)
+    out_a, r_a = sr.route_decode(q_rot, view(kA), view(vA), k0, v0, 0.0)
+    out_b, r_b, q_b = sr.rope_route_decode(qn, kn, vn, view(kB), view(vB), k0, v0, f, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(q_b, q_rot) and torch.equal(out_b, out_a)
+    assert torch.equal(r_b.work_list, r_a.work_list)
+    assert torch.equal(kB, kA) and torch.equal(vB, vA)  # padding included
+    assert torch.all(kB[..., d:] == -3.0) and torch.all(vB[..., d:] == -3.0)
+
+
 def test_rope_step_graph_replay_matches_eager():
     # A captured one-launch decode step, replayed with the new row of the
     # caches reset by eager work in between: every replay writes the row
