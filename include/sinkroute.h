@@ -215,16 +215,17 @@ sr_status sr_route_decode(const sr_shape* shape, const sr_launch* launch, const 
                           uint8_t* mask, int32_t* work_list, int32_t* n_active, void* ws,
                           size_t ws_bytes, float* out, void* stream);
 
-/* One decode step of a layer in one launch: sr_rope_append of the new token
+/* One decode step of a layer in one call: sr_rope_append of the new token
  * at position T - 1 (T = shape->seq_len, the positions attended after the
  * append), then sr_route_decode over positions 0 .. T - 1 (README decode-time
  * steps: rotate the new query, compare it with the position-0 key, route,
- * attend).  Every workgroup rotates the queries itself; the new key and value
- * row of each KV group is written by the one workgroup that reads it in this
- * launch (for a sink group, the one that copies its v0 rows), before it reads.
+ * attend).  Up to 64 query heads it is one launch: every workgroup rotates
+ * the queries itself, and the new key and value row of each KV group is
+ * written by the one workgroup that reads it in this launch (for a sink
+ * group, the one that copies its v0 rows), before it reads.
  *   q_new, k_new, v_new, inv_freq: as sr_rope_append (unrotated, fp32).
- *   q_out: the rotated query [B][Hq][d] (may be NULL; must not overlap q_new
- *   or out).
+ *   q_out: the rotated query [B][Hq][d] (may be NULL up to 64 query heads;
+ *   must not overlap q_new or out).
  *   k_cache, v_cache: caches with room for position T - 1 (strides as usual).
  *   k0, v0, tau, sm_scale, scores, mask, work_list, n_active, ws, out: as
  *   sr_route_decode.
