@@ -1011,14 +1011,15 @@ def _random_layers(n, seed):
 
 
 # Counts of the randomized tests; larger sweeps run with, e.g.,
-# SR_FUZZ_LAYERS=5000 SR_FUZZ_STEPS=2000 python -m pytest tests -m gpu -k randomized
+# SR_FUZZ_LAYERS=5000 SR_FUZZ_STEPS=2000 [SR_FUZZ_SEED=n] python -m pytest tests -m gpu -k randomized
 N_RANDOM_LAYERS = int(os.environ.get("SR_FUZZ_LAYERS", "48"))
 N_RANDOM_STEPS = int(os.environ.get("SR_FUZZ_STEPS", "24"))
+FUZZ_SEED = int(os.environ.get("SR_FUZZ_SEED", "7001"))
 
 
 @pytest.mark.parametrize("i", range(N_RANDOM_LAYERS))
 def test_randomized_layers_against_oracle(i):
-    layer, kernel, waves, splits = _random_layers(N_RANDOM_LAYERS, 7001)[i]
+    layer, kernel, waves, splits = _random_layers(N_RANDOM_LAYERS, FUZZ_SEED)[i]
     wl = layer.wl
     log(f"{wl.name}: B={wl.batch} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} d={wl.head_dim} "
         f"T={wl.seq_len} {wl.kv_dtype} {wl.sink_plan} kernel={kernel} waves={waves} splits={splits}")
@@ -1053,4 +1054,4 @@ def _random_rope_steps(n, seed):
 
 @pytest.mark.parametrize("i", range(N_RANDOM_STEPS))
 def test_randomized_rope_steps(i):
-    _rope_step_check(_random_rope_steps(N_RANDOM_STEPS, 7002)[i], planted=False)
+    _rope_step_check(_random_rope_steps(N_RANDOM_STEPS, FUZZ_SEED + 1)[i], planted=False)
