@@ -203,9 +203,10 @@ sr_status sr_decode_attn(const sr_shape* shape, const sr_launch* launch, const f
  * outputs.  That saves a launch and the routing kernel per layer-step.
  * Larger layers run the routing kernel and then the decode on `stream`,
  * since scoring hundreds of heads in every workgroup costs more than the
- * extra launch; the routing kernel is then a single launch at any size (the
- * workgroup that finishes scoring last partitions, through a ticket in the
- * workspace).  Either way the decisions, the work list and the output are
+ * extra launch.  Up to 64 KV groups (B*Hkv <= 64) the routing kernel only
+ * writes the per-group flags and every decode workgroup partitions them
+ * itself; above, the workgroup that finishes scoring last partitions,
+ * through a ticket in the workspace.  Either way the decisions, the work list and the output are
  * bit-identical to the two-call form under the same launch policy.  scores /
  * mask / work_list / n_active may each be NULL; the workspace holds the
  * flags, list and count when they are. */

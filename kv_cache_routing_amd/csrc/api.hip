@@ -221,7 +221,7 @@ sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (fused && static_cast<int64_t>(s.batch) * s.num_q_heads > kMaxFusedHeads) {
-        // large layer: the routing kernel, then the routed decode
+        // large layer: the routing kernel (spread over the chip), then the decode
         const int32_t n_items = s.batch * s.num_kv_heads;
         int32_t* ws_list = reinterpret_cast<int32_t*>(base + w.route);
         uint32_t* ticket = reinterpret_cast<uint32_t*>(ws_list + n_items + 1);
@@ -237,12 +237,23 @@ sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float
             a.rope = 0;          // done by the routing kernel
             a.q = rope->q_out;   // the decode reads the rotated queries
         }
-        hipError_t e = launch_route(s, q, fused->k0, fused->tau, fused->scores, flags, list,
-                                    n_act, ticket, hs, rr);
-        if (e != hipSuccess) return SR_ERR_HIP;
-        a.fused = 0;
-        a.work_list = list;
-        a.n_active = n_act;
+        if (n_items <= 64) {
+            // the routing kernel writes the flags only; every decode workgroup
+            // partitions them with one ballot (as when it scores itself) and
+            // workgroup 0 writes the list and count
+            hipError_t e = launch_route(s, q, fused->k0, fused->tau, fused->scores, flags,
+                                        nullptr, nullptr, nullptr, hs, rr);
+            if (e != hipSuccess) return SR_ERR_HIP;
+            a.flags_in = flags;
+            a.mask_out = nullptr;  // the flags are the mask
+        } else {
+            hipError_t e = launch_route(s, q, fused->k0, fused->tau, fused->scores, flags, list,
+                                        n_act, ticket, hs, rr);
+            if (e != hipSuccess) return SR_ERR_HIP;
+            a.fused = 0;
+            a.work_list = list;
+            a.n_active = n_act;
+        }
     }
     hipError_t e = p.kernel == SR_KERNEL_MFMA ? launch_decode_mfma(s, a, p.gp, p.waves, hs)
                                                : launch_decode_valu(s, a, p.gp, p.waves, hs);

@@ -30,13 +30,6 @@ __global__ void k_record(const void* k, const void* v, float* k0, float* v0, int
     v0[e] = load_elem(v, src, dtype);
 }
 
-// The decision step for a whole layer.  Item-major: each aligned 16-lane
-// group scores every head of one item at a time (shared arithmetic in
-// routing.h) and writes its flag; the workgroups stride over the items.
-// Then one workgroup partitions the flags: the only workgroup of a
-// one-workgroup launch (its flags stay in LDS), else the one that draws the
-// last ticket (when `ticket` is given; a partition launch follows otherwise).  The ticket starts
-// at zero and is left at zero.
 // The rotary step of the routing kernel (RouteRope), per round of items
 // [j0, j0 + cnt) of a workgroup: all its threads turn the items' query rows
 // into q_out and append each item's key (turned) and value row at pos, each
@@ -119,6 +112,15 @@ __device__ inline void rope_round(const RouteRope& rr, const double* s_c, const 
     __syncthreads();
 }
 
+// The decision step for a whole layer.  Item-major: each aligned 16-lane
+// group scores every head of one item at a time (shared arithmetic in
+// routing.h) and writes its flag; the workgroups stride over the items.
+// Then one workgroup partitions the flags: the only workgroup of a
+// one-workgroup launch (its flags stay in LDS), else the one that draws the
+// last ticket (when `ticket` is given; a partition launch follows otherwise).
+// The ticket starts at zero and is left at zero.  Without a work list the
+// flags are the whole output (a decode launch that takes its decisions from
+// them partitions the items itself).
 template <int NT>
 __global__ __launch_bounds__(NT) void k_route(
     const float* __restrict__ q, const float* __restrict__ k0, float tau,
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(NT) void k_route(
             flags[j] = sink ? 1 : 0;
             s_flag[j] = sink ? 1 : 0;
         }
-        partition_flags<NT>(s_flag, n_items, work_list, n_active);
+        if (work_list) partition_flags<NT>(s_flag, n_items, work_list, n_active);
         return;
     }
     const int32_t stride = static_cast<int32_t>(gridDim.x) * ipw;
@@ -238,7 +240,9 @@ hipError_t launch_route(const sr_shape& s, const float* q, const float* k0, floa
     const int32_t grid = want < kRouteMaxWgs ? want : kRouteMaxWgs;
     hipLaunchKernelGGL(k_route<NT>, dim3(grid), dim3(NT), 0, st, q, k0, tau, scores, flags,
                        work_list, n_active, ticket, n_items, G, s.head_dim, s.num_kv_heads, rope);
-    if (ticket || grid == 1) return hipGetLastError();
+    // flags only (no list asked for: the decode partitions), or partitioned
+    // already by the last workgroup or the only one
+    if (!work_list || ticket || grid == 1) return hipGetLastError();
     // one tile of 4 flags per thread: 256 threads up to 1024 groups, 1024 above
     if (n_items <= 4 * 256)
         hipLaunchKernelGGL(k_partition<256>, dim3(1), dim3(256), 0, st, flags, work_list,

@@ -413,9 +413,14 @@ __device__ inline bool map_work(const DecodeArgs& a, WorkRange& r) {
         double *s_c = nullptr, *s_s = nullptr;
         if (a.rope) r.q = rope_queries<D, NT>(a, s_c, s_s);
         const uint64_t all = n_items >= 64 ? ~0ull : ((1ull << n_items) - 1);
-        const uint64_t sinks =
-            fused_sink_mask<NT, 4>(r.q, a.k0, a.tau, n_items, G, D, s_pass,
-                                   w0 ? a.scores_out : nullptr) & all;
+        uint64_t sinks;
+        if (a.flags_in) {  // decided by the routing kernel: every wave ballots the flags
+            const int lane = threadIdx.x & 63;
+            sinks = __ballot(lane < n_items && a.flags_in[lane] != 0) & all;
+        } else {
+            sinks = fused_sink_mask<NT, 4>(r.q, a.k0, a.tau, n_items, G, D, s_pass,
+                                           w0 ? a.scores_out : nullptr) & all;
+        }
         const uint64_t act = all & ~sinks;
         n_act = uniform(__popcll(act));
         plan_range(n_act);

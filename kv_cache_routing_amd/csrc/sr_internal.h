@@ -39,6 +39,10 @@ struct DecodeArgs {
     uint8_t* mask_out;         // [B][Hkv]  (fused, optional)
     int32_t* list_out;         // [B*Hkv]   (fused, optional)
     int32_t* n_active_out;     // [1]       (fused, optional)
+    // Fused, from flags: the routing kernel scored every group and wrote one
+    // flag byte per item (B*Hkv <= 64); the decode workgroups take the
+    // decisions from there instead of scoring (flags_in == nullptr: score).
+    const uint8_t* flags_in;
     float* alpha0_out;         // [B][Hq] weight of position 0 per head (optional)
     // Fused rotary + append (sr_rope_route_decode, fused routing only): q is
     // the unrotated new query; every workgroup rotates all queries to
