@@ -50,6 +50,27 @@ def scratch_kernels(remarks: str) -> list:
     return bad
 
 
+# LDS per workgroup on gfx950, and the most dynamic LDS a decode launch adds
+# (the fused rotary step: cos/sin of d/2 = 64 angles in fp64 and the rotated
+# queries of 64 heads of d = 128 in fp32, rope_lds_bytes in sr_internal.h).
+LDS_LIMIT = 160 * 1024
+ROPE_LDS_MAX = 64 * 2 * 8 + 64 * 128 * 4
+
+
+def lds_overflows(remarks: str) -> list:
+    """Decode kernels whose static LDS plus the largest dynamic LDS of a fused
+    rotary launch would not fit a workgroup: such a launch would fail."""
+    bad, name = [], None
+    for ln in remarks.splitlines():
+        if "Function Name:" in ln:
+            name = ln.split("Function Name:")[1].split("[")[0].strip()
+        elif "LDS Size [bytes/block]:" in ln and name and "k_decode" in name:
+            n = int(ln.split("LDS Size [bytes/block]:")[1].split("[")[0])
+            if n + ROPE_LDS_MAX > LDS_LIMIT:
+                bad.append(f"{name} ({n} + {ROPE_LDS_MAX} bytes)")
+    return bad
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
@@ -63,6 +84,10 @@ def _compile(src: str) -> str:
     bad = scratch_kernels(r.stderr or "")
     if bad:
         raise RuntimeError(f"{src}: kernels use scratch memory: " + "; ".join(bad))
+    bad = lds_overflows(r.stderr or "")
+    if bad:
+        raise RuntimeError(f"{src}: LDS over {LDS_LIMIT} bytes with the rotary step: "
+                           + "; ".join(bad))
     noise, in_remark = [], False
     for ln in (r.stderr or "").splitlines():
         if "remark:" in ln:  # the resource report and the source lines it quotes

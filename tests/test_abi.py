@@ -356,3 +356,28 @@ def test_build_rejects_kernels_with_scratch():
     ])
     assert scratch_kernels(report) == ["k_spills (96 bytes/lane)"]
     assert scratch_kernels("") == []
+
+
+def test_build_checks_lds_for_the_rotary_step():
+    from kv_cache_routing_amd.build import LDS_LIMIT, ROPE_LDS_MAX, lds_overflows
+    fits = LDS_LIMIT - ROPE_LDS_MAX
+    report = "\n".join([
+        "a.hip:1:1: remark: Function Name: k_decode_mfma_a [-Rpass-analysis=kernel-resource-usage]",
+        f"a.hip:1:1: remark:     LDS Size [bytes/block]: {fits} [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark: Function Name: k_decode_mfma_b [-Rpass-analysis=kernel-resource-usage]",
+        f"a.hip:9:1: remark:     LDS Size [bytes/block]: {fits + 1} [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark: Function Name: k_route [-Rpass-analysis=kernel-resource-usage]",
+        f"a.hip:9:1: remark:     LDS Size [bytes/block]: {LDS_LIMIT} [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert [b.split(" ")[0] for b in lds_overflows(report)] == ["k_decode_mfma_b"]
+
+
+def test_build_lds_bound_follows_the_fused_head_limit():
+    # the build's dynamic-LDS bound is rope_lds_bytes at the largest fused
+    # launch: kMaxFusedHeads query rows of the largest head size (128)
+    from kv_cache_routing_amd.build import CSRC, ROPE_LDS_MAX
+    src = open(os.path.join(CSRC, "sr_internal.h")).read()
+    heads = int(re.search(r"kMaxFusedHeads\s*=\s*(\d+)", src).group(1))
+    assert "static_cast<size_t>(d / 2) * 2 * sizeof(double)" in src
+    assert "static_cast<size_t>(q_rows) * d * sizeof(float)" in src
+    assert ROPE_LDS_MAX == 128 // 2 * 2 * 8 + heads * 128 * 4
