@@ -20,7 +20,7 @@ Sources (the method is described on these pages):
     sum of the cached values; the Figure 10 caption scores the routing proxy
     as cos(q, K_BOS) at the KV-group level.
 
-Readings where the pages are silent (each is listed in the design doc too):
+Readings where the pages are silent:
   * a group is a sink only when every one of its query heads scores >= tau;
   * a zero-norm query or key scores 0 (so the group stays active);
   * query head h reads KV head h // G (the Hugging Face repeat_kv layout);

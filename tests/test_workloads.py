@@ -5,8 +5,9 @@ import pytest
 import torch
 
 import oracle
-from workloads import (CONFIGS, L8B_512K, SINK_FRACTIONS, TINY, as_numpy, make_caches, make_k0,
-                       make_layer, make_queries, planted_sinks, sweep)
+from workloads import (CONFIGS, L8B_128K, L8B_256K_B4, L8B_512K, L70B_128K_B8, SINK_FRACTIONS,
+                       TINY, as_numpy, make_caches, make_k0, make_layer, make_queries,
+                       planted_sinks, sweep)
 
 MARGIN = 0.05
 
@@ -29,7 +30,7 @@ def test_margin_and_planted_mask_match_oracle(wl):
 
 @pytest.mark.parametrize("f", SINK_FRACTIONS)
 def test_sweep_margins_and_counts(f):
-    for base in (L8B_512K, CONFIGS[2]):
+    for base in (L8B_512K, L8B_256K_B4):
         wl = sweep(base, f)
         q, planted = make_queries(wl)
         assert (planted.sum(dim=1) == round(f * wl.num_kv_heads)).all()
@@ -47,7 +48,7 @@ def test_tiny_is_the_stated_layer():
 
 
 def test_reproducible_and_thread_count_independent():
-    wl = CONFIGS[1].with_(seq_len=3000)
+    wl = L8B_128K.with_(seq_len=3000)
     k1, v1 = make_caches(wl, threads=1)
     k2, v2 = make_caches(wl, threads=7)
     assert torch.equal(k1, k2) and torch.equal(v1, v2)
@@ -60,14 +61,14 @@ def test_reproducible_and_thread_count_independent():
 
 
 def test_bernoulli_plan_varies_per_item():
-    p = planted_sinks(CONFIGS[4])
+    p = planted_sinks(L70B_128K_B8)
     assert p.shape == (8, 8)
     assert 0 < int(p.sum()) < 64
     assert len({tuple(r.tolist()) for r in p}) > 1
 
 
 def test_cache_entries_look_standard_normal():
-    wl = CONFIGS[1].with_(seq_len=20000)
+    wl = L8B_128K.with_(seq_len=20000)
     k, v = make_caches(wl)
     vv = v.float()
     assert abs(vv.mean().item()) < 5e-3 and abs(vv.std().item() - 1.0) < 5e-3
