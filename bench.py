@@ -541,9 +541,46 @@ def decode_layers_report(sr, torch, args):
     return 0
 
 
+# --- routing proxy against position-0 attention mass (evaluation only) -------
+# The pith.science rendering of arXiv 2604.16883 (Figure 10 caption) scores
+# cos(q, K_BOS) as a predictor of an "oracle" sink event defined from the
+# full-attention weight of the first position, per KV group, across the
+# threshold tau.  Predictions here are the HIP routing mask at each tau;
+# events come from the HIP dense decode's alpha_0.  Reading for the event
+# threshold, which the pages do not print: a group is an event when every
+# one of its heads puts at least `event_mass` of its attention on position 0.
+def sink_events(alpha0, num_kv_heads: int, event_mass: float):
+    """[B][Hkv] bool tensor: every head of the group has alpha_0 >= event_mass."""
+    B, Hq = alpha0.shape
+    return (alpha0 >= event_mass).view(B, num_kv_heads, Hq // num_kv_heads).all(dim=-1)
+
+
+def precision_recall(predicted, events):
+    """(precision, recall, F1); precision is 1 when nothing is predicted,
+    recall 1 when there is no event, F1 0 when both are 0."""
+    p = predicted.reshape(-1).bool()
+    e = events.reshape(-1).bool()
+    tp = int((p & e).sum())
+    fp = int((p & ~e).sum())
+    fn = int((~p & e).sum())
+    prec = tp / (tp + fp) if tp + fp else 1.0
+    rec = tp / (tp + fn) if tp + fn else 1.0
+    f1 = 2 * prec * rec / (prec + rec) if prec + rec else 0.0
+    return prec, rec, f1
+
+
+def proxy_sweep(predict, events, taus):
+    """Precision / recall / F1 of the routing decision at every tau;
+    predict(tau) returns the [B][Hkv] sink mask."""
+    rows = []
+    for tau in taus:
+        p, r, f = precision_recall(predict(float(tau)), events)
+        rows.append({"tau": float(tau), "precision": p, "recall": r, "f1": f})
+    return rows
+
+
 def bos_proxy_report(sr, torch):
-    """Routing proxy vs position-0 attention mass, GPU outputs only."""
-    from kv_cache_routing_amd import proxy
+    """Routing proxy vs position-0 attention mass, from GPU outputs only."""
     from workloads import L8B_128K, make_layer
     dev = torch.device("cuda:0")
     taus = [round(0.05 * i, 2) for i in range(21)]
@@ -554,15 +591,17 @@ def bos_proxy_report(sr, torch):
         layer = make_layer(wl)
         q, k, v = layer.q.to(dev), layer.k.to(dev), layer.v.to(dev)
         k0, _ = sr.record_sink(k, v)
-        r = sr.route(q, k0, wl.tau)
         _, a0 = sr.dense_decode_alpha0(q, k, v)
         torch.cuda.synchronize()
-        ev = proxy.sink_events(a0, wl.num_kv_heads, 0.5)
+        ev = sink_events(a0, wl.num_kv_heads, 0.5)
+
+        def predict(tau, q=q, k0=k0):
+            return sr.route(q, k0, tau).mask.bool()
         report.append({"layer": wl.name, "planted_sinks": int(layer.planted.sum()),
                        "events": int(ev.sum()), "groups": wl.batch * wl.num_kv_heads,
                        "alpha0_planted_mean": float(a0.view(wl.batch, wl.num_kv_heads, -1)[
                            layer.planted.to(dev)].mean()),
-                       "sweep": proxy.threshold_sweep(r.scores, a0, wl.num_kv_heads, taus, 0.5)})
+                       "sweep": proxy_sweep(predict, ev, taus)})
         log(f"bos proxy {wl.name}: events {int(ev.sum())}")
     print(json.dumps({"bos_proxy": report}), flush=True)
     return 0

@@ -246,9 +246,13 @@ sr_status sr_rope_route_decode(const sr_shape* shape, const sr_launch* launch,
                                int32_t* n_active, void* ws, size_t ws_bytes, float* out,
                                void* stream);
 
-/* Dense baseline: the decode kernel of sr_decode_attn with routing off
- * (identity work list, every item active).  sr_decode_attn with a work list
- * routed at tau > 1 gives the same bits for the same launch policy. */
+/* Dense baseline (README efficiency-benchmark section: the decode latency of
+ * the unmodified model, which SinkRouter's speedup is measured against; the
+ * paper's Eq. (1) over every group): the decode kernel of sr_decode_attn with
+ * routing off (identity work list, every item active).  sr_decode_attn with
+ * a work list routed at tau > 1 gives the same bits for the same launch
+ * policy.  Arguments, layout, ownership and errors as sr_decode_attn, without
+ * v0, work_list and n_active. */
 sr_status sr_dense_decode(const sr_shape* shape, const sr_launch* launch, const float* q,
                           const void* k_cache, const void* v_cache, float sm_scale,
                           void* ws, size_t ws_bytes, float* out, void* stream);
@@ -263,8 +267,15 @@ sr_status sr_dense_decode_alpha0(const sr_shape* shape, const sr_launch* launch,
                                  const void* k_cache, const void* v_cache, float sm_scale, void* ws,
                                  size_t ws_bytes, float* out, float* alpha0, void* stream);
 
-/* Lanes per active item (S) the decode kernel will use for a given n_active
- * under this policy (what the adaptive mode derives on the device). */
+/* Split count.  The pages show the split count only as a launch knob (the
+ * README's routing controls give 32 splits as an example at 524288
+ * positions).  Here it is not one number per shape: the adaptive policy
+ * (sr_launch.num_splits = 0) derives it on the device from n_active, so there
+ * is no default-split call; these two calls report what a launch will do.
+ *
+ * Lanes per active item (S) the decode kernel will use for a given n_active
+ * under this policy (what the adaptive mode derives on the device); 0 for an
+ * invalid shape or policy. */
 int32_t sr_splits_for(const sr_shape* shape, const sr_launch* launch, int32_t n_active);
 
 /* One workgroup's part of one item, as the decode kernel divides the work. */
@@ -288,7 +299,8 @@ typedef struct {
 int32_t sr_plan_parts(const sr_shape* shape, const sr_launch* launch, int32_t n_active, int32_t wg,
                       sr_part* parts, int32_t max_parts);
 
-/* Workgroups the decode kernel launches under this policy. */
+/* Workgroups the decode kernel launches under this policy (0 for an invalid
+ * shape or policy). */
 int32_t sr_grid_size(const sr_shape* shape, const sr_launch* launch);
 
 const char* sr_status_string(sr_status status);

@@ -84,7 +84,7 @@ __device__ inline float wave_max(float x) {
 // The walk keeps pos, the first cache position of the current chunk; within
 // a lane it advances by step = S * chunk positions and is recomputed only at
 // a lane change.  A finished walk points at `past` (>= T), where every row a
-// prefetch asks for clamps to the last cached row.  Steps are 32-bit
+// prefetch asks for clamps to one cached row (WorkUnit::clamp).  Steps are 32-bit
 // (C < 2^31), so the walk stays in scalar registers (the scalar unit has no
 // 64-bit ordered compare).
 struct ChunkWalk {
@@ -145,6 +145,7 @@ struct WorkUnit {
     int32_t base;   // partial slot of the item's first part
     int32_t mine;   // partial slot of this part
     int64_t t1;     // positions [0, t1) exist (t1 = T)
+    int64_t clamp;  // the row a prefetch of a position >= T reads instead
     ChunkWalk walk;
 };
 
@@ -192,6 +193,11 @@ __device__ inline WorkUnit part_of(const DecodeArgs& a, const WorkRange& r, int3
     u.g = item - u.b * a.num_kv_heads;
     u.mine = r.w + i;
     u.t1 = a.seq_len;
+    // A prefetch past the end reads one real row and discards it.  With the
+    // rotary step fused, row T - 1 is written in this launch by the workgroup
+    // that owns it, so the others must not read it: they take row T - 2
+    // (T >= 2 there), which no workgroup writes.
+    u.clamp = a.rope ? a.seq_len - 2 : a.seq_len - 1;
     if (!p.balanced) {  // all of lane r.lane: no division needed
         u.parts = p.S;
         u.base = i * p.S + i;
@@ -223,8 +229,8 @@ __device__ inline WorkUnit part_of(const DecodeArgs& a, const WorkRange& r, int3
 // Two-stage register pipeline over a walk: the next tile's loads are in
 // flight while the current tile is computed, also across the lanes of the
 // walk.  This wave's tile of a chunk starts at pos + wave * WT.  issue() must
-// clamp rows past T: the prefetch after the last tile asks for rows at or
-// past T, which costs one row.
+// clamp rows past T to WorkUnit::clamp: the prefetch after the last tile asks
+// for rows at or past T, which costs one row.
 template <int WT, typename Raw, typename Issue, typename Compute>
 __device__ inline void stream_walk(ChunkWalk w, int wave, Raw& ra, Raw& rb, Issue issue,
                                    Compute compute) {

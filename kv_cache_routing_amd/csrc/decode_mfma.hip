@@ -145,9 +145,9 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
         struct Raw {
             Tile16 t[SUB];
         };
-        const int64_t last = u.t1 - 1;
-        // Positions past T are clamped to the last row: every lane then reads the
-        // same row, so a prefetch past the end costs one row and no branch.
+        const int64_t last = u.clamp;
+        // Positions past T are clamped to one row (u.clamp): every lane then reads
+        // the same row, so a prefetch past the end costs one row and no branch.
         auto issue16 = [&](Tile16& r, int64_t tile) {
             int64_t tk = tile + col;
             tk = tk < u.t1 ? tk : last;
@@ -432,9 +432,9 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma_f32(DecodeArgs a) {
             uint4 k[KD / 4];      // key row tile + col, elements 16*j + 4*grp ..
             uint4 v[4][DV / 4];   // value rows tile + 4*grp + kq, elements 4*col + 64*h ..
         };
-        const int64_t last = u.t1 - 1;
-        // Rows past T are clamped to the last row: a prefetch past the end costs
-        // one row and no branch.
+        const int64_t last = u.clamp;
+        // Rows past T are clamped to one row (u.clamp): a prefetch past the end
+        // costs one row and no branch.
         auto issue = [&](Raw& r, int64_t tile) {
             int64_t tk = tile + col;
             tk = tk < u.t1 ? tk : last;

@@ -147,9 +147,9 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
             typename Slice::T k[U][Slice::W];
             typename Slice::T v[U][Slice::W];
         };
-        const int64_t last = u.t1 - 1;
-        // Rows past T are clamped to the last row: every lane then reads the same
-        // row, so a prefetch past the end costs one row and no branch.
+        const int64_t last = u.clamp;
+        // Rows past T are clamped to one row (u.clamp): every lane then reads the
+        // same row, so a prefetch past the end costs one row and no branch.
         auto issue = [&](Raw& r, int64_t tile) {
 #pragma unroll
             for (int v = 0; v < U; ++v) {

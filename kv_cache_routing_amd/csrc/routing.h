@@ -439,9 +439,10 @@ __device__ inline bool map_work(const DecodeArgs& a, WorkRange& r) {
         if (a.rope) {
             // Row T - 1 of every item is written by exactly one workgroup:
             // for a sink, the one that copies its v0 rows; for an active
-            // item, the one whose part holds the chunk with T - 1 (the only
-            // reader of that row in this launch).  It writes before it
-            // streams, and its own loads then see the row.
+            // item, the one whose part holds the chunk with T - 1, the only
+            // workgroup that reads that row in this launch (the other parts'
+            // prefetches past the end read row T - 2 instead: WorkUnit::clamp).
+            // It writes before it streams, and its own loads then see the row.
             const SplitPlan& p = r.plan;
             const int32_t c = static_cast<int32_t>((a.seq_len - 1) / CHUNK);
             const int32_t l = c % p.S, k = c / p.S;  // lane and step of that chunk

@@ -8,6 +8,6 @@ from .sinkrouter import (  # noqa: F401
     attend_group, bos_mass, cosine, default_scale, dense_decode, group_mask, merge_partials,
     oracle_sink_events, proxy_precision_recall, record_sink, rope, rope_append, round_bf16,
     route, route_scores,
-    routed_decode, routed_decode_items, split_k_decode, split_partials, threshold_sweep,
+    routed_decode, split_k_decode, split_partials, threshold_sweep,
     work_list,
 )

@@ -199,26 +199,6 @@ def routed_decode(q, k_cache, v_cache, v0, mask, scale: float | None = None):
     return out
 
 
-def routed_decode_items(q, k_cache, v_cache, v0, mask, items, scale: float | None = None):
-    """Routed output for the listed items j = b*Hkv + g only: {j: [G][d]}.
-
-    Used to check sampled outputs of very large layers item by item."""
-    q = np.asarray(q)
-    B, Hq, d = q.shape
-    Hkv = np.asarray(k_cache).shape[1]
-    G = Hq // Hkv
-    s = default_scale(d) if scale is None else scale
-    res = {}
-    for j in items:
-        b, g = divmod(int(j), Hkv)
-        rows = slice(g * G, (g + 1) * G)
-        if mask is not None and mask[b, g]:
-            res[int(j)] = np.repeat(_f64(v0[b, g])[None, :], G, axis=0)
-        else:
-            res[int(j)] = attend_group(q[b, rows], k_cache[b, g], v_cache[b, g], s)
-    return res
-
-
 # ---------------------------------------------------------------------------
 # Split-K algebra (README decode-time steps: the context is split across
 # programs and the pieces are merged inside the kernel).  Used only to show the result does not depend on S;

@@ -4,7 +4,7 @@ Every test draws its layer from the seeded generator, runs record -> route ->
 decode on cuda:0 and checks: routing mask and work list bit-exact, sink rows
 bit-exact v0, active rows within max-abs 1e-2 / mean-abs 1e-3 / per-row
 rel-L2 1e-3 of the oracle (plus a tighter 2e-4 precision check).
-Small layers are checked in full; the full-size layers on sampled items.
+Small layers are checked in full, and so is every group of the full-size layers.
 """
 import functools
 import math
@@ -94,6 +94,25 @@ REDUCED = [
 def test_reduced_layers(wl, kernel):
     log(f"reduced {wl.name} kernel={kernel}")
     full_check(make_layer(wl), launch(kernel))
+
+
+# The paper's operating threshold (pith.science, Figure 10 caption: tau =
+# 0.55) on the reduced layers: both kernels, two calls against the oracle,
+# and the one-call form bitwise equal to them.
+@pytest.mark.parametrize("wl", REDUCED, ids=lambda w: w.name)
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_reduced_layers_at_tau_055(wl, kernel):
+    log(f"reduced {wl.name} kernel={kernel} tau=0.55")
+    layer = make_layer(wl)
+    lau = launch(kernel)
+    got = full_check(layer, lau, tau=0.55, check_dense=False)
+    q, k, v = upload(layer)
+    k0, v0 = sr.record_sink(k, v)
+    fused, rf = sr.route_decode(q, k, v, k0, v0, 0.55, launch=lau)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.cpu(), torch.from_numpy(got))
+    q_np, k_np, v_np = oracle_inputs(layer)
+    assert_route(rf, q_np, oracle.record_sink(k_np, v_np)[0], 0.55)
 
 
 # Groups of 8 and 16 heads take the PV product on the matrix cores (keys as
@@ -242,52 +261,99 @@ def test_strided_cache_views(wl, kernel):
     v = big_v.cuda()[:, :, :T]
     q = layer.q.cuda()
     k0, v0, r, out = run_routed(q, k, v, wl.tau, launch(kernel))
+    torch.cuda.synchronize()
     q_np, k_np, v_np = oracle_inputs(layer)
-    mask = r.mask.cpu().numpy()
-    ref = oracle.routed_decode(q_np, k_np, v_np, as_numpy(layer.v[:, :, 0]), mask)
-    assert_outputs(out.cpu().numpy(), ref, f"strided routed {kernel}")
+    # every reference from the oracle on the unpadded host arrays
+    k0_ref, v0_ref = oracle.record_sink(k_np, v_np)
+    assert np.array_equal(k0.cpu().numpy(), k0_ref) and np.array_equal(v0.cpu().numpy(), v0_ref)
+    mask, n_active = assert_route(r, q_np, k0_ref, wl.tau)
+    assert 0 < n_active < wl.batch * wl.num_kv_heads
+    got = out.cpu().numpy()
+    sink_rows_exact(got, v0_ref, mask, wl.group_size)
+    ref = oracle.routed_decode(q_np, k_np, v_np, v0_ref, mask)
+    act = np.repeat(mask == 0, wl.group_size, axis=1)
+    assert_outputs(got[act], ref[act], f"strided routed {kernel}")
+    dense = sr.dense_decode(q, k, v, launch=launch(kernel)).cpu().numpy()
+    assert_outputs(dense, oracle.dense_decode(q_np, k_np, v_np), f"strided dense {kernel}")
 
 
-# --- full-size layers, sampled outputs ----------------------------------------
-def sampled_check(layer, q, k, v, lau, n_samples=2, seed=0):
+# --- full-size layers, every item --------------------------------------------
+# The oracle finishes a whole routed layer-step of these layers in about a
+# second, so every active group is compared with it (and every group of the
+# dense path), not a sample.
+def _item_refs(layer, items):
+    """Oracle attention of the listed items j = b*Hkv + g: {j: [G][d]}."""
     wl = layer.wl
     G = wl.group_size
-    k0, v0, r, out = run_routed(q, k, v, wl.tau, lau)
-    torch.cuda.synchronize()
     q_np = as_numpy(layer.q)
-    k0_ref = as_numpy(layer.k[:, :, 0])
-    v0_ref = as_numpy(layer.v[:, :, 0])
-    mask, n_active = assert_route(r, q_np, k0_ref, wl.tau)
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    refs = {}
+    for j in items:
+        b, g = divmod(int(j), wl.num_kv_heads)
+        refs[int(j)] = oracle.attend_group(q_np[b, g * G:(g + 1) * G], as_numpy(layer.k[b, g]),
+                                           as_numpy(layer.v[b, g]), scale)
+    return refs
+
+
+def _check_items(got, refs, wl, what):
+    G = wl.group_size
+    rows_got, rows_ref = [], []
+    for j, ref in sorted(refs.items()):
+        b, g = divmod(j, wl.num_kv_heads)
+        rows_got.append(got[b, g * G:(g + 1) * G])
+        rows_ref.append(ref)
+    if rows_got:
+        assert_outputs(np.concatenate(rows_got), np.concatenate(rows_ref),
+                       f"{what}: {len(refs)} groups")
+
+
+def full_size_check(layer, q, k, v, lau, tau, check_dense=True):
+    """Two calls and the one-call form on a full-size layer: routing bit-exact
+    against the oracle, the two forms bitwise equal, sink rows exactly v0,
+    every active group (and, with check_dense, every group of the dense
+    path) against the oracle."""
+    wl = layer.wl
+    G = wl.group_size
+    k0, v0, r, out = run_routed(q, k, v, tau, lau)
+    out1, rf = sr.route_decode(q, k, v, k0, v0, tau, launch=lau)
+    torch.cuda.synchronize()
+    k0_ref = as_numpy(layer.k[:, :, 0]).astype(np.float64)
+    v0_ref = as_numpy(layer.v[:, :, 0]).astype(np.float64)
+    assert np.array_equal(k0.cpu().numpy(), k0_ref) and np.array_equal(v0.cpu().numpy(), v0_ref)
+    mask, n_active = assert_route(r, as_numpy(layer.q), k0_ref, tau)
+    for name in ("scores", "mask", "work_list", "n_active"):
+        assert torch.equal(getattr(rf, name), getattr(r, name)), name
+    assert torch.equal(out1, out), "one-call form differs from two calls"
     got = out.cpu().numpy()
     n_sink = sink_rows_exact(got, v0_ref, mask, G)
-    act = [j for j in r.work_list.cpu().numpy()[:n_active]]
-    rng = np.random.default_rng(seed)
-    picks = sorted(set([act[0], act[-1]] + list(rng.choice(act, size=min(n_samples, len(act)),
-                                                           replace=False)))) if act else []
-    scale = 1.0 / math.sqrt(wl.head_dim)
-    log(f"{wl.name}: n_active={n_active} sink_rows={n_sink} sampled items={picks}")
-    for j in picks:
-        b, g = divmod(int(j), wl.num_kv_heads)
-        ref = oracle.attend_group(q_np[b, g * G:(g + 1) * G], as_numpy(layer.k[b, g]),
-                                  as_numpy(layer.v[b, g]), scale)
-        assert_outputs(got[b, g * G:(g + 1) * G], ref, f"item {j}")
+    active = [int(j) for j in r.work_list.cpu().numpy()[:n_active]]
+    log(f"{wl.name} tau={tau}: n_active={n_active} sink_rows={n_sink}")
+    refs = _item_refs(layer, active)
+    _check_items(got, refs, wl, f"{wl.name} routed")
+    if check_dense:
+        dense = sr.dense_decode(q, k, v, launch=lau).cpu().numpy()
+        rest = [j for j in range(wl.batch * wl.num_kv_heads) if j not in refs]
+        refs.update(_item_refs(layer, rest))
+        _check_items(dense, refs, wl, f"{wl.name} dense")
     return r
 
 
 @pytest.mark.parametrize("wl", [L8B_128K, L8B_512K, L70B_128K_B8], ids=lambda w: w.name)
-@pytest.mark.parametrize("kernel", ["auto"])
-def test_full_size_layers_sampled(wl, kernel):
+def test_full_size_layers_every_item(wl):
     log(f"full-size {wl.name}")
     layer = make_layer(wl)
     q, k, v = upload(layer)
-    sampled_check(layer, q, k, v, launch(kernel))
-    # dense path on one sampled item
-    dense = sr.dense_decode(q, k, v, launch=launch(kernel)).cpu().numpy()
-    G = wl.group_size
-    b, g = wl.batch - 1, wl.num_kv_heads - 1
-    ref = oracle.attend_group(as_numpy(layer.q)[b, g * G:(g + 1) * G], as_numpy(layer.k[b, g]),
-                              as_numpy(layer.v[b, g]), 1.0 / math.sqrt(wl.head_dim))
-    assert_outputs(dense[b, g * G:(g + 1) * G], ref, "dense last item")
+    full_size_check(layer, q, k, v, launch("auto"), wl.tau)
+
+
+# The paper's operating threshold (pith.science, Figure 10 caption: tau =
+# 0.55) on the full 128K layer, both decode kernels, both call forms.
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_full_size_128k_at_tau_055(kernel):
+    layer = make_layer(L8B_128K)
+    q, k, v = upload(layer)
+    r = full_size_check(layer, q, k, v, launch(kernel), 0.55, check_dense=False)
+    assert int(r.n_active.cpu()[0]) == 4
 
 
 def test_full_size_256k_b4_sink_fraction_sweep():
@@ -295,12 +361,13 @@ def test_full_size_256k_b4_sink_fraction_sweep():
     log(f"full-size {base.name} sweep")
     k_cpu, v_cpu = make_caches(base)
     k, v = k_cpu.cuda(), v_cpu.cuda()
-    for f in SINK_FRACTIONS:
+    from workloads import Layer
+    for i, f in enumerate(SINK_FRACTIONS):
         wl = sweep(base, f)
         q_cpu, planted = make_queries(wl)
-        from workloads import Layer
         layer = Layer(wl, q_cpu, k_cpu, v_cpu, planted)
-        r = sampled_check(layer, q_cpu.cuda(), k, v, launch("auto"), n_samples=1, seed=int(f * 4))
+        r = full_size_check(layer, q_cpu.cuda(), k, v, launch("auto"), wl.tau,
+                            check_dense=i == 0)
         assert int(r.n_active.cpu()[0]) == round((1 - f) * 8) * 4
 
 
@@ -357,27 +424,6 @@ def test_fused_edges_all_sinks_no_sinks_and_repeats():
         assert torch.equal(again, first)
     torch.cuda.synchronize()
     assert int(ticket_region(ws, 8).abs().sum()) == 0
-
-
-def test_fused_full_size_70b_layer_sampled():
-    wl = L70B_128K_B8
-    layer = make_layer(wl)
-    q, k, v = upload(layer)
-    k0, v0 = sr.record_sink(k, v)
-    out, r = sr.route_decode(q, k, v, k0, v0, wl.tau)
-    r2 = sr.route(q, k0, wl.tau)
-    out2 = sr.decode_attn(q, k, v, v0, r2.work_list, r2.n_active)
-    torch.cuda.synchronize()
-    assert torch.equal(r.mask, r2.mask) and torch.equal(r.work_list, r2.work_list)
-    assert torch.equal(out, out2)
-    G = wl.group_size
-    q_np = as_numpy(layer.q)
-    n_act = int(r.n_active.cpu()[0])
-    j = int(r.work_list.cpu()[n_act // 2])
-    b, g = divmod(j, wl.num_kv_heads)
-    ref = oracle.attend_group(q_np[b, g * G:(g + 1) * G], as_numpy(layer.k[b, g]),
-                              as_numpy(layer.v[b, g]), 1.0 / math.sqrt(wl.head_dim))
-    assert_outputs(out.cpu().numpy()[b, g * G:(g + 1) * G], ref, f"fused 70b item {j}")
 
 
 # --- sr_route_decode picks one launch (<= 64 query heads) or two ----------------
@@ -730,15 +776,17 @@ def test_decode_steps_with_append_match_oracle():
         out, r = sr.route_decode(q_rot, kd[:, :, :T], vd[:, :, :T], k0, v0, 0.5)
         q_ref, k_np, v_np = oracle.rope_append(qn.numpy(), kn.numpy(), vn.numpy(), k_np, v_np,
                                                pos, f.numpy(), bf16=True)
-        # the device appended key may differ from the oracle's by one bf16 ulp:
-        # attend with the device's stored cache, compare rotation separately
+        # the device's rotation and append within their bounds (its appended
+        # key may differ from the oracle's by one bf16 ulp) ...
         k_dev = as_numpy(kd.cpu()).astype(np.float64)
         assert (np.abs(k_dev[:, :, pos] - k_np[:, :, pos]) <= _bf16_ulp(k_np[:, :, pos])).all()
+        assert np.array_equal(as_numpy(vd.cpu()).astype(np.float64)[:, :, pos], v_np[:, :, pos])
         q_dev = q_rot.cpu().numpy().astype(np.float64)
-        assert np.abs(q_dev - q_ref).max() <= 1e-5
-        _, mask, wl_ref, n_act = oracle.route(q_dev, k_dev[:, :, 0], 0.5)
-        assert np.array_equal(r.mask.cpu().numpy(), mask)
-        ref = oracle.routed_decode(q_dev, k_dev[:, :, :T], v_np[:, :, :T], v_np[:, :, 0], mask)
+        assert (np.abs(q_dev - q_ref) <= np.abs(q_ref) * 2 ** -23 + 1e-30).all()
+        # ... and the routing and output against the oracle stepping its own
+        # caches, with its own rotated query
+        mask = assert_route(r, q_ref, k_np[:, :, 0], 0.5)[0]
+        ref = oracle.routed_decode(q_ref, k_np[:, :, :T], v_np[:, :, :T], v_np[:, :, 0], mask)
         assert_outputs(out.cpu().numpy(), ref, f"step {step} T={T}")
 
 
@@ -836,12 +884,28 @@ def _rope_step_check(case, planted):
     if name == "8b-lanes":
         assert not balanced and n_active > 0  # found from the workgroup's lane
 
+    # The reference comes from the oracle alone: its own rotation of the new
+    # query and key and its own append (rounded to the cache dtype), then
+    # routing and attention over positions 0 .. T - 1.  The device's rotated
+    # query and appended row are held to their own bounds first.
+    q_ref, k_ref, v_ref = oracle.rope_append(qn.numpy(), kn.numpy(), vn.numpy(), as_numpy(kc),
+                                             as_numpy(vc), pos, f.numpy(), bf16=dtype == "bf16")
+    k_ref, v_ref = k_ref[:, :, :T], v_ref[:, :, :T]
+    q_dev = q_b.cpu().numpy().astype(np.float64)
+    assert (np.abs(q_dev - q_ref) <= np.abs(q_ref) * 2 ** -23 + 1e-30).all(), f"{name}: q_out"
     k_dev = as_numpy(kB[:, :, :T].cpu()).astype(np.float64)
     v_dev = as_numpy(vB[:, :, :T].cpu()).astype(np.float64)
-    q_dev = q_b.cpu().numpy().astype(np.float64)
-    _, mask, _, _ = oracle.route(q_dev, k_dev[:, :, 0], tau)
-    assert np.array_equal(r_b.mask.cpu().numpy(), mask)
-    ref = oracle.routed_decode(q_dev, k_dev, v_dev, v_dev[:, :, 0], mask)
+    ulp = _bf16_ulp(k_ref[:, :, pos]) if dtype == "bf16" else np.abs(k_ref[:, :, pos]) * 2 ** -23
+    assert (np.abs(k_dev[:, :, pos] - k_ref[:, :, pos]) <= ulp + 1e-30).all(), f"{name}: key row"
+    assert np.array_equal(v_dev[:, :, pos], v_ref[:, :, pos]), f"{name}: value row"
+    assert np.array_equal(k_dev[:, :, :pos], k_ref[:, :, :pos]), f"{name}: other key rows"
+    scores, mask, wl_ref, n_ref = oracle.route(q_ref, k_ref[:, :, 0], tau)
+    assert np.abs(scores - tau).min() >= 1e-4, f"{name}: a score within 1e-4 of tau"
+    assert np.array_equal(r_b.mask.cpu().numpy(), mask), f"{name}: mask"
+    assert np.array_equal(r_b.work_list.cpu().numpy(), wl_ref) and n_active == n_ref
+    assert np.abs(r_b.scores.cpu().numpy() - scores).max() <= 2e-5
+    ref = oracle.routed_decode(q_ref, k_ref, v_ref, v_ref[:, :, 0], mask)
+    sink_rows_exact(out_b.cpu().numpy(), v_ref[:, :, 0].astype(np.float32), mask, G)
     assert_outputs(out_b.cpu().numpy(), ref, f"{name} T={T}")
 
 

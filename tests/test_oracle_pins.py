@@ -344,6 +344,71 @@ def test_threshold_tie_counts_as_sink():
     assert orc.group_mask(np.array([[0.5, np.nextafter(0.5, 0.0)]]), 1, 0.5).tolist() == [[0]]
 
 
+# --- oracle sink events (hand-built weights, tests/golden/sink_event_cases.json) --
+def _event_cases():
+    with open(os.path.join(GOLDEN, "sink_event_cases.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _event_cases(), ids=lambda c: c["name"])
+def test_oracle_sink_events_golden(case):
+    a0 = np.array(case["alpha0"], dtype=np.float64)
+    assert a0.shape == (case["batch"], case["num_q_heads"])
+    ev = oracle.oracle_sink_events(a0, case["num_kv_heads"], case["event_mass"])
+    assert ev.dtype == bool and ev.tolist() == case["expect_events"]
+
+
+def test_oracle_sink_events_from_closed_form_weights():
+    # End to end with alpha_0 from the oracle's own softmax, on layers whose
+    # weights are known in closed form: one head of each group aligned with a
+    # norm-400 position-0 key (alpha_0 > 1 - (T-1) e^-delta, near 1), the other
+    # head a zero query (alpha_0 = 1/T exactly).
+    d, T = 32, 64
+    rng = np.random.default_rng(76)
+    k = rng.standard_normal((1, 2, T, d))
+    k[0, :, 0] *= (400.0 / np.linalg.norm(k[0, :, 0], axis=-1))[:, None]
+    q = np.zeros((1, 4, d))
+    q[0, 0] = k[0, 0, 0] / np.linalg.norm(k[0, 0, 0])  # group 0: aligned + zero query
+    q[0, 2] = k[0, 1, 0] / np.linalg.norm(k[0, 1, 0])  # group 1: aligned ...
+    q[0, 3] = k[0, 1, 0] / np.linalg.norm(k[0, 1, 0])  # ... twice
+    a0 = oracle.bos_mass(q, k)
+    assert a0[0, 1] == 1.0 / T and a0[0, 0] > 0.999 and a0[0, 2] > 0.999
+    assert oracle.oracle_sink_events(a0, 2, 0.5).tolist() == [[False, True]]
+    # at a mass below 1/T every head qualifies
+    assert oracle.oracle_sink_events(a0, 2, 1.0 / T).tolist() == [[True, True]]
+
+
+def test_planted_event_mistakes_fail_golden():
+    # Each plausible misreading of the event rule, applied to the golden
+    # weights, must disagree with the stated events somewhere.
+    def rule(combine, cmp, interleaved=False):
+        def events(a0, Hkv, mass):
+            B, Hq = a0.shape
+            G = Hq // Hkv
+            heads = (lambda g: range(g, Hq, Hkv)) if interleaved else \
+                (lambda g: range(g * G, (g + 1) * G))
+            return np.array([[combine([cmp(a0[b, h], mass) for h in heads(g)], a0[b, list(heads(g))], mass)
+                              for g in range(Hkv)] for b in range(B)])
+        return events
+
+    every = lambda flags, vals, mass: all(flags)
+    mutants = {
+        "any head": rule(lambda f, v, m: any(f), lambda x, m: x >= m),
+        "strict >": rule(every, lambda x, m: x > m),
+        "mean of heads": rule(lambda f, v, m: float(np.mean(v)) >= m, lambda x, m: x >= m),
+        "interleaved head map": rule(every, lambda x, m: x >= m, interleaved=True),
+    }
+    exact = rule(every, lambda x, m: x >= m)
+    for name, mut in mutants.items():
+        wrong = 0
+        for case in _event_cases():
+            a0 = np.array(case["alpha0"], dtype=np.float64)
+            args = (a0, case["num_kv_heads"], case["event_mass"])
+            assert exact(*args).tolist() == case["expect_events"]  # the harness itself
+            wrong += mut(*args).tolist() != case["expect_events"]
+        assert wrong, f"mutant '{name}' passes every golden case"
+
+
 # --- position-0 attention mass and the proxy's precision/recall --------------
 def test_bos_mass_against_torch_softmax_weights():
     q, k, v = rand_layer(71, 2, 8, 2, 150, 32, k0_norm=20.0)
