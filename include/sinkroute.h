@@ -40,7 +40,8 @@
  *  library never allocates, frees or keeps them.  `stream` is a hipStream_t
  *  (NULL = the default stream).  Calls only enqueue work: none of them waits
  *  for the device, so results are ready once the stream is synchronised.
- *  The only state the library keeps is the CU count of each device it meets.
+ *  The only state the library keeps is the CU count of each device it meets
+ *  and, for sr_route_decode_static only, one scratch array per device.
  *
  *  Errors: arguments are checked on the host before anything is enqueued, so
  *  a call that returns an error has done nothing.  SR_ERR_UNSUPPORTED means
@@ -215,6 +216,32 @@ sr_status sr_route_decode(const sr_shape* shape, const sr_launch* launch, const 
                           const float* v0, float tau, float sm_scale, float* scores,
                           uint8_t* mask, int32_t* work_list, int32_t* n_active, void* ws,
                           size_t ws_bytes, float* out, void* stream);
+
+/* For callers that cannot allocate device memory or hand over a workspace
+ * (code under HIP graph capture that must not allocate, tight serving loops,
+ * harnesses that forbid hipMalloc): sr_route_decode without the ws / ws_bytes
+ * arguments.  Its scratch (tickets and split partials) is a device array the
+ * library owns, one per GPU, reserved when the library is loaded and held
+ * until the process ends; the call itself allocates nothing.  The first call
+ * on a device looks the array up and clears its ticket region with a small
+ * fill kernel on `stream`; every call leaves the tickets at zero again.
+ *   Limit: shapes whose sr_workspace_bytes(shape, launch) exceeds
+ *   SR_STATIC_SCRATCH_BYTES are rejected with SR_ERR_UNSUPPORTED before
+ *   anything is enqueued.  That size is about (grid + B*Hkv) * GP * (d + 3) * 4
+ *   bytes, GP = G rounded up to a power of two: every Llama-3.1-8B or
+ *   70B-shaped layer of up to 64 KV groups fits at any adaptive grid of up to
+ *   8 workgroups per CU.
+ *   Concurrency: every call on one GPU shares that GPU's array, which keeps
+ *   the last call's contents.  Calls that may overlap on one device (other
+ *   streams, other threads) race and give wrong results; order them.
+ * Otherwise the contract, the arguments and the results are sr_route_decode's,
+ * bit for bit under the same launch policy. */
+#define SR_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+sr_status sr_route_decode_static(const sr_shape* shape, const sr_launch* launch, const float* q,
+                                 const void* k_cache, const void* v_cache, const float* k0,
+                                 const float* v0, float tau, float sm_scale, float* scores,
+                                 uint8_t* mask, int32_t* work_list, int32_t* n_active, float* out,
+                                 void* stream);
 
 /* One decode step of a layer in one call: sr_rope_append of the new token
  * at position T - 1 (T = shape->seq_len, the positions attended after the

@@ -22,7 +22,9 @@ EXPORTS = (
     "sr_decode_attn", "sr_dense_decode", "sr_splits_for", "sr_grid_size",
     "sr_status_string", "sr_version", "sr_stream_read", "sr_route_decode",
     "sr_dense_decode_alpha0", "sr_rope_append", "sr_plan_parts", "sr_rope_route_decode",
+    "sr_route_decode_static",
 )
+SR_STATIC_SCRATCH_BYTES = 16 << 20
 
 
 class SrShape(ctypes.Structure):
@@ -74,6 +76,7 @@ def _load():
         "sr_decode_attn": (i32, [S, Lp, P, P, P, P, P, P, f32, P, sz, P, P]),
         "sr_dense_decode": (i32, [S, Lp, P, P, P, f32, P, sz, P, P]),
         "sr_route_decode": (i32, [S, Lp, P, P, P, P, P, f32, f32, P, P, P, P, P, sz, P, P]),
+        "sr_route_decode_static": (i32, [S, Lp, P, P, P, P, P, f32, f32, P, P, P, P, P, P]),
         "sr_dense_decode_alpha0": (i32, [S, Lp, P, P, P, f32, P, sz, P, P, P]),
         "sr_rope_append": (i32, [S, P, P, P, P, ctypes.c_int64, P, P, P, P]),
         "sr_rope_route_decode": (i32, [S, Lp, P, P, P, P, P, P, P, P, P, f32, f32, P, P, P, P,

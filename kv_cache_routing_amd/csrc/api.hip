@@ -3,6 +3,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "sr_internal.h"
 
@@ -102,6 +103,19 @@ struct WsLayout {
     size_t tickets, ml, acc, route, total;
 };
 
+// Where one decode call keeps its scratch: the per-item tickets and the
+// routing kernel's ticket (zero between calls: every call leaves them at zero),
+// the partials, and the routing list, count and flags of sr_route_decode's
+// two-launch form.
+struct Scratch {
+    uint32_t* tickets;       // [B*Hkv]
+    uint32_t* route_ticket;  // [1]
+    float* part_ml;
+    float* part_acc;
+    int32_t* route_list;     // [B*Hkv + 1]: list, then n_active
+    uint8_t* route_flags;    // [B*Hkv]
+};
+
 WsLayout ws_layout(const sr_shape& s, const Plan& p) {
     const size_t n_items = static_cast<size_t>(s.batch) * s.num_kv_heads;
     WsLayout w;
@@ -116,6 +130,70 @@ WsLayout ws_layout(const sr_shape& s, const Plan& p) {
     w.route = w.acc + align256(parts * p.gp * s.head_dim * sizeof(float));
     w.total = w.route + align256((n_items + 2) * sizeof(int32_t) + n_items);
     return w;
+}
+
+// The caller's workspace: tickets first, then the partials and the routing
+// region [list | n_active | routing ticket | flags].
+Scratch scratch_in_workspace(const sr_shape& s, const WsLayout& w, void* ws) {
+    const size_t n_items = static_cast<size_t>(s.batch) * s.num_kv_heads;
+    char* base = static_cast<char*>(ws);
+    Scratch c;
+    c.tickets = reinterpret_cast<uint32_t*>(base + w.tickets);
+    c.part_ml = reinterpret_cast<float*>(base + w.ml);
+    c.part_acc = reinterpret_cast<float*>(base + w.acc);
+    c.route_list = reinterpret_cast<int32_t*>(base + w.route);
+    c.route_ticket = reinterpret_cast<uint32_t*>(c.route_list + n_items + 1);
+    c.route_flags = reinterpret_cast<uint8_t*>(c.route_list + n_items + 2);
+    return c;
+}
+
+// ---------------------------------------------------------------------------
+// Library-owned scratch of sr_route_decode_static, for callers that cannot
+// allocate.  One array per device (each GPU the library runs on holds its own
+// copy until the process ends): a ticket region sized for the largest layer
+// the envelope allows, the routing kernel's ticket, then the rest of a
+// workspace of up to SR_STATIC_SCRATCH_BYTES.  The ticket region is used for
+// nothing else, so a call of any shape finds its tickets at zero: they are
+// zeroed once at set-up and every call leaves them at zero.  Calls that
+// overlap on one device share the array and race.
+constexpr size_t kStaticTicketBytes = align256(kMaxItems * sizeof(uint32_t) + sizeof(uint32_t));
+constexpr size_t kStaticScratchBytes = kStaticTicketBytes + SR_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+std::atomic<char*> g_scratch[kMaxDevices];  // device address of `scratch`, per device
+
+// This device's address of `scratch`, set up on its first use: the symbol's
+// address is looked up with the device current and the ticket region cleared
+// with a fill kernel on `st` (no memset node, so a call under stream capture
+// records a plain kernel).
+sr_status static_scratch(hipStream_t st, char*& out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SR_ERR_HIP;
+    out = g_scratch[dev].load(std::memory_order_acquire);
+    if (out) return SR_OK;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    out = g_scratch[dev].load(std::memory_order_acquire);
+    if (out) return SR_OK;
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SR_ERR_HIP;
+    if (launch_zero(ptr, kStaticTicketBytes, st) != hipSuccess) return SR_ERR_HIP;
+    out = static_cast<char*>(ptr);
+    g_scratch[dev].store(out, std::memory_order_release);
+    return SR_OK;
+}
+
+Scratch scratch_in_static(const sr_shape& s, const WsLayout& w, char* base) {
+    const size_t n_items = static_cast<size_t>(s.batch) * s.num_kv_heads;
+    char* rest = base + kStaticTicketBytes;  // the workspace layout from its partials on
+    Scratch c;
+    c.tickets = reinterpret_cast<uint32_t*>(base);
+    c.route_ticket = reinterpret_cast<uint32_t*>(base) + kMaxItems;
+    c.part_ml = reinterpret_cast<float*>(rest);
+    c.part_acc = reinterpret_cast<float*>(rest + (w.acc - w.ml));
+    c.route_list = reinterpret_cast<int32_t*>(rest + (w.route - w.ml));
+    c.route_flags = reinterpret_cast<uint8_t*>(c.route_list + n_items + 2);
+    return c;
 }
 
 struct FusedRoute {
@@ -139,11 +217,16 @@ bool overlaps(const void* a, const void* b, size_t bytes) {
     return x < y + bytes && y < x + bytes;
 }
 
+// ws == nullptr with ws_bytes == kUseStaticScratch: the library's own scratch
+// (sr_route_decode_static).
+constexpr size_t kUseStaticScratch = ~static_cast<size_t>(0);
+
 sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float* q,
                      const void* k, const void* v, const float* v0, const int32_t* work_list,
                      const int32_t* n_active, float sm_scale, void* ws, size_t ws_bytes,
                      float* out, void* stream, bool routed, const FusedRoute* fused = nullptr,
                      float* alpha0 = nullptr, const FusedRope* rope = nullptr) {
+    const bool use_static = !ws && ws_bytes == kUseStaticScratch;
     sr_status st = check_shape(shape);
     if (st != SR_OK) return st;
     const sr_shape& s = *shape;
@@ -160,8 +243,8 @@ sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float
             return SR_ERR_INVALID_ARG;
     }
     if ((st = check_caches(s, k, v)) != SR_OK) return st;
-    if (!q || !out || !ws || !aligned16(q) || !aligned16(out) || !aligned16(ws))
-        return SR_ERR_INVALID_ARG;
+    if (!q || !out || !aligned16(q) || !aligned16(out)) return SR_ERR_INVALID_ARG;
+    if (!use_static && (!ws || !aligned16(ws))) return SR_ERR_INVALID_ARG;
     // every workgroup reads q (all of it when it routes) while others write out
     const size_t q_bytes = static_cast<size_t>(s.batch) * s.num_q_heads * s.head_dim * sizeof(float);
     if (overlaps(out, q, q_bytes)) return SR_ERR_INVALID_ARG;
@@ -172,7 +255,17 @@ sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float
     Plan p;
     if ((st = make_plan(s, launch, p)) != SR_OK) return st;
     const WsLayout w = ws_layout(s, p);
-    if (ws_bytes < w.total) return SR_ERR_INVALID_ARG;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    Scratch sc;
+    if (use_static) {
+        if (w.total > SR_STATIC_SCRATCH_BYTES) return SR_ERR_UNSUPPORTED;
+        char* base = nullptr;
+        if ((st = static_scratch(hs, base)) != SR_OK) return st;
+        sc = scratch_in_static(s, w, base);
+    } else {
+        if (ws_bytes < w.total) return SR_ERR_INVALID_ARG;
+        sc = scratch_in_workspace(s, w, ws);
+    }
 
     DecodeArgs a{};
     a.q = q;
@@ -182,10 +275,9 @@ sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float
     a.work_list = work_list;
     a.n_active = n_active;
     a.out = out;
-    char* base = static_cast<char*>(ws);
-    a.tickets = reinterpret_cast<uint32_t*>(base + w.tickets);
-    a.part_ml = reinterpret_cast<float*>(base + w.ml);
-    a.part_acc = reinterpret_cast<float*>(base + w.acc);
+    a.tickets = sc.tickets;
+    a.part_ml = sc.part_ml;
+    a.part_acc = sc.part_acc;
     a.stride_b = s.stride_b;
     a.stride_h = s.stride_h;
     a.stride_t = s.stride_t;
@@ -219,16 +311,13 @@ sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float
         a.n_active_out = fused->n_active;
     }
 
-    hipStream_t hs = static_cast<hipStream_t>(stream);
     if (fused && static_cast<int64_t>(s.batch) * s.num_q_heads > kMaxFusedHeads) {
         // large layer: the routing kernel (spread over the chip), then the decode
         const int32_t n_items = s.batch * s.num_kv_heads;
-        int32_t* ws_list = reinterpret_cast<int32_t*>(base + w.route);
-        uint32_t* ticket = reinterpret_cast<uint32_t*>(ws_list + n_items + 1);
-        uint8_t* ws_flags = reinterpret_cast<uint8_t*>(ws_list + n_items + 2);
-        int32_t* list = fused->work_list ? fused->work_list : ws_list;
-        int32_t* n_act = fused->n_active ? fused->n_active : ws_list + n_items;
-        uint8_t* flags = fused->mask ? fused->mask : ws_flags;
+        uint32_t* ticket = sc.route_ticket;
+        int32_t* list = fused->work_list ? fused->work_list : sc.route_list;
+        int32_t* n_act = fused->n_active ? fused->n_active : sc.route_list + n_items;
+        uint8_t* flags = fused->mask ? fused->mask : sc.route_flags;
         RouteRope rr{};
         if (rope) {
             rr = RouteRope{q, rope->k_new, rope->v_new, rope->inv_freq, rope->q_out,
@@ -332,6 +421,16 @@ sr_status sr_route_decode(const sr_shape* shape, const sr_launch* launch, const 
     const FusedRoute f{k0, tau, scores, mask, work_list, n_active};
     return run_decode(shape, launch, q, k_cache, v_cache, v0, nullptr, nullptr, sm_scale, ws,
                       ws_bytes, out, stream, true, &f);
+}
+
+sr_status sr_route_decode_static(const sr_shape* shape, const sr_launch* launch, const float* q,
+                                 const void* k_cache, const void* v_cache, const float* k0,
+                                 const float* v0, float tau, float sm_scale, float* scores,
+                                 uint8_t* mask, int32_t* work_list, int32_t* n_active, float* out,
+                                 void* stream) {
+    const FusedRoute f{k0, tau, scores, mask, work_list, n_active};
+    return run_decode(shape, launch, q, k_cache, v_cache, v0, nullptr, nullptr, sm_scale, nullptr,
+                      kUseStaticScratch, out, stream, true, &f);
 }
 
 sr_status sr_rope_route_decode(const sr_shape* shape, const sr_launch* launch,

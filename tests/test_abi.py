@@ -185,6 +185,34 @@ def test_fused_route_decode_validation():
     assert fused(shape(B=4097, Hq=8, Hkv=8)) == N.SR_ERR_UNSUPPORTED
 
 
+def test_static_scratch_route_decode_validation():
+    # The no-allocation form checks its arguments like sr_route_decode and
+    # rejects, before anything is enqueued, a shape whose workspace would not
+    # fit its fixed scratch.
+    def call(s, launch=None, k0=FAKE, v0=FAKE, tau=0.5, q=FAKE, out=OUT):
+        lp = None if launch is None else ctypes.byref(launch)
+        return N.lib.sr_route_decode_static(ctypes.byref(s), lp, p(q), p(), p(), p(k0), p(v0),
+                                            ctypes.c_float(tau), 0.0, p(0), p(0), p(0), p(0),
+                                            p(out), None)
+    s = shape()
+    assert call(s, k0=0) == N.SR_ERR_INVALID_ARG
+    assert call(s, v0=0) == N.SR_ERR_INVALID_ARG
+    assert call(s, q=0) == N.SR_ERR_INVALID_ARG
+    assert call(s, tau=float("nan")) == N.SR_ERR_INVALID_ARG
+    assert call(s, out=FAKE + 64) == N.SR_ERR_INVALID_ARG     # out overlaps q
+    assert call(shape(Hq=136)) == N.SR_ERR_UNSUPPORTED        # G = 17
+    # 1024 KV groups of 16 heads at 4 workgroups per CU need just over 16 MiB
+    big = shape(B=128, Hq=128, Hkv=8, T=64)
+    lau = N.SrLaunch(0, 0, 4, 0)
+    need = N.lib.sr_workspace_bytes(ctypes.byref(big), ctypes.byref(lau))
+    assert need > N.SR_STATIC_SCRATCH_BYTES
+    assert call(big, launch=lau) == N.SR_ERR_UNSUPPORTED
+    # fixed split counts grow the workspace too
+    lau = N.SrLaunch(4096, 0, 0, 0)
+    assert N.lib.sr_workspace_bytes(ctypes.byref(s), ctypes.byref(lau)) > N.SR_STATIC_SCRATCH_BYTES
+    assert call(s, launch=lau) == N.SR_ERR_UNSUPPORTED
+
+
 def test_rope_route_decode_validation():
     def call(s, kn=FAKE, vn=FAKE, f=FAKE, q_out=0, q=FAKE):
         return N.lib.sr_rope_route_decode(ctypes.byref(s), None, p(q), p(kn), p(vn), p(f),
