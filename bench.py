@@ -1,23 +1,32 @@
 #!/usr/bin/env python3
-"""Benchmark of one sink-routed decode layer-step on one MI355X.
+"""Benchmark of the sink-routed decode layer-step on one MI355X.
 
 A step is one pass of the whole hot path on one layer's cache: the routing
 (cosine scores, group decision, compacted work list) and the decode (sink
 bypass + split-K flash-decode of the active groups with the in-kernel merge),
-timed both as one sr_route_decode launch and as the two-call form (sr_route,
-then sr_decode_attn); the line reports the faster form and names it.  The default workload is the Llama-3.1-8B decode layer
-at 524288 cached positions (B=1, 32 query / 8 KV heads, d=128, bf16 K/V,
-4 of 8 KV groups planted as sinks), the shape the SinkRouter pages quote
-their 512K speedup on.  Two copies of the layer are rotated so nothing of a
-step's working set is still in the 256 MB Infinity Cache from the step before
-(in general enough copies to rotate over at least 4 GiB).
+timed both as one sr_route_decode call and as the two-call form (sr_route,
+then sr_decode_attn); each figure reports the faster form and names it.
+
+The headline workload (the JSON line's `value`) is the Llama-3.1-8B decode
+layer at 524288 cached positions (B=1, 32 query / 8 KV heads, d=128, bf16
+K/V, 4 of 8 KV groups planted as sinks), the shape the SinkRouter pages
+quote their 512K speedup on.  The line's `configs` list then times every
+layer shape of the suite the same way: the 4096-position fp32 layer, the 8B
+layer at 131072 positions, the 8B layer at 262144 positions with B=4 at sink
+fractions 0/25/50/75/100 %, the 512K layer, and the 70B-shaped layer at
+131072 positions with B=8.  Caches are drawn on the device (seeded, same
+recipe as the parity tests' host generator) and enough layer copies are
+rotated that nothing of a step's working set is still in the 256 MB Infinity
+Cache from the step before (at least 4 GiB).  Every figure is the median of
+--loops loops of --steps back-to-back steps after a settling warmup.
 
 Prints ONE JSON line (the metric: effective HBM GB/s of the routed
-layer-step, with us per layer-step, the dense baseline and the speedup), plus
-the decode kernel's roofline position, measured live with HIP events, and
-the fp64 CPU oracle timed on a bounded sample of the same workload.
+layer-step, with us per layer-step, the dense baseline and the speedup), the
+decode kernel's roofline position measured live with HIP events, and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--steps 50] [--warmup 20] [--settle 0.5] [--no-sweep] [--no-cpu-baseline]
+    python bench.py [--steps 50] [--warmup 20] [--loops 5] [--settle 0.5]
+                    [--no-configs] [--no-sweep] [--no-cpu-baseline]
 Environment knobs (no rebuild needed): SR_TAU, SR_SPLITS, SR_WGS_PER_CU,
 SR_KERNEL (auto|valu|mfma).
 """
@@ -78,7 +87,7 @@ def traffic_record(kernel_name: str, workload: str, path: str = TRAFFIC_JSON):
     return rec.get("hbm_bytes_per_launch")
 
 
-COPY_BYTES = 256 << 20
+CAL_BYTES = 256 << 20  # calibration buffer of the traffic counters
 
 
 def _pmc_rows(path, counter):
@@ -93,39 +102,68 @@ def _pmc_rows(path, counter):
     return rows
 
 
-def summarize_counters(fetch_csv, write_csv, out_path: str = TRAFFIC_JSON):
-    """HBM bytes per decode launch = counter (KiB) x 1024 x (COPY_BYTES / the
-    same counter's reading on the plain COPY_BYTES copy that `--calibrate-copy`
-    runs first).  Both runs execute the same program, so dispatch ids match;
-    the calibration copy is the copy kernel writing COPY_BYTES."""
-    out = {}
+def calibrate_counters(sr, torch, dev):
+    """Kernels of known traffic for the counter scale, launched before the
+    measured ones (`--calibrate`): the library's read probe with the decode
+    kernels' access shape (16-byte non-temporal loads, 8 in flight per lane,
+    256 workgroups), over CAL_BYTES once grid-strided and once per-workgroup
+    blocked, then the library's fill kernel writing CAL_BYTES
+    (sr_workspace_init)."""
+    import ctypes
+    from kv_cache_routing_amd import _native as N
+    buf = torch.empty(CAL_BYTES, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for blocked in (0, N.SR_READ_BLOCKED):
+        N.check(N.lib.sr_stream_read(ctypes.c_void_p(buf.data_ptr()), CAL_BYTES, 256, 8,
+                                     N.SR_READ_NONTEMPORAL | blocked,
+                                     ctypes.c_void_p(sink.data_ptr()), stream), "sr_stream_read")
+    N.check(N.lib.sr_workspace_init(ctypes.c_void_p(buf.data_ptr()), CAL_BYTES, stream),
+            "sr_workspace_init")
+    torch.cuda.synchronize()
+    del buf
+
+
+def summarize_counters(fetch_csv, write_csv, workload: str, out_path: str = TRAFFIC_JSON):
+    """HBM bytes per decode launch of one workload from two rocprofv3 --pmc
+    runs of `bench.py --roofline-only --calibrate`: counter (KiB) x 1024 x
+    scale, where FETCH_SIZE's scale is CAL_BYTES over its reading on the read
+    probe's two calibration launches (the decode kernels' load shape) and
+    WRITE_SIZE's is CAL_BYTES over its reading on the fill kernel.  Merged
+    into out_path under kernel@workload."""
     fetch, write = _pmc_rows(fetch_csv, "FETCH_SIZE"), _pmc_rows(write_csv, "WRITE_SIZE")
-    target = COPY_BYTES / 1024.0
-    cal = min((d for d, (k, v) in write.items() if "copy" in k.lower()),
-              key=lambda d: abs(write[d][1] - target))
-    assert abs(write[cal][1] - target) < 0.01 * target, "calibration copy not found"
-    for counter, rows in (("FETCH_SIZE", fetch), ("WRITE_SIZE", write)):
-        copy_kib = rows[cal][1]
-        scale = COPY_BYTES / (copy_kib * 1024.0)
-        for kname in ("k_decode_valu", "k_decode_mfma", "k_route"):
+    target = CAL_BYTES / 1024.0
+    probe = sorted(d for d, (k, _) in fetch.items() if "k_stream_read" in k)
+    fill = sorted(d for d, (k, _) in write.items() if "k_zero" in k)
+    assert len(probe) == 2 and fill, "calibration launches not found"
+    fill = [d for d in fill if abs(write[d][1] - target) < 0.05 * target] or fill[-1:]
+    cal = {"FETCH_SIZE": {"kernel": "k_stream_read<8, true> (grid-strided, blocked)",
+                          "kib": [fetch[d][1] for d in probe]},
+           "WRITE_SIZE": {"kernel": "k_zero", "kib": [write[fill[-1]][1]]}}
+    for c in cal.values():
+        c["scale"] = CAL_BYTES / (sum(c["kib"]) / len(c["kib"]) * 1024.0)
+    recs = {}
+    if os.path.exists(out_path):
+        with open(out_path) as f:
+            recs = json.load(f)
+    for kname in ("k_decode_valu", "k_decode_mfma", "k_route"):
+        per = {}
+        for counter, rows in (("FETCH_SIZE", fetch), ("WRITE_SIZE", write)):
             vals = [v for k, v in rows.values() if kname in k]
             if vals:
-                rec = out.setdefault(kname, {})
-                rec[counter] = {"kib_per_dispatch": sum(vals) / len(vals), "dispatches": len(vals),
-                                "copy_kib": copy_kib, "scale": scale,
-                                "bytes_per_dispatch": sum(vals) / len(vals) * 1024.0 * scale}
-    recs = {}
-    from workloads import L8B_512K
-    for kname, rec in out.items():
-        if "FETCH_SIZE" in rec and "WRITE_SIZE" in rec:
-            recs[f"{kname}@{L8B_512K.name}"] = {
-                "sources": decode_sources_digest(),
-                "hbm_bytes_per_launch": round(rec["FETCH_SIZE"]["bytes_per_dispatch"]
-                                              + rec["WRITE_SIZE"]["bytes_per_dispatch"]),
-                "fetch": rec["FETCH_SIZE"], "write": rec["WRITE_SIZE"]}
+                kib = sum(vals) / len(vals)
+                per[counter] = {"kib_per_dispatch": kib, "dispatches": len(vals),
+                                "scale": cal[counter]["scale"],
+                                "bytes_per_dispatch": kib * 1024.0 * cal[counter]["scale"]}
+        if len(per) == 2:
+            recs[f"{kname}@{workload}"] = {
+                "sources": decode_sources_digest(), "calibration": cal,
+                "hbm_bytes_per_launch": round(per["FETCH_SIZE"]["bytes_per_dispatch"]
+                                              + per["WRITE_SIZE"]["bytes_per_dispatch"]),
+                "fetch": per["FETCH_SIZE"], "write": per["WRITE_SIZE"]}
     with open(out_path, "w") as f:
         json.dump(recs, f, indent=1, sort_keys=True)
-    print(json.dumps(recs, indent=1))
+    print(json.dumps({k: v for k, v in recs.items() if k.endswith("@" + workload)}, indent=1))
     return recs
 
 
@@ -218,56 +256,85 @@ def time_loop(fn, steps, stream):
     return start.elapsed_time(end) / steps  # ms
 
 
-def cpu_baseline(layer, n_active_items, budget_s=12.0):
-    """The fp64 oracle on whole active items of the same layer, until about
-    budget_s of CPU work; reported as effective GB/s of KV processed."""
+def cpu_baseline(wl, q, k0, slabs, tau, budget_s=12.0, chunk=32768, gpu_out=None):
+    """The fp64 oracle on one routed layer-step of the workload, on the host
+    cores: a thread pool over (active group, chunk of `chunk` positions), each
+    piece the oracle's split partial of its chunk (oracle.split_partials with
+    one split), merged per group in ascending chunk order by
+    oracle.merge_partials (the oracle's split algebra, exact attention up to
+    rounding), plus the oracle's routing of every head.  BLAS runs one thread
+    per worker.  Passes repeat until budget_s of wall time; the median pass
+    is the layer-step time.  slabs: {item: (q rows [G][d], K [T][d], V [T][d])}
+    as host float32 arrays (exact copies of the bf16 caches)."""
+    import concurrent.futures as cf
+    import statistics
+
     import numpy as np
 
     import oracle
-    from workloads import as_numpy
-    blas = "unknown"
+    blas, limits = "unknown", None
     try:
-        from threadpoolctl import threadpool_info
-        info = threadpool_info()
-        cores = max([i.get("num_threads", 1) for i in info] or [1])
-        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in info) or blas
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')} "
+                         f"({i.get('threading_layer', '')})" for i in threadpool_info()) or blas
+        limits = threadpool_limits
     except Exception:  # pragma: no cover
-        cores = 1
-    wl = layer.wl
-    G = wl.group_size
-    q = as_numpy(layer.q)
+        pass
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
     scale = 1.0 / math.sqrt(wl.head_dim)
-    slabs = {}
-    for j in n_active_items:
-        b, g = divmod(int(j), wl.num_kv_heads)
-        slabs[j] = (q[b, g * G:(g + 1) * G], as_numpy(layer.k[b, g]), as_numpy(layer.v[b, g]))
-    done, t_total, bytes_total, passes = 0, 0.0, 0, 0
-    while t_total < budget_s:
-        for j in n_active_items:
-            t0 = time.perf_counter()
-            oracle.attend_group(*slabs[j], scale)
-            t_total += time.perf_counter() - t0
-            bytes_total += 2 * wl.seq_len * wl.head_dim * 2
-            done += 1
-        passes += 1
-    t0 = time.perf_counter()
-    oracle.route(q, as_numpy(layer.k[:, :, 0]), wl.tau)
-    t_route = time.perf_counter() - t0
-    step_s = t_total / passes + t_route
-    return {
-        "value": round(bytes_total / t_total / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+    items = sorted(slabs)
+    tasks = [(j, t0) for j in items for t0 in range(0, wl.seq_len, chunk)]
+
+    def piece(task):
+        j, t0 = task
+        qg, kk, vv = slabs[j]
+        return oracle.split_partials(qg, kk[t0:t0 + chunk], vv[t0:t0 + chunk], scale, 1)[0]
+
+    passes, outs = [], {}
+    ctx = limits(limits=1) if limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        cpu0, wall0 = time.process_time(), time.perf_counter()
+        with cf.ThreadPoolExecutor(threads) as ex:
+            while not passes or sum(passes) < budget_s:
+                t0 = time.perf_counter()
+                oracle.route(q, k0, tau)
+                parts = list(ex.map(piece, tasks))
+                for j in items:
+                    outs[j] = oracle.merge_partials([p for (jj, _), p in zip(tasks, parts)
+                                                     if jj == j])
+                passes.append(time.perf_counter() - t0)
+        cpu_s, wall_s = time.process_time() - cpu0, time.perf_counter() - wall0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    step_s = statistics.median(passes)
+    kv_bytes = len(items) * 2 * wl.seq_len * wl.head_dim * (2 if wl.kv_dtype == "bf16" else 4)
+    rep = {
+        "value": round(kv_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": threads,
         "kind": "oracle",
-        "sample": (f"{passes} passes over the {len(n_active_items)} active KV groups of one "
-                   f"{wl.name} layer-step ({done} group attentions, fp64 numpy, "
-                   f"{wl.seq_len} positions, G={G}) in {t_total:.1f} s; one routed "
-                   f"layer-step takes {step_s * 1e3:.0f} ms"),
+        "sample": (f"{len(passes)} routed layer-steps of {wl.name} ({len(items)} active KV "
+                   f"groups of {wl.seq_len} positions, G={wl.group_size}, fp64 numpy; "
+                   f"{len(tasks)} pieces of {chunk} positions per step on {threads} threads) "
+                   f"in {sum(passes):.1f} s; median step {step_s * 1e3:.0f} ms"),
         "us_per_layer_step": round(step_s * 1e6, 1),
-        "seconds": round(t_total, 2),
+        "passes": len(passes),
+        "seconds": round(sum(passes), 2),
+        "cpu_seconds_per_wall_second": round(cpu_s / wall_s, 2),
         "cpu_model": _cpu_model(),
         "host_cpus": len(os.sched_getaffinity(0)),
         "numpy": np.__version__,
         "blas": blas,
     }
+    if gpu_out is not None:  # the same step's GPU output, as a check of the sample
+        G = wl.group_size
+        err = 0.0
+        for j in items:
+            b, g = divmod(j, wl.num_kv_heads)
+            err = max(err, float(np.abs(gpu_out[b, g * G:(g + 1) * G] - outs[j]).max()))
+        rep["max_abs_vs_gpu"] = err
+    return rep
 
 
 def _cpu_model() -> str:
@@ -607,19 +674,227 @@ def bos_proxy_report(sr, torch):
     return 0
 
 
+def device_clocks():
+    """GPU clocks as rocm-smi reports them (best effort; None if unavailable)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        data = json.loads(r.stdout)
+        return {card: {k.rstrip(":"): v for k, v in vals.items() if "clk" in k.lower()}
+                for card, vals in data.items() if isinstance(vals, dict)}
+    except Exception as e:  # pragma: no cover
+        return {"unavailable": type(e).__name__}
+
+
+def sclk_now():
+    """The GPU core clock level marked current in sysfs (MHz), if readable."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                for ln in f:
+                    if ln.rstrip().endswith("*"):
+                        return ln.split(":", 1)[1].strip().rstrip("*").strip()
+        except OSError:
+            continue
+    return None
+
+
+def rotation(wl, rotate: int) -> int:
+    """Layer copies rotated over the timed steps: enough for >= 4 GiB, so no
+    step finds the previous step's data in the 256 MB Infinity Cache."""
+    if rotate > 0:
+        return rotate
+    es = 2 if wl.kv_dtype == "bf16" else 4
+    layer_bytes = 2 * wl.batch * wl.num_kv_heads * wl.seq_len * wl.head_dim * es
+    return max(1, min(8, -(-(4 << 30) // layer_bytes)))
+
+
+def device_layers(sr, torch, wl, R, dev):
+    """R device copies (k, v, k0, v0) of the workload's caches, drawn on the
+    device (timing only: the parity tests use the host generator)."""
+    from workloads import make_caches_device
+    k, v = make_caches_device(wl, dev)
+    caches = []
+    for r in range(R):
+        kk, vv = (k, v) if r == 0 else (k.clone(), v.clone())
+        caches.append((kk, vv, *sr.record_sink(kk, vv)))
+    return caches
+
+
+def same_size_read(sr, torch, nbytes: int, R: int, args, stream):
+    """The library's read probe over `nbytes` in one launch (the decode's
+    grid of 256 workgroups of 4 waves, 16-byte non-temporal loads, 8 in
+    flight), best of grid-strided and blocked, timed like the decode kernel
+    (back-to-back launches between one event pair, median of --loops loops),
+    over R rotated buffers.  The bare-read time of the decode kernel's bytes."""
+    import ctypes
+    import statistics
+
+    from kv_cache_routing_amd import _native as N
+    nbytes = nbytes // 16 * 16
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    best = None
+    for blocked in (0, N.SR_READ_BLOCKED):
+        def f(i, blocked=blocked):
+            N.check(N.lib.sr_stream_read(ctypes.c_void_p(bufs[i % R].data_ptr()), nbytes, 256, 8,
+                                         N.SR_READ_NONTEMPORAL | blocked,
+                                         ctypes.c_void_p(sink.data_ptr()),
+                                         ctypes.c_void_p(stream.cuda_stream)), "sr_stream_read")
+        warm_up([f], args.warmup, 0.1)
+        us = statistics.median(time_loop(f, args.steps, stream) for _ in range(args.loops)) * 1e3
+        best = us if best is None else min(best, us)
+    del bufs
+    return best
+
+
+def graph_time(torch, fn, steps, loops, stream):
+    """us per step of `steps` steps captured in one HIP graph and replayed
+    (median of `loops` replays): the GPU's own time per step, without the
+    host's launch rate and argument checks."""
+    import statistics
+    fn(0)  # eager first
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(loops):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e3 / steps)
+    del g
+    return statistics.median(times)
+
+
+def measure(sr, torch, wl, lau, tau, args, caches, q, *, dense=True, decode=True, probe=True,
+            dense_us=None):
+    """One workload's layer-step, each form timed as the median of --loops
+    loops of --steps back-to-back steps (HIP events on the launch stream)
+    after the settling warmup: sr_route_decode (one call), sr_route +
+    sr_decode_attn (two calls), sr_dense_decode, the one-call and dense steps
+    again replayed from a HIP graph; the decode kernel alone, back to back
+    (the roofline figure) and with an event pair per launch; and the bare
+    read of the same bytes."""
+    import statistics
+    stream = torch.cuda.current_stream()
+    R = len(caches)
+    shape = sr.make_shape(q, caches[0][0], caches[0][1])
+    ws = sr.Workspace(shape, lau, q.device)
+    out = torch.empty_like(q)
+    routes = [sr.route(q, c[2], tau) for c in caches]
+    torch.cuda.synchronize()
+    n_items = wl.batch * wl.num_kv_heads
+    n_active = int(routes[0].n_active.item())
+
+    def fused(i):
+        k, v, k0, v0 = caches[i % R]
+        sr.route_decode(q, k, v, k0, v0, tau, launch=lau, ws=ws, out=out, routing=routes[i % R])
+
+    def two_calls(i):
+        k, v, k0, v0 = caches[i % R]
+        r = routes[i % R]
+        sr.route(q, k0, tau, out=r)
+        sr.decode_attn(q, k, v, v0, r.work_list, r.n_active, launch=lau, ws=ws, out=out)
+
+    def dense_step(i):
+        k, v, _, _ = caches[i % R]
+        sr.dense_decode(q, k, v, launch=lau, ws=ws, out=out)
+
+    def decode_only(i):
+        k, v, k0, v0 = caches[i % R]
+        r = routes[i % R]
+        sr.decode_attn(q, k, v, v0, r.work_list, r.n_active, launch=lau, ws=ws, out=out)
+
+    forms = {"fused": fused, "two_calls": two_calls}
+    if dense:
+        forms["dense"] = dense_step
+    warm = warm_up(list(forms.values()) + ([decode_only] if decode else []), args.warmup,
+                   args.settle)
+    runs = {name: [] for name in forms}
+    dec, dec_b2b = [], []
+    for _ in range(args.loops):
+        for name, fn in forms.items():
+            runs[name].append(time_loop(fn, args.steps, stream) * 1e3)
+        if decode:
+            dec.append(time_launches(decode_only, args.steps, stream) * 1e3)
+            dec_b2b.append(time_loop(decode_only, args.steps, stream) * 1e3)
+    med = {name: statistics.median(v) for name, v in runs.items()}
+    graph = {"fused": graph_time(torch, fused, args.steps, args.loops, stream)}
+    if dense:
+        graph["dense"] = graph_time(torch, dense_step, args.steps, args.loops, stream)
+    step = min(med["fused"], med["two_calls"])
+    alg = algorithmic_bytes(wl, n_active)
+    rep = {"workload": wl.name,
+           "shape": f"B={wl.batch} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} d={wl.head_dim} "
+                    f"T={wl.seq_len} {wl.kv_dtype}",
+           "tau": tau, "groups": n_items, "n_active": n_active,
+           "sink_ratio": round(1 - n_active / n_items, 4),
+           "us_per_layer_step": round(step, 2),
+           "form": "sr_route_decode" if med["fused"] <= med["two_calls"] else
+                   "sr_route + sr_decode_attn",
+           "us_fused": round(med["fused"], 2), "us_two_calls": round(med["two_calls"], 2),
+           "us_fused_graph": round(graph["fused"], 2),
+           "us_loops": {k: [round(x, 2) for x in v] for k, v in runs.items()},
+           "algorithmic_bytes": alg, "step_gbs": round(alg / step / 1e3, 1),
+           "loops": args.loops, "steps": args.steps, "warmup_rounds_run": warm,
+           "rotated_layers": R}
+    d_us = med.get("dense", dense_us)
+    if d_us is not None:
+        rep["us_dense"] = round(d_us, 2)
+        if "dense" in graph:
+            rep["us_dense_graph"] = round(graph["dense"], 2)
+        rep["speedup_vs_dense"] = round(d_us / step, 4)
+        rep["pages_fields"] = {"context_length": wl.seq_len, "baseline_latency_us": round(d_us, 2),
+                               "sinkrouter_latency_us": round(step, 2),
+                               "throughput": round(1e6 / step, 1),
+                               "sink_ratio": rep["sink_ratio"],
+                               "speedup": round(d_us / step, 4)}
+    if decode:
+        # back to back: includes the gap between launches, so it errs low;
+        # it matched rocprof's per-dispatch average within 0.2 % at 512K, while
+        # an event pair per launch adds the events' own ~2.5 us
+        d = statistics.median(dec_b2b)
+        rep["decode_kernel_us"] = round(d, 2)
+        rep["decode_kernel_us_event_pairs"] = round(statistics.median(dec), 2)
+        rep["decode_gbs"] = round(alg / d / 1e3, 1)
+        rep["decode_frac_of_8tbs"] = round(alg / d / 1e3 / HBM_PEAK_GBS, 4)
+        if probe and n_active:
+            kv = alg - algorithmic_bytes(wl, 0)
+            r_us = same_size_read(sr, torch, kv, R, args, stream)
+            rep["same_size_read_us"] = round(r_us, 2)
+            rep["same_size_read_gbs"] = round(kv / r_us / 1e3, 1)
+            rep["decode_frac_of_same_size_read"] = round(r_us / d, 4)
+    rep["sclk_after"] = sclk_now()
+    del ws, out, routes
+    return rep
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--loops", type=int, default=5,
+                    help="timed loops of --steps steps per form; the median is reported")
     ap.add_argument("--settle", type=float, default=0.5,
                     help="seconds of untimed warmup at least (beyond --warmup steps)")
     ap.add_argument("--workload", default="llama8b-512k",
-                    help="llama8b-512k (default), llama8b-128k, llama8b-256k-b4-sink{0,25,50,75,100}, "
-                         "llama70b-128k-b8, tiny-4k-f32")
+                    help="headline workload: llama8b-512k (default), llama8b-128k, "
+                         "llama8b-256k-b4-sink{0,25,50,75,100}, llama70b-128k-b8, tiny-4k-f32")
     ap.add_argument("--rotate", type=int, default=0,
                     help="layer copies rotated over steps (0 = enough for >= 4 GiB)")
-    ap.add_argument("--no-sweep", action="store_true", help="skip the sink-fraction sweep")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only the headline workload, not every configuration")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the 512K sink-fraction sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-compare", action="store_true",
@@ -646,14 +921,16 @@ def main():
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the routed decode launches of the roofline measurement "
                          "(the command the committed rocprofv3 summaries profile)")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help=f"run one plain {COPY_BYTES >> 20} MiB device copy first (counter scale)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="with --roofline-only: first run the counter calibration kernels "
+                         f"(the read probe and the fill kernel over {CAL_BYTES >> 20} MiB)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
-                         "`bench.py --calibrate-copy` into profiles/traffic.json and exit")
+                         "`bench.py --roofline-only --calibrate --workload W` into "
+                         "profiles/traffic.json and exit")
     args = ap.parse_args()
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        summarize_counters(*args.summarize_counters, args.workload)
         return 0
 
     if args.gpus != 1:
@@ -661,11 +938,12 @@ def main():
               f"(asked for --gpus {args.gpus}). Run with --gpus 1.", flush=True)
         return 2
 
+    import statistics
+
     import torch
 
     import kv_cache_routing_amd as sr
-    from workloads import (CONFIGS, L8B_256K_B4, SINK_FRACTIONS, make_caches, make_queries,
-                           sweep)
+    from workloads import CONFIGS, L8B_256K_B4, SINK_FRACTIONS, make_queries, sweep
 
     if args.bos_proxy:
         return bos_proxy_report(sr, torch)
@@ -680,216 +958,220 @@ def main():
         print(f"unknown workload {args.workload}; choose from {sorted(names)}", flush=True)
         return 2
     wl = names[args.workload]
-    es = 2 if wl.kv_dtype == "bf16" else 4
-    layer_bytes = 2 * wl.batch * wl.num_kv_heads * wl.seq_len * wl.head_dim * es
-    if args.rotate <= 0:
-        args.rotate = max(1, min(8, -(-(4 << 30) // layer_bytes)))
     tau = float(os.environ.get("SR_TAU", wl.tau))
     kernel = os.environ.get("SR_KERNEL", "auto")
     lau = sr.make_launch(int(os.environ.get("SR_SPLITS", "0")), KERNEL_IDS[kernel],
                          int(os.environ.get("SR_WGS_PER_CU", "0")))
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
-
-    if args.calibrate_copy:  # a plain copy of known size, for the traffic counters
-        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    t0 = time.time()
-    k_cpu, v_cpu = make_caches(wl)
-    q_cpu, planted = make_queries(wl)
-    log(f"generated {wl.name} in {time.time() - t0:.1f} s")
-    caches = []
-    for r in range(args.rotate):
-        k = k_cpu.to(dev) if r == 0 else caches[0][0].clone()
-        v = v_cpu.to(dev) if r == 0 else caches[0][1].clone()
-        k0, v0 = sr.record_sink(k, v)
-        caches.append((k, v, k0, v0))
-    q = q_cpu.to(dev)
-    shape = sr.make_shape(q, caches[0][0], caches[0][1])
-    ws = sr.Workspace(shape, lau, dev)
-    routes = [sr.route(q, c[2], tau) for c in caches]
-    out = torch.empty_like(q)
-    torch.cuda.synchronize()
-    n_active = int(routes[0].n_active.cpu()[0])
-    active_items = routes[0].work_list.cpu().tolist()[:n_active]
-    R = len(caches)
-
-    def routed_step(i):
-        k, v, k0, v0 = caches[i % R]
-        r = routes[i % R]
-        sr.route(q, k0, tau, out=r)
-        sr.decode_attn(q, k, v, v0, r.work_list, r.n_active, launch=lau, ws=ws, out=out)
-
-    def decode_only(i):
-        k, v, k0, v0 = caches[i % R]
-        r = routes[i % R]
-        sr.decode_attn(q, k, v, v0, r.work_list, r.n_active, launch=lau, ws=ws, out=out)
-
-    def fused_step(i):
-        k, v, k0, v0 = caches[i % R]
-        sr.route_decode(q, k, v, k0, v0, tau, launch=lau, ws=ws, out=out, routing=routes[i % R])
-
-    def dense_step(i):
-        k, v, _, _ = caches[i % R]
-        sr.dense_decode(q, k, v, launch=lau, ws=ws, out=out)
-
     kname = "k_decode_valu" if kernel == "valu" else "k_decode_mfma"
-    alg = algorithmic_bytes(wl, n_active)
+
+    if args.roofline_only:
+        if args.calibrate:
+            calibrate_counters(sr, torch, dev)
+        caches = device_layers(sr, torch, wl, rotation(wl, args.rotate), dev)
+        q = make_queries(wl)[0].to(dev)
+        R = len(caches)
+        routes = [sr.route(q, c[2], tau) for c in caches]
+        ws = sr.Workspace(sr.make_shape(q, caches[0][0], caches[0][1]), lau, dev)
+        out = torch.empty_like(q)
+        torch.cuda.synchronize()
+        n_active = int(routes[0].n_active.item())
+
+        def decode_only(i):
+            k, v, k0, v0 = caches[i % R]
+            r = routes[i % R]
+            sr.decode_attn(q, k, v, v0, r.work_list, r.n_active, launch=lau, ws=ws, out=out)
+        warm_up([decode_only], args.warmup, args.settle)
+        us = time_loop(decode_only, args.steps, stream) * 1e3
+        alg = algorithmic_bytes(wl, n_active)
+        print(json.dumps({"roofline_only": True, "workload": wl.name, "kernel": kname,
+                          "decode_kernel_us": round(us, 2),
+                          "achieved_gbs": round(alg / us / 1e3, 1),
+                          "algorithmic_bytes_per_launch": alg, "launches": args.steps}),
+              flush=True)
+        return 0
+
+    t0 = time.time()
+    caches = device_layers(sr, torch, wl, rotation(wl, args.rotate), dev)
+    q_cpu = make_queries(wl)[0]
+    q = q_cpu.to(dev)
+    log(f"generated {wl.name} x{len(caches)} on the device in {time.time() - t0:.1f} s")
     if args.read_ceiling:
         best, rows = read_ceiling([t for c in caches for t in c[:2]], stream)
         print(json.dumps({"read_ceiling_gbs": round(best, 1), "bytes": sum(
             t.numel() * t.element_size() for c in caches for t in c[:2]), "sweep": rows}),
             flush=True)
         return 0
-    if args.roofline_only:
-        warm_up([decode_only], args.warmup, args.settle)
-        ms_decode = time_launches(decode_only, args.steps, stream)
-        dec_gbs = alg / (ms_decode * 1e-3) / 1e9
-        print(json.dumps({"roofline_only": True, "kernel": kname, "decode_kernel_us":
-                          round(ms_decode * 1e3, 2), "achieved_gbs": round(dec_gbs, 1),
-                          "algorithmic_bytes_per_launch": alg, "launches": args.steps}),
-              flush=True)
-        return 0
-    warm_rounds = warm_up([routed_step, fused_step, dense_step], args.warmup, args.settle)
-    ms_fused = time_loop(fused_step, args.steps, stream)
-    ms_routed = time_loop(routed_step, args.steps, stream)
-    ms_decode = time_launches(decode_only, args.steps, stream)
-    ms_dense = time_loop(dense_step, args.steps, stream)
+
+    head = measure(sr, torch, wl, lau, tau, args, caches, q)
+    log(f"{wl.name}: {json.dumps({k: head[k] for k in ('us_per_layer_step', 'us_dense', 'decode_kernel_us')})}")
+    R = len(caches)
+    shape = sr.make_shape(q, caches[0][0], caches[0][1])
+    n_active = head["n_active"]
 
     compare = {}
     if not args.no_compare:
         for name in ("valu", "mfma"):
             lk = sr.make_launch(lau.num_splits, KERNEL_IDS[name], lau.wgs_per_cu)
             wsk = sr.Workspace(shape, lk, dev)
+            outk = torch.empty_like(q)
+            rk = [sr.route(q, c[2], tau) for c in caches]
 
-            def dk(i, lk=lk, wsk=wsk):
+            def dk(i, lk=lk, wsk=wsk, outk=outk, rk=rk):
                 k, v, k0, v0 = caches[i % R]
-                r = routes[i % R]
-                sr.decode_attn(q, k, v, v0, r.work_list, r.n_active, launch=lk, ws=wsk, out=out)
+                r = rk[i % R]
+                sr.decode_attn(q, k, v, v0, r.work_list, r.n_active, launch=lk, ws=wsk, out=outk)
 
-            def dd(i, lk=lk, wsk=wsk):
+            def dd(i, lk=lk, wsk=wsk, outk=outk):
                 k, v, _, _ = caches[i % R]
-                sr.dense_decode(q, k, v, launch=lk, ws=wsk, out=out)
-            for i in range(args.warmup):
-                dk(i)
-                dd(i)
-            compare[name] = {"routed_decode_us": round(time_loop(dk, args.steps, stream) * 1e3, 2),
-                             "dense_decode_us": round(time_loop(dd, args.steps, stream) * 1e3, 2)}
+                sr.dense_decode(q, k, v, launch=lk, ws=wsk, out=outk)
+            warm_up([dk, dd], args.warmup, 0.1)
+            compare[name] = {
+                "routed_decode_us": round(statistics.median(
+                    time_loop(dk, args.steps, stream) for _ in range(args.loops)) * 1e3, 2),
+                "dense_decode_us": round(statistics.median(
+                    time_loop(dd, args.steps, stream) for _ in range(args.loops)) * 1e3, 2)}
             log(f"kernel {name}: {compare[name]}")
 
-    alg_dense = algorithmic_bytes(wl, wl.batch * wl.num_kv_heads)
-    # The layer-step is timed in both library forms; the line reports the
-    # faster one and names it.
-    fused_wins = ms_fused <= ms_routed
-    ms_step = ms_fused if fused_wins else ms_routed
-    gbs = alg / (ms_step * 1e-3) / 1e9
-    dec_gbs = alg / (ms_decode * 1e-3) / 1e9
-    dense_gbs = alg_dense / (ms_dense * 1e-3) / 1e9
-    splits = sr.splits_for(shape, lau, n_active)
-    traffic = traffic_record(kname, wl.name)
+    sweep_rows = []
+    if not args.no_sweep:
+        for f in SINK_FRACTIONS:
+            swl = sweep(wl, f)
+            row = measure(sr, torch, swl, lau, tau, args, caches,
+                          make_queries(swl)[0].to(dev), dense=False, decode=False,
+                          probe=False, dense_us=head["us_dense"])
+            sweep_rows.append({"sink_fraction": f, "n_active": row["n_active"],
+                               "us": row["us_per_layer_step"], "form": row["form"],
+                               "us_fused_graph": row["us_fused_graph"],
+                               "t_over_t_dense": round(row["us_per_layer_step"] / head["us_dense"], 4),
+                               "active_fraction": round(1 - row["sink_ratio"], 4),
+                               "gbs": row["step_gbs"]})
+            log(f"sweep f={f}: {row['us_per_layer_step']} us (n_active={row['n_active']})")
+        t_full = sweep_rows[0]["us"]
+        for row in sweep_rows:
+            row["t_over_t0"] = round(row["us"] / t_full, 4)
+            row["dev_from_linear"] = round(row["us"] / t_full - (1 - row["sink_fraction"]), 4)
+
     ceiling, _ = read_ceiling([t for c in caches for t in c[:2]], stream, grids=(256, 512),
                               unrolls=(8,))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        # host copies of the active groups (exact: bf16 widens to fp32)
+        from workloads import as_numpy
+        k, v, k0, v0 = caches[0]
+        r = sr.route(q, k0, tau)
+        out = sr.route_decode(q, k, v, k0, v0, tau, launch=lau)[0]
+        torch.cuda.synchronize()
+        active = [int(j) for j in r.work_list.cpu().tolist()[:n_active]]
+        G = wl.group_size
+        q_np = as_numpy(q_cpu)
+        slabs = {}
+        for j in active:
+            b, g = divmod(j, wl.num_kv_heads)
+            slabs[j] = (q_np[b, g * G:(g + 1) * G], as_numpy(k[b, g].cpu()),
+                        as_numpy(v[b, g].cpu()))
+        cpu = cpu_baseline(wl, q_np, as_numpy(k0.cpu()), slabs, tau, args.cpu_budget,
+                           gpu_out=out.cpu().numpy())
+        del slabs
+        log(f"cpu baseline: {cpu['sample']}")
+    del caches
+    torch.cuda.empty_cache()
+
+    configs = []
+    if not args.no_configs:
+        for cwl in CONFIGS:
+            if cwl.name == wl.name:
+                configs.append(head)
+                continue
+            cc = device_layers(sr, torch, cwl, rotation(cwl, args.rotate), dev)
+            ctau = float(os.environ.get("SR_TAU", cwl.tau))
+            if cwl.name == L8B_256K_B4.name:  # five sink fractions on the same caches
+                for i, f in enumerate(SINK_FRACTIONS):
+                    swl = sweep(cwl, f)
+                    rep = measure(sr, torch, swl, lau, ctau, args, cc,
+                                  make_queries(swl)[0].to(dev), dense=i == 0,
+                                  dense_us=configs[-1]["us_dense"] if i else None)
+                    configs.append(rep)
+                    log(f"{swl.name}: {rep['us_per_layer_step']} us")
+            else:
+                rep = measure(sr, torch, cwl, lau, ctau, args, cc, make_queries(cwl)[0].to(dev))
+                if cwl.kv_dtype == "f32" and cwl.seq_len <= 4096:
+                    rep["note"] = "launch-bound layer (4 MiB of cache): the time in us is the figure"
+                configs.append(rep)
+                log(f"{cwl.name}: {rep['us_per_layer_step']} us")
+            del cc
+            torch.cuda.empty_cache()
+    for rep in configs:
+        rep["traffic"] = traffic_record(kname, rep["workload"])
 
     props = torch.cuda.get_device_properties(dev)
     device = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
               "compute_units": props.multi_processor_count,
               "hbm_gib": round(props.total_memory / 2**30, 1), "hip": torch.version.hip,
-              "torch": torch.__version__}
+              "torch": torch.__version__, "clocks": device_clocks()}
+    splits = sr.splits_for(shape, lau, n_active)
     grid = sr.grid_size(shape, lau)
     parts0 = sr.plan_parts(shape, lau, n_active, 0)
-    chunk = parts0[0]["chunk"] if parts0 else 0
     balanced = n_active * splits < grid and splits < -(-wl.seq_len // 512)
     launch_info = {"waves_per_wg": lau.waves_per_wg or 4, "grid": grid,
                    "lanes_per_active_group": splits,
                    "positions_per_lane": -(-wl.seq_len // splits),
-                   "chunk_positions": chunk, "mode": "balanced" if balanced else "lanes"}
-
-    sweep_rows = []
-    if not args.no_sweep:
-        k, v, k0, v0 = caches[0]
-        for f in SINK_FRACTIONS:
-            swl = sweep(wl, f)
-            qf = make_queries(swl)[0].to(dev)
-            rf = sr.route(qf, k0, tau)
-            torch.cuda.synchronize()
-            na = int(rf.n_active.cpu()[0])
-
-            def st(i, qf=qf, rf=rf):
-                kk, vv, kk0, vv0 = caches[i % R]
-                sr.route_decode(qf, kk, vv, kk0, vv0, tau, launch=lau, ws=ws, out=out,
-                                routing=rf)
-            for i in range(args.warmup):
-                st(i)
-            ms = time_loop(st, args.steps, stream)
-            sweep_rows.append({"sink_fraction": f, "n_active": na, "us": round(ms * 1e3, 2),
-                               "t_over_t_dense": round(ms / ms_dense, 4),
-                               "active_fraction": round(na / (wl.batch * wl.num_kv_heads), 4),
-                               "gbs": round(algorithmic_bytes(wl, na) / (ms * 1e-3) / 1e9, 1)})
-            log(f"sweep f={f}: {ms * 1e3:.1f} us (n_active={na})")
-        t0 = sweep_rows[0]["us"]
-        for row in sweep_rows:
-            row["t_over_t0"] = round(row["us"] / t0, 4)
-            row["dev_from_linear"] = round(row["us"] / t0 - (1 - row["sink_fraction"]), 4)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        layer = type("L", (), {})()
-        layer.wl, layer.q, layer.k, layer.v = wl, q_cpu, k_cpu, v_cpu
-        cpu = cpu_baseline(layer, active_items, args.cpu_budget)
-
+                   "chunk_positions": parts0[0]["chunk"] if parts0 else 0,
+                   "mode": "balanced" if balanced else "lanes"}
+    ms_step = head["us_per_layer_step"] / 1e3
+    dec_gbs = head["decode_gbs"]
     line = {
         "metric": "decode-attn µs/layer-step + effective HBM GB/s at 512K ctx bf16, vs dense path",
         "workload": wl.name,
-        "value": round(gbs, 2),
+        "value": head["step_gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "warmup_rounds_run": warm_rounds,
+        "loops": args.loops,
+        "timing": (f"median of {args.loops} loops of {args.steps} back-to-back layer-steps, "
+                   "HIP events on the launch stream, after a settling warmup"),
         "settle_s": args.settle,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.kv_dtype,
-        "data": "synthetic",
+        "data": "synthetic (seeded N(0,1) caches drawn on the device, planted sink queries)",
         "config": {"workload": f"{wl.name}: B={wl.batch} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} "
                                f"d={wl.head_dim} T={wl.seq_len} {wl.kv_dtype} K/V, "
-                               f"{wl.batch * wl.num_kv_heads - n_active}/{wl.batch * wl.num_kv_heads} "
-                               f"groups sink, tau={tau}",
+                               f"{head['groups'] - n_active}/{head['groups']} groups sink, "
+                               f"tau={tau}",
                    "global_batch": wl.batch, "seq_len": wl.seq_len, "parallelism": "none (1 GPU)",
-                   "rotated_layers": R},
-        "us_per_layer_step": round(ms_step * 1e3, 2),
-        "us_per_layer_step_fused": round(ms_fused * 1e3, 2),
-        "us_per_layer_step_two_calls": round(ms_routed * 1e3, 2),
-        "us_per_layer_step_dense": round(ms_dense * 1e3, 2),
-        "speedup_vs_dense": round(ms_dense / ms_step, 4),
-        "step": ("sr_route_decode (routing + decode in one call)" if fused_wins else
-                 "sr_route + sr_decode_attn (two launches)") + ", the faster of the two forms",
-        "sink_ratio": round(1 - n_active / (wl.batch * wl.num_kv_heads), 4),
-        "dense_gbs": round(dense_gbs, 1),
-        "decode_kernel_us": round(ms_decode * 1e3, 2),
+                   "rotated_layers": head["rotated_layers"]},
+        "us_per_layer_step": head["us_per_layer_step"],
+        "us_per_layer_step_fused": head["us_fused"],
+        "us_per_layer_step_two_calls": head["us_two_calls"],
+        "us_per_layer_step_dense": head["us_dense"],
+        "speedup_vs_dense": head["speedup_vs_dense"],
+        "step": f"{head['form']}, the faster of the one-call and two-call forms",
+        "sink_ratio": head["sink_ratio"],
+        "decode_kernel_us": head["decode_kernel_us"],
         "splits_per_active_group": splits,
         "kernel": kernel,
         "launch": launch_info,
         "device": device,
-        # the output fields of the pages' efficiency benchmark
-        "pages_fields": {"context_length": wl.seq_len,
-                         "baseline_latency_us": round(ms_dense * 1e3, 2),
-                         "sinkrouter_latency_us": round(ms_step * 1e3, 2),
-                         "throughput": round(1e3 / ms_step, 1),
-                         "sink_ratio": round(1 - n_active / (wl.batch * wl.num_kv_heads), 4),
-                         "speedup": round(ms_dense / ms_step, 4)},
-        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
+        "pages_fields": head["pages_fields"],
+        "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": kname,
-                     "algorithmic_bytes_per_launch": alg,
+                     "traffic": traffic_record(kname, wl.name), "kernel": kname,
+                     "algorithmic_bytes_per_launch": head["algorithmic_bytes"],
+                     "launch_us": head["decode_kernel_us"],
+                     "timing": (f"{args.steps} decode launches back to back between one event "
+                                "pair on the launch stream, median of the loops"),
                      "measured_read_ceiling_gbs": round(ceiling, 1),
-                     "frac_of_measured_ceiling": round(dec_gbs / ceiling, 4)},
+                     "frac_of_measured_ceiling": round(dec_gbs / ceiling, 4),
+                     "same_size_read_us": head.get("same_size_read_us"),
+                     "frac_of_same_size_read": head.get("decode_frac_of_same_size_read")},
         "cpu_baseline": cpu,
+        "configs": configs,
         "sink_fraction_sweep": sweep_rows,
         "sink_fraction_sweep_max_dev_from_linear": (
             max(abs(r["dev_from_linear"]) for r in sweep_rows) if sweep_rows else None),

@@ -146,6 +146,25 @@ def make_caches(wl: Workload, *, threads: int | None = None):
     return k, v
 
 
+def make_caches_device(wl: Workload, device, *, seed_offset: int = 0):
+    """K, V [B][Hkv][T][d] drawn on `device`, for timing runs: the same recipe
+    as make_caches (N(0, 1) entries rounded to the layer's dtype, the key at
+    position 0 of every group replaced by make_k0(wl), so make_queries(wl)
+    plants the same sinks) from torch's device generator, so the bits differ
+    from make_caches'.  A multi-GiB layer takes well under a second; the
+    parity tests draw on the host with make_caches."""
+    B, Hkv, T, d = wl.batch, wl.num_kv_heads, wl.seq_len, wl.head_dim
+    gen = torch.Generator(device=device).manual_seed(wl.seed * 4096 + 7000 + seed_offset)
+    k = torch.empty((B, Hkv, T, d), dtype=wl.torch_dtype, device=device)
+    v = torch.empty_like(k)
+    for b in range(B):  # one item at a time bounds the fp32 staging
+        for t in (k, v):
+            t[b].copy_(torch.randn((Hkv, T, d), generator=gen, device=device,
+                                   dtype=torch.float32))
+    k[:, :, 0] = make_k0(wl).to(device=device, dtype=wl.torch_dtype)
+    return k, v
+
+
 def planted_sinks(wl: Workload) -> torch.Tensor:
     """[B][Hkv] bool: the groups whose queries are built aligned with k0."""
     B, Hkv = wl.batch, wl.num_kv_heads
