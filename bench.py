@@ -192,10 +192,11 @@ def time_launches(fn, steps, stream):
     return sum(a.elapsed_time(b) for a, b in evs) / steps  # ms
 
 
-def read_ceiling(tensors, stream, grids=(256, 512, 1024), unrolls=(4, 8)):
+def read_ceiling(tensors, stream, grids=(256, 512, 1024), unrolls=(4, 8), lds=(0,)):
     """Best read bandwidth of the library's streaming probe over the given
     device tensors (16-byte loads per lane, the decode kernels' access width),
-    grid-strided and per-workgroup-blocked, default and non-temporal loads."""
+    grid-strided and per-workgroup-blocked, default and non-temporal loads,
+    into registers or (lds=(0, 1)) staged through LDS by direct-to-LDS loads."""
     import ctypes
 
     import torch
@@ -204,23 +205,25 @@ def read_ceiling(tensors, stream, grids=(256, 512, 1024), unrolls=(4, 8)):
     sink = torch.zeros(max(grids), dtype=torch.int32, device=tensors[0].device)
     total = sum(t.numel() * t.element_size() for t in tensors)
     best, rows = 0.0, []
-    for nontemporal in (0, 1):
-        for blocked in (0, 1):
-            flags = blocked * N.SR_READ_BLOCKED + nontemporal * N.SR_READ_NONTEMPORAL
-            for grid in grids:
-                for un in unrolls:
-                    def f(i):
-                        for t in tensors:
-                            N.check(N.lib.sr_stream_read(
-                                ctypes.c_void_p(t.data_ptr()), t.numel() * t.element_size(), grid,
-                                un, flags, ctypes.c_void_p(sink.data_ptr()),
-                                ctypes.c_void_p(stream.cuda_stream)), "sr_stream_read")
-                    f(0)
-                    ms = time_loop(f, 5, stream)
-                    gbs = total / (ms * 1e-3) / 1e9
-                    rows.append({"nontemporal": nontemporal, "blocked": blocked, "grid": grid,
-                                 "unroll": un, "gbs": round(gbs, 1)})
-                    best = max(best, gbs)
+    shapes = [(st, nt, bl, grid, un) for st in lds for nt in (0, 1) for bl in (0, 1)
+              for grid in grids for un in unrolls]
+    for staged, nontemporal, blocked, grid, un in shapes:
+        flags = (blocked * N.SR_READ_BLOCKED + nontemporal * N.SR_READ_NONTEMPORAL
+                 + staged * N.SR_READ_LDS)
+
+        def f(i, flags=flags, grid=grid, un=un):
+            for t in tensors:
+                N.check(N.lib.sr_stream_read(
+                    ctypes.c_void_p(t.data_ptr()), t.numel() * t.element_size(), grid, un, flags,
+                    ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream)),
+                    "sr_stream_read")
+        f(0)
+        ms = time_loop(f, 5, stream)
+        gbs = total / (ms * 1e-3) / 1e9
+        rows.append({"lds": staged, "nontemporal": nontemporal, "blocked": blocked, "grid": grid,
+                     "unroll": un, "gbs": round(gbs, 1)})
+        if not staged:
+            best = max(best, gbs)
     return best, rows
 
 
@@ -998,7 +1001,8 @@ def main():
     q = q_cpu.to(dev)
     log(f"generated {wl.name} x{len(caches)} on the device in {time.time() - t0:.1f} s")
     if args.read_ceiling:
-        best, rows = read_ceiling([t for c in caches for t in c[:2]], stream)
+        best, rows = read_ceiling([t for c in caches for t in c[:2]], stream,
+                                  unrolls=(4, 8, 16), lds=(0, 1))
         print(json.dumps({"read_ceiling_gbs": round(best, 1), "bytes": sum(
             t.numel() * t.element_size() for c in caches for t in c[:2]), "sweep": rows}),
             flush=True)

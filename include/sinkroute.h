@@ -339,12 +339,15 @@ const char* sr_status_string(sr_status status);
  * achievable HBM read bandwidth.  `flags` bit 0 (SR_READ_BLOCKED): each
  * workgroup streams its own contiguous slice instead of the grid walking the
  * buffer together; bit 1 (SR_READ_NONTEMPORAL): loads use the non-temporal
- * cache policy, as the decode kernels' cache loads do.  Other bits are an
- * error.  `sink` (>= grid u32, device) is written only in the practically
+ * cache policy, as the decode kernels' cache loads do; bit 2 (SR_READ_LDS):
+ * every load goes straight into the wave's LDS tile (16-byte direct-to-LDS
+ * loads, U KiB of LDS per wave) and is read back from there, the shape of a
+ * kernel that stages its tiles through LDS.  Other bits are an error.  `sink` (>= grid u32, device) is written only in the practically
  * impossible case that a workgroup's XOR of the data is 0x9e3779b9; it exists
  * so no load can be optimised away. */
 #define SR_READ_BLOCKED 1
 #define SR_READ_NONTEMPORAL 2
+#define SR_READ_LDS 4
 sr_status sr_stream_read(const void* buf, size_t bytes, int32_t grid, int32_t unroll,
                          int32_t flags, uint32_t* sink, void* stream);
 

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(_HERE, "libsinkroute.so")
 SR_OK, SR_ERR_INVALID_ARG, SR_ERR_UNSUPPORTED, SR_ERR_HIP = 0, 1, 2, 3
 SR_KV_BF16, SR_KV_F32 = 0, 1
 SR_KERNEL_AUTO, SR_KERNEL_VALU, SR_KERNEL_MFMA = 0, 1, 2
-SR_READ_BLOCKED, SR_READ_NONTEMPORAL = 1, 2
+SR_READ_BLOCKED, SR_READ_NONTEMPORAL, SR_READ_LDS = 1, 2, 4
 
 # Every function include/sinkroute.h declares.
 EXPORTS = (

@@ -521,7 +521,7 @@ sr_status sr_stream_read(const void* buf, size_t bytes, int32_t grid, int32_t un
     if (!buf || !sink || !aligned16(buf) || bytes < 16 || grid < 1) return SR_ERR_INVALID_ARG;
     if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8 && unroll != 16)
         return SR_ERR_INVALID_ARG;
-    if (flags & ~(SR_READ_BLOCKED | SR_READ_NONTEMPORAL)) return SR_ERR_INVALID_ARG;
+    if (flags & ~(SR_READ_BLOCKED | SR_READ_NONTEMPORAL | SR_READ_LDS)) return SR_ERR_INVALID_ARG;
     hipError_t e = launch_stream_read(buf, bytes, grid, unroll, flags, sink,
                                       static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SR_OK : SR_ERR_HIP;

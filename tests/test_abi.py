@@ -153,8 +153,9 @@ def test_route_and_record_validation():
 def test_stream_read_validation():
     def rd(flags=0, unroll=4, grid=256, buf=FAKE, nbytes=1 << 20):
         return N.lib.sr_stream_read(p(buf), nbytes, grid, unroll, flags, p(), None)
-    assert rd(flags=4) == N.SR_ERR_INVALID_ARG
+    assert rd(flags=8) == N.SR_ERR_INVALID_ARG
     assert rd(flags=-1) == N.SR_ERR_INVALID_ARG
+    assert rd(flags=N.SR_READ_LDS, unroll=32) == N.SR_ERR_INVALID_ARG
     assert rd(unroll=3) == N.SR_ERR_INVALID_ARG
     assert rd(grid=0) == N.SR_ERR_INVALID_ARG
     assert rd(buf=FAKE + 8) == N.SR_ERR_INVALID_ARG
@@ -167,6 +168,7 @@ def test_header_constants_match_binding():
     defines = dict(re.findall(r"#define\s+(SR_[A-Z_0-9]+)\s+(\d+)", text))
     assert int(defines["SR_READ_BLOCKED"]) == N.SR_READ_BLOCKED
     assert int(defines["SR_READ_NONTEMPORAL"]) == N.SR_READ_NONTEMPORAL
+    assert int(defines["SR_READ_LDS"]) == N.SR_READ_LDS
 
 
 def test_fused_route_decode_validation():
