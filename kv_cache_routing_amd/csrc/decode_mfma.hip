@@ -90,19 +90,34 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma(DecodeArgs a) {
     auto pass = [&](int32_t part, MergeJob& job) -> bool {
         const WorkUnit u = part_of<NW * 16 * SUB>(a, wr, part);
 
-        // A operands: query row = col, elements d = 32*kb + 8*grp + e
+        // A operands: query row = col, elements d = 32*kb + 8*grp + e.  Every
+        // load goes out before any is used and none sits under a branch: the
+        // padded rows (col >= G) read the group's last real row and are zeroed
+        // by a select.  (q may be in memory or, with the rotary step fused, in
+        // LDS, so these are generic loads; as loads under a per-lane condition
+        // the compiler issued them one at a time, each waiting for the last:
+        // about 2.5 us before the first cache load.)
         bf16x8 qhi[KB], qlo[KB];
         {
+            const int32_t hq = col < G ? col : G - 1;
             const float* qr = wr.q + (static_cast<int64_t>(u.b) * a.num_q_heads +
-                                     static_cast<int64_t>(u.g) * G + col) * D;
+                                     static_cast<int64_t>(u.g) * G + hq) * D + 8 * grp;
             const bool real = col < G;
+            float4 xq[KB][2];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
+                xq[kb][0] = *reinterpret_cast<const float4*>(qr + 32 * kb);
+                xq[kb][1] = *reinterpret_cast<const float4*>(qr + 32 * kb + 4);
+            }
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const float xs[8] = {xq[kb][0].x, xq[kb][0].y, xq[kb][0].z, xq[kb][0].w,
+                                     xq[kb][1].x, xq[kb][1].y, xq[kb][1].z, xq[kb][1].w};
                 uint32_t hw[4], lw[4];
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
-                    float x0 = real ? qr[32 * kb + 8 * grp + e] * a.qscale : 0.f;
-                    float x1 = real ? qr[32 * kb + 8 * grp + e + 1] * a.qscale : 0.f;
+                    float x0 = real ? xs[e] * a.qscale : 0.f;
+                    float x1 = real ? xs[e + 1] * a.qscale : 0.f;
                     const uint32_t h0 = bf16_rne_bits(x0), h1 = bf16_rne_bits(x1);
                     const uint32_t l0 = bf16_rne_bits(x0 - bf16_bits_to_float(h0));
                     const uint32_t l1 = bf16_rne_bits(x1 - bf16_bits_to_float(h1));
@@ -406,17 +421,22 @@ __global__ __launch_bounds__(NW * 64) void k_decode_mfma_f32(DecodeArgs a) {
 
         float qv[KD];  // B operand of QK: head col, element 16*(kb/4) + 4*grp + kb%4
         {
+            // branch-free loads, all issued before any is used (padded rows
+            // re-read the last real row and are zeroed by the select)
+            const int32_t hq = col < G ? col : G - 1;
             const float* qr = wr.q + (static_cast<int64_t>(u.b) * a.num_q_heads +
-                                     static_cast<int64_t>(u.g) * G + col) * D + 4 * grp;
-            const bool real = col < G;
+                                     static_cast<int64_t>(u.g) * G + hq) * D + 4 * grp;
+            const float sc = col < G ? a.qscale : 0.f;
+            float4 xq[KD / 4];
+#pragma unroll
+            for (int j = 0; j < KD / 4; ++j) xq[j] = *reinterpret_cast<const float4*>(qr + 16 * j);
 #pragma unroll
             for (int j = 0; j < KD / 4; ++j) {
-                const float4 x = real ? *reinterpret_cast<const float4*>(qr + 16 * j)
-                                      : make_float4(0.f, 0.f, 0.f, 0.f);
-                qv[4 * j] = x.x * a.qscale;
-                qv[4 * j + 1] = x.y * a.qscale;
-                qv[4 * j + 2] = x.z * a.qscale;
-                qv[4 * j + 3] = x.w * a.qscale;
+                const float4 x = xq[j];
+                qv[4 * j] = col < G ? x.x * sc : 0.f;
+                qv[4 * j + 1] = col < G ? x.y * sc : 0.f;
+                qv[4 * j + 2] = col < G ? x.z * sc : 0.f;
+                qv[4 * j + 3] = col < G ? x.w * sc : 0.f;
             }
         }
         const float* kbase = static_cast<const float*>(a.k) + u.b * a.stride_b + u.g * a.stride_h;

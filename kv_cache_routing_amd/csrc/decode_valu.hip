@@ -108,24 +108,28 @@ __global__ __launch_bounds__(NW * 64) void k_decode_valu(DecodeArgs a) {
 
         float qs[GP][E];
         {
+            // branch-free loads, all issued before any is used: the padded
+            // heads (h >= G) re-read the last real head and are zeroed by a
+            // select (as loads under a branch, each waited for the one before)
             const float* qb = wr.q + (static_cast<int64_t>(u.b) * a.num_q_heads +
                                      static_cast<int64_t>(u.g) * G) * D + chunk * E;
+            float4 xq[GP][E / 4];
 #pragma unroll
-            for (int h = 0; h < GP; ++h) {
-                if (h < G) {
+            for (int h = 0; h < GP; ++h)
 #pragma unroll
-                    for (int e4 = 0; e4 < E; e4 += 4) {
-                        const float4 x = *reinterpret_cast<const float4*>(qb + h * D + e4);
-                        qs[h][e4] = x.x * a.qscale;
-                        qs[h][e4 + 1] = x.y * a.qscale;
-                        qs[h][e4 + 2] = x.z * a.qscale;
-                        qs[h][e4 + 3] = x.w * a.qscale;
-                    }
-                } else {
+                for (int e4 = 0; e4 < E; e4 += 4)
+                    xq[h][e4 / 4] = *reinterpret_cast<const float4*>(
+                        qb + static_cast<int64_t>(h < G ? h : G - 1) * D + e4);
 #pragma unroll
-                    for (int e = 0; e < E; ++e) qs[h][e] = 0.f;
+            for (int h = 0; h < GP; ++h)
+#pragma unroll
+                for (int e4 = 0; e4 < E; e4 += 4) {
+                    const float4 x = xq[h][e4 / 4];
+                    qs[h][e4] = h < G ? x.x * a.qscale : 0.f;
+                    qs[h][e4 + 1] = h < G ? x.y * a.qscale : 0.f;
+                    qs[h][e4 + 2] = h < G ? x.z * a.qscale : 0.f;
+                    qs[h][e4 + 3] = h < G ? x.w * a.qscale : 0.f;
                 }
-            }
         }
 
         const KV* kb = static_cast<const KV*>(a.k) + u.b * a.stride_b + u.g * a.stride_h + chunk * E;
