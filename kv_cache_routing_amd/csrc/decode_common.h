@@ -305,6 +305,13 @@ __device__ inline void merge_splits(const DecodeArgs& a, const MergeJob& u, floa
     const int32_t G = a.group;
     const int32_t S = u.parts;
     const float* ml0 = a.part_ml + static_cast<int64_t>(u.base) * 3 * GP;
+    // Nothing is in flight here (the ticket waited for every memory operation),
+    // but the compiler cannot see that through the passes' control flow: it
+    // guarded the registers of the streaming loop's last prefetch with waits
+    // placed between the loads below, which held half of the accumulator
+    // loads back until (m, l) had arrived.  An explicit wait, free at run time,
+    // clears that bookkeeping, so every load below goes out at once.
+    __builtin_amdgcn_s_waitcnt(0);
     const float4* acc0 =
         reinterpret_cast<const float4*>(a.part_acc + static_cast<int64_t>(u.base) * GP * D);
     const int gi = GROUPS > 1 ? t / NV : 0;
