@@ -417,6 +417,8 @@ def decode_layers_report(sr, torch, args):
     generator (timing only; every kernel's parity is tested elsewhere).  Sink
     groups' queries are built in the rotated frame (0.9 k0/|k0| + 0.05 noise)
     and turned back by -pos on the host, so the routing sees planted sinks."""
+    import statistics
+
     from workloads import rope_inv_freq
     from workloads.synth import K0_NORM
     L, T0, N = args.decode_layers, args.context, args.tokens
@@ -564,21 +566,33 @@ def decode_layers_report(sr, torch, args):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / (reps * len(gs)) * 1e3  # us per token
 
-    routed = run(graphs(routed=True))
-    dense = run(graphs(routed=False))
-    append_only = run(graphs(attend=False))
-    attend_routed = run(graphs(routed=True, append=False))
-    attend_dense = run(graphs(routed=False, append=False))
-    routed_one = run(graphs(routed=True, fused=True))
-    dense_one = run(graphs(routed=False, fused=True))
-    model_rep = None
+    variants = {"routed": dict(routed=True), "dense": dict(routed=False),
+                "append_only": dict(attend=False),
+                "attend_routed": dict(routed=True, append=False),
+                "attend_dense": dict(routed=False, append=False),
+                "routed_one": dict(routed=True, fused=True),
+                "dense_one": dict(routed=False, fused=True)}
     if args.model_step:
         for kw in (dict(routed=True), dict(routed=False), dict(attend=False)):
             token(0, fused=True, model=True, **kw)  # eager first: library handles, workspaces
         torch.cuda.synchronize()
-        full_routed = run(graphs(routed=True, fused=True, model=True))
-        full_dense = run(graphs(routed=False, fused=True, model=True))
-        rest = run(graphs(attend=False, fused=True, model=True))
+        variants.update({"full_routed": dict(routed=True, fused=True, model=True),
+                         "full_dense": dict(routed=False, fused=True, model=True),
+                         "rest": dict(attend=False, fused=True, model=True)})
+    captured = {name: graphs(**kw) for name, kw in variants.items()}
+    # Interleaved: every loop replays every variant once, so clock drift over
+    # the run falls on all of them alike; each figure is the median of the loops.
+    times = {name: [] for name in captured}
+    for _ in range(args.loops):
+        for name, gs in captured.items():
+            times[name].append(run(gs))
+    med = {name: statistics.median(v) for name, v in times.items()}
+    routed, dense, append_only = med["routed"], med["dense"], med["append_only"]
+    attend_routed, attend_dense = med["attend_routed"], med["attend_dense"]
+    routed_one, dense_one = med["routed_one"], med["dense_one"]
+    model_rep = None
+    if args.model_step:
+        full_routed, full_dense, rest = med["full_routed"], med["full_dense"], med["rest"]
         model_rep = {
             "layer": "Llama-3.1-8B decoder layer, random-init bf16 weights "
                      f"({sum(x.numel() for w in wts for x in w.values()) * 2 / 2 ** 30:.1f} GiB "
@@ -594,7 +608,8 @@ def decode_layers_report(sr, torch, args):
     rep = {"decode_layers": {
         "layers": L, "context": T0, "tokens": N, "routed_layers": [start, end],
         "shape": f"B={B} Hq={Hq} Hkv={Hkv} d={d} bf16 K/V, half of the groups planted as sinks",
-        "timing": "one HIP graph per token (rotary + append + attention for every layer)",
+        "timing": "one HIP graph per token (rotary + append + attention for every layer); "
+                  f"median of {args.loops} interleaved loops of 3 replays of every token",
         "active_groups_last_token": active, "groups_routed_layers": gated * B * Hkv,
         "us_per_token_routed": round(routed, 1), "us_per_token_dense": round(dense, 1),
         "speedup": round(dense / routed, 4),
