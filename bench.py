@@ -1133,7 +1133,7 @@ def main():
     splits = sr.splits_for(shape, lau, n_active)
     grid = sr.grid_size(shape, lau)
     parts0 = sr.plan_parts(shape, lau, n_active, 0)
-    balanced = n_active * splits < grid and splits < -(-wl.seq_len // 512)
+    balanced = n_active * splits < grid and splits < sr.split_cap(shape, lau)
     launch_info = {"waves_per_wg": lau.waves_per_wg or 4, "grid": grid,
                    "lanes_per_active_group": splits,
                    "positions_per_lane": -(-wl.seq_len // splits),

@@ -109,10 +109,15 @@ typedef struct {
      *      below T is an empty part).
      *   0: adaptive: the grid is a fixed number of workgroups sized from the
      *      device's CU count; the kernel reads the device-side n_active and
-     *      takes S = min(grid / n_active, ceil(T / 512)) lanes per item, in
-     *      balanced mode when grid / n_active is not a whole number below that
-     *      cap, so the GPU stays full at any sink fraction without a host
-     *      sync. */
+     *      takes S = min(grid / n_active, cap) lanes per item, in balanced
+     *      mode when grid / n_active is not a whole number below the cap, so
+     *      the GPU stays full at any sink fraction without a host sync.  The
+     *      cap (sr_split_cap) weighs the parts' streaming against the merge:
+     *      more lanes mean fewer chunks per part, but each started multiple
+     *      of the merge's round size (the partials one round trip takes in)
+     *      adds a round to the last part's merge.  It is the lane count,
+     *      at most the item's chunk count and the grid, that minimises the
+     *      estimated chunk and round times measured on MI355X. */
     int32_t num_splits;
     int32_t kernel;        /* sr_kernel */
     int32_t wgs_per_cu;    /* adaptive grid size in workgroups per CU (0 = 1) */
@@ -304,6 +309,11 @@ sr_status sr_dense_decode_alpha0(const sr_shape* shape, const sr_launch* launch,
  * under this policy (what the adaptive mode derives on the device); 0 for an
  * invalid shape or policy. */
 int32_t sr_splits_for(const sr_shape* shape, const sr_launch* launch, int32_t n_active);
+
+/* The most lanes per item the policy takes: the adaptive cap above, or the
+ * fixed count; 0 for an invalid shape or policy.  The adaptive policy runs in
+ * balanced mode exactly when n_active * S < grid and S < this cap. */
+int32_t sr_split_cap(const sr_shape* shape, const sr_launch* launch);
 
 /* One workgroup's part of one item, as the decode kernel divides the work. */
 typedef struct {

@@ -25,7 +25,7 @@ from ._native import (SR_KERNEL_AUTO, SR_KERNEL_MFMA, SR_KERNEL_VALU,  # noqa: F
 __all__ = ["record_sink", "route", "decode_attn", "route_decode", "dense_decode",
            "dense_decode_alpha0", "rope_append", "rope_route_decode", "Workspace",
            "make_shape",
-           "make_launch", "splits_for", "grid_size", "plan_parts", "SinkRouteError", "Routing",
+           "make_launch", "splits_for", "split_cap", "grid_size", "plan_parts", "SinkRouteError", "Routing",
            "SR_KERNEL_AUTO", "SR_KERNEL_VALU", "SR_KERNEL_MFMA"]
 
 
@@ -88,6 +88,10 @@ def make_launch(num_splits: int = 0, kernel: int = SR_KERNEL_AUTO, wgs_per_cu: i
 
 def splits_for(shape: N.SrShape, launch: N.SrLaunch | None, n_active: int) -> int:
     return N.lib.sr_splits_for(ctypes.byref(shape), _lp(launch), n_active)
+
+
+def split_cap(shape: N.SrShape, launch: N.SrLaunch | None) -> int:
+    return N.lib.sr_split_cap(ctypes.byref(shape), _lp(launch))
 
 
 def grid_size(shape: N.SrShape, launch: N.SrLaunch | None) -> int:

@@ -19,7 +19,7 @@ SR_READ_BLOCKED, SR_READ_NONTEMPORAL, SR_READ_LDS = 1, 2, 4
 # Every function include/sinkroute.h declares.
 EXPORTS = (
     "sr_record_sink", "sr_route", "sr_workspace_bytes", "sr_workspace_init",
-    "sr_decode_attn", "sr_dense_decode", "sr_splits_for", "sr_grid_size",
+    "sr_decode_attn", "sr_dense_decode", "sr_splits_for", "sr_split_cap", "sr_grid_size",
     "sr_status_string", "sr_version", "sr_stream_read", "sr_route_decode",
     "sr_dense_decode_alpha0", "sr_rope_append", "sr_plan_parts", "sr_rope_route_decode",
     "sr_route_decode_static",
@@ -82,6 +82,7 @@ def _load():
         "sr_rope_route_decode": (i32, [S, Lp, P, P, P, P, P, P, P, P, P, f32, f32, P, P, P, P,
                                        P, sz, P, P]),
         "sr_splits_for": (i32, [S, Lp, i32]),
+        "sr_split_cap": (i32, [S, Lp]),
         "sr_grid_size": (i32, [S, Lp]),
         "sr_status_string": (ctypes.c_char_p, [i32]),
         "sr_version": (i32, []),

@@ -78,7 +78,6 @@ sr_status make_plan(const sr_shape& s, const sr_launch* launch, Plan& p) {
     p.gp = pad_group(s.num_q_heads / s.num_kv_heads);
     // the vector-ALU kernel's 16-head state only fits one wave per SIMD
     if (p.kernel == SR_KERNEL_VALU && p.gp >= 16) p.waves = 4;
-    const int64_t cap = (s.seq_len + kMinSplitLen - 1) / kMinSplitLen;
     if (l.num_splits > 0) {
         const int64_t grid = n_items * l.num_splits;
         if (grid > INT32_MAX) return SR_ERR_UNSUPPORTED;
@@ -90,9 +89,13 @@ sr_status make_plan(const sr_shape& s, const sr_launch* launch, Plan& p) {
         int64_t grid = static_cast<int64_t>(per_cu) * cu_count();
         if (grid < n_items) grid = n_items;
         if (grid > INT32_MAX) return SR_ERR_UNSUPPORTED;
+        const int32_t kv_bytes = static_cast<int32_t>(elem_size(s));
+        const int32_t chunk = chunk_positions(p.kernel, s.head_dim, p.gp, p.waves, kv_bytes);
         p.fixed_splits = 0;
         p.grid = static_cast<int32_t>(grid);
-        p.split_cap = static_cast<int32_t>(cap < 1 ? 1 : cap);
+        p.split_cap = adaptive_split_cap(s.seq_len, chunk,
+                                         static_cast<int64_t>(chunk) * 2 * s.head_dim * kv_bytes,
+                                         merge_round_splits(s.head_dim, p.gp, p.waves), p.grid);
     }
     return SR_OK;
 }
@@ -466,6 +469,13 @@ int32_t sr_splits_for(const sr_shape* shape, const sr_launch* launch, int32_t n_
     Plan p;
     if (make_plan(*shape, launch, p) != SR_OK) return 0;
     return splits_for(p.fixed_splits, p.grid, p.split_cap, n_active);
+}
+
+int32_t sr_split_cap(const sr_shape* shape, const sr_launch* launch) {
+    if (check_shape(shape) != SR_OK) return 0;
+    Plan p;
+    if (make_plan(*shape, launch, p) != SR_OK) return 0;
+    return p.split_cap;
 }
 
 int32_t sr_plan_parts(const sr_shape* shape, const sr_launch* launch, int32_t n_active, int32_t wg,

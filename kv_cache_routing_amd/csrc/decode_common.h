@@ -293,6 +293,7 @@ __device__ inline void merge_splits(const DecodeArgs& a, const MergeJob& u, floa
     constexpr int SLOTS = NV >= NT ? NV / NT : 1;  // float4 slots per thread
     constexpr int PF = SLOTS >= 2 ? 16 : 32;       // splits prefetched per thread and slot
     constexpr int CH = PF * GROUPS;                // splits per chunk
+    static_assert(CH == merge_round_splits(D, GP, NW), "the host sizes lanes by this round");
     constexpr int SP = NT / GP;                    // splits one pass over (m, l) covers
     static_assert(NT % GP == 0 && NV % (NV >= NT ? NT : NV) == 0, "merge layout");
     static_assert(CH % SP == 0, "a chunk is whole (m, l) passes");

@@ -74,8 +74,6 @@ constexpr int32_t kMaxFusedHeads = 64;
 // Most workgroups the routing kernel spreads its scoring over.
 constexpr int32_t kRouteMaxWgs = 1024;
 
-// Adaptive mode never makes a split shorter than this many positions.
-constexpr int64_t kMinSplitLen = 512;
 // Launch defaults: wave64s per decode workgroup and workgroups per CU in
 // the adaptive grid.
 constexpr int kDefaultWaves = 4;
@@ -249,6 +247,47 @@ inline int32_t pad_group(int32_t g) {
     int32_t p = 1;
     while (p < g) p <<= 1;
     return p;
+}
+
+// Splits the last-arriver merge takes per memory round trip (merge_splits:
+// each thread holds PF accumulator slots of one split group in registers).
+constexpr int32_t merge_round_splits(int32_t d, int32_t gp, int32_t waves) {
+    const int32_t nt = waves * 64, nv = gp * d / 4;
+    const int32_t groups = nv >= nt ? 1 : nt / nv;
+    const int32_t slots = nv >= nt ? nv / nt : 1;
+    return (slots >= 2 ? 16 : 32) * groups;
+}
+
+// Adaptive mode's cap on lanes per item.  More lanes cut the chunks each
+// part streams; past a multiple of merge_round_splits they add a round trip
+// to the item's merge, which the last part to arrive runs alone.  Measured on
+// MI355X (sweeps of the lane count at 4K to 512K positions, one to four
+// active items, groups of 2 to 8 heads): a part streams a chunk at about
+// 36 GB/s, and each merge round costs about 3 us (its round trip plus the
+// partials through one CU).  The cap is the lane count S that minimises
+// ceil(C / S) chunk times plus ceil(S / round) round times, over the best
+// S of each round count (S = min(C, grid, rounds * round)); ties keep fewer
+// rounds.
+inline int32_t adaptive_split_cap(int64_t seq_len, int32_t chunk, int64_t chunk_bytes,
+                                  int32_t round, int32_t grid) {
+    constexpr double kChunkBytesPerUs = 36.0e3;  // one part's streaming rate
+    constexpr double kRoundUs = 3.0;             // one merge round
+    const int64_t chunks = (seq_len + chunk - 1) / chunk;
+    const int64_t top = chunks < grid ? chunks : grid;
+    if (top <= 1) return 1;
+    int64_t best_s = 1;
+    double best = 0.0;
+    for (int64_t r = 1;; ++r) {
+        const int64_t s = r * round < top ? r * round : top;
+        const double cost = static_cast<double>((chunks + s - 1) / s) * chunk_bytes /
+                                kChunkBytesPerUs + kRoundUs * static_cast<double>(r);
+        if (r == 1 || cost < best) {
+            best = cost;
+            best_s = s;
+        }
+        if (s == top) break;
+    }
+    return static_cast<int32_t>(best_s);
 }
 
 // Host launchers, one per translation unit.

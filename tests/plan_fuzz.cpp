@@ -33,8 +33,12 @@ int main(int argc, char** argv) {
         if (!fixed && grid64 < n_items) grid64 = n_items;
         if (grid64 > 0x7fffffffLL) continue;
         const int32_t grid = static_cast<int32_t>(grid64);
-        const int64_t cap64 = (T + kMinSplitLen - 1) / kMinSplitLen;
-        const int32_t cap = fixed ? fixed : static_cast<int32_t>(cap64 < 1 ? 1 : cap64);
+        const int32_t es = pick(0, 1) ? 2 : 4, gp = 1 << pick(0, 4), d = pick(0, 1) ? 64 : 128;
+        const int32_t round = merge_round_splits(d, gp, pick(0, 1) ? 4 : 8);
+        const int32_t cap = fixed ? fixed
+                                  : adaptive_split_cap(T, chunk, int64_t{chunk} * 2 * d * es, round, grid);
+        if (!fixed && (cap < 1 || cap > (T + chunk - 1) / chunk || cap > grid))
+            fail("cap out of range", cap, T);
         const int32_t n = static_cast<int32_t>(pick(0, n_items));
         const SplitPlan p = make_split_plan(fixed, grid, cap, n, T, chunk);
         if (n == 0) continue;

@@ -107,6 +107,37 @@ def test_launch_policy_checks():
     assert decode(s, launch=N.SrLaunch(0, 0, -1, 0)) == N.SR_ERR_INVALID_ARG
 
 
+def test_adaptive_split_cap_values():
+    # The lane count that minimises ceil(C / S) chunk times (32 KiB of bf16
+    # K and V per 64-position chunk at 36 GB/s: 0.91 us) plus one merge round
+    # (3 us) per started multiple of the merge's round size, capped by the
+    # chunk count and the grid (256 workgroups when no GPU is visible).
+    adaptive = N.SrLaunch(0, 0, 0, 0)
+    cases = [  # (Hq, Hkv, d, T, dtype, expected cap)
+        # 2048 chunks, rounds of 64: S = 64/128/192/256 cost 32.1/20.6/19.0/19.3 us
+        (32, 8, 128, 131072, N.SR_KV_BF16, 192),
+        # groups of 8, rounds of 32: S = 96/128/160 cost 29.0/26.6/26.8 us
+        (64, 8, 128, 131072, N.SR_KV_BF16, 128),
+        # one head per group, rounds of 256: one round reaches the grid
+        (8, 8, 128, 524288, N.SR_KV_BF16, 256),
+        # 64 fp32 chunks of 64 positions, rounds of 256: every chunk its own lane
+        (4, 2, 64, 4096, N.SR_KV_F32, 64),
+        (32, 8, 128, 100, N.SR_KV_BF16, 2),        # two chunks
+        (32, 8, 128, 1, N.SR_KV_BF16, 1),
+    ]
+    grid = N.lib.sr_grid_size(ctypes.byref(shape()), ctypes.byref(adaptive))
+    for Hq, Hkv, d, T, dt, want in cases:
+        s = shape(Hq=Hq, Hkv=Hkv, d=d, T=T, dt=dt)
+        got = N.lib.sr_split_cap(ctypes.byref(s), ctypes.byref(adaptive))
+        if grid == 256:
+            assert got == want, (Hq, d, T)
+        assert 1 <= got <= min(grid, max(1, T))
+    caps = [N.lib.sr_split_cap(ctypes.byref(shape(T=T)), ctypes.byref(adaptive))
+            for T in (64, 1000, 4096, 8192, 65536, 1 << 20)]
+    assert caps == sorted(caps)
+    assert N.lib.sr_split_cap(ctypes.byref(shape(Hq=33)), ctypes.byref(adaptive)) == 0
+
+
 def test_split_policy_host_math():
     s = shape(T=131072)
     fixed = N.SrLaunch(37, 0, 0, 0)
@@ -118,9 +149,12 @@ def test_split_policy_host_math():
     for n_act in (1, 2, 4, 8):
         S = N.lib.sr_splits_for(ctypes.byref(s), ctypes.byref(adaptive), n_act)
         assert 1 <= S and S * n_act <= grid
-        assert S <= -(-131072 // 512)
+        assert S <= N.lib.sr_split_cap(ctypes.byref(s), ctypes.byref(adaptive))
+    assert N.lib.sr_split_cap(ctypes.byref(s), ctypes.byref(fixed)) == 37
+    # 100 positions are two 64-position chunks: at most two lanes
     small = shape(T=100)
-    assert N.lib.sr_splits_for(ctypes.byref(small), ctypes.byref(adaptive), 1) == 1
+    assert N.lib.sr_split_cap(ctypes.byref(small), ctypes.byref(adaptive)) == 2
+    assert N.lib.sr_splits_for(ctypes.byref(small), ctypes.byref(adaptive), 1) == 2
 
 
 def test_workspace_grows_with_splits():
@@ -293,7 +327,8 @@ def test_plan_covers_every_chunk_once(kw, n_active, launch):
         wgs = sorted(w for _, _, w in ps)
         assert wgs == list(range(wgs[0], wgs[0] + count))  # parts are consecutive workgroups
     S = N.lib.sr_splits_for(ctypes.byref(s), ctypes.byref(lau), n_active)
-    balanced = launch[0] == 0 and n_active * S < grid and S < -(-kw["T"] // 512)
+    balanced = (launch[0] == 0 and n_active * S < grid
+                and S < N.lib.sr_split_cap(ctypes.byref(s), ctypes.byref(lau)))
     if balanced:
         assert len(per_wg) == grid and max(per_wg) - min(per_wg) <= 1
     else:  # one lane of one item per workgroup
@@ -359,7 +394,8 @@ def test_plan_random_layouts_tile_every_item():
             for a, b in zip(ps, ps[1:]):
                 assert a[4] == b[3] and b[0] == a[0] + 1
         S = N.lib.sr_splits_for(ctypes.byref(s), ctypes.byref(lau), n_act)
-        if fixed == 0 and n_act and n_act * S < grid and S < -(-T // 512):
+        if (fixed == 0 and n_act and n_act * S < grid
+                and S < N.lib.sr_split_cap(ctypes.byref(s), ctypes.byref(lau))):
             assert len(totals) == grid and max(totals) - min(totals) <= 1
 
 

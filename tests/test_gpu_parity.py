@@ -589,7 +589,8 @@ def test_balanced_division_full_parity(wl, kernel):
     grid = sr.grid_size(sr.make_shape(q, k, v), lau)
     n_act = wl.batch * (wl.num_kv_heads - wl.sink_plan[1])
     S = sr.splits_for(sr.make_shape(q, k, v), lau, n_act)
-    assert n_act * S < grid and S < -(-wl.seq_len // 512), "layer must divide in balanced mode"
+    cap = sr.split_cap(sr.make_shape(q, k, v), lau)
+    assert n_act * S < grid and S < cap, "layer must divide in balanced mode"
     got = full_check(layer, lau, check_dense=False)
     k0, v0 = sr.record_sink(k, v)
     fused, _ = sr.route_decode(q, k, v, k0, v0, wl.tau, launch=lau)
@@ -877,7 +878,7 @@ def _rope_step_check(case, planted):
     assert n_active == expect or not planted, f"{name}: planted routing gave {n_active} active"
     shape = sr.make_shape(qn_d, kB[:, :, :T], vB[:, :, :T])
     grid, lanes = sr.grid_size(shape, lau), sr.splits_for(shape, lau, n_active)
-    balanced = splits == 0 and n_active * lanes < grid and lanes < -(-T // 512)
+    balanced = splits == 0 and n_active * lanes < grid and lanes < sr.split_cap(shape, lau)
     log(f"{name}: n_active={n_active} grid={grid} lanes={lanes} balanced={balanced}")
     if name == "8b-balanced":
         assert balanced  # the appended row's owner found from the workgroup's range
