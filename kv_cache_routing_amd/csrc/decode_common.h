@@ -281,10 +281,12 @@ __device__ inline void write_alpha0(const DecodeArgs& a, int32_t b, int32_t g, i
 // reproducible for a given split count.
 //
 // Latency: every global load is issued before anything waits.  Each thread
-// first loads (m, l) of one (split, head) pair, then the accumulators of the
-// first CH splits; loads return in order, so the maxima wait only for the
-// (m, l) loads while the accumulators stream in.  A merge of up to SP splits
-// costs one memory round trip plus LDS work.
+// first loads (m, l) of its (split, head) pair in every pass over the splits
+// (up to MP passes, so up to MP * SP splits, in one run of loads), then the
+// accumulators of the first CH splits; loads return in order, so the maxima
+// wait only for the (m, l) loads while the accumulators stream in.  A merge
+// of up to CH splits costs one memory round trip plus LDS work; each further
+// CH splits cost one more round trip for their accumulators.
 template <int D, int GP, int NW>
 __device__ inline void merge_splits(const DecodeArgs& a, const MergeJob& u, float* out_item) {
     constexpr int NT = NW * 64;
@@ -295,11 +297,13 @@ __device__ inline void merge_splits(const DecodeArgs& a, const MergeJob& u, floa
     constexpr int CH = PF * GROUPS;                // splits per chunk
     static_assert(CH == merge_round_splits(D, GP, NW), "the host sizes lanes by this round");
     constexpr int SP = NT / GP;                    // splits one pass over (m, l) covers
+    constexpr int MP = 4;                          // (m, l) passes held in registers
+    constexpr int WS = MP * SP > CH ? MP * SP : CH;  // weights LDS holds
     static_assert(NT % GP == 0 && NV % (NV >= NT ? NT : NV) == 0, "merge layout");
     static_assert(CH % SP == 0, "a chunk is whole (m, l) passes");
     __shared__ float s_red[NW][GP];
     __shared__ float s_M[GP], s_L[GP];
-    __shared__ float s_w[CH][GP];
+    __shared__ float s_w[WS][GP];
     __shared__ float4 s_grp[GROUPS][GROUPS > 1 ? NV : 1];
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -319,14 +323,27 @@ __device__ inline void merge_splits(const DecodeArgs& a, const MergeJob& u, floa
     const int v0 = GROUPS > 1 ? t % NV : t;
     const int hm = t % GP, sm = t / GP;  // this thread's (head, split) in every (m, l) pass
 
-    // (m, l) of split sm, z0 of split 0 (position 0's logit), then the
-    // accumulators of the first chunk.  No load sits under a branch: indexes
+    // (m, l) of splits sm, sm + SP, ... (the passes the split count has, at
+    // most MP; the pass count is the same in every thread, so the branches
+    // are uniform), z0 of split 0 (position 0's logit), then the accumulators
+    // of the first chunk.  No load depends on a per-lane condition: indexes
     // past the last split are clamped to it and the values masked (weight 0),
     // so the loads form one straight run and each wait counts exactly the
     // loads it needs.
-    const int sm_c = sm < S ? sm : S - 1;
-    float m_first = ml0[static_cast<int64_t>(sm_c) * 3 * GP + hm];
-    float l_first = ml0[static_cast<int64_t>(sm_c) * 3 * GP + GP + hm];
+    const int np = (S + SP - 1) / SP;
+    const bool in_regs = np <= MP;  // every split's weight fits in LDS at once
+    float mv[MP], lv[MP];
+#pragma unroll
+    for (int p = 0; p < MP; ++p) {
+        mv[p] = kNegInf;
+        lv[p] = 0.f;
+        if (p < np) {
+            const int s = sm + p * SP;
+            const int64_t o = static_cast<int64_t>(s < S ? s : S - 1) * 3 * GP;
+            mv[p] = ml0[o + hm];
+            lv[p] = ml0[o + GP + hm];
+        }
+    }
     const float z0 = ml0[2 * GP + (t < G ? t : 0)];
     float4 pre[SLOTS][PF];
     auto fetch = [&](int c0) {
@@ -339,10 +356,12 @@ __device__ inline void merge_splits(const DecodeArgs& a, const MergeJob& u, floa
             }
     };
     fetch(0);
-    if (sm >= S) {
-        m_first = kNegInf;
-        l_first = 0.f;
-    }
+#pragma unroll
+    for (int p = 0; p < MP; ++p)
+        if (sm + p * SP >= S) {
+            mv[p] = kNegInf;
+            lv[p] = 0.f;
+        }
 
     // Sum (or max) over the threads that hold head hm: lanes l, l ^ GP, ...
     // within the wave, then the waves in ascending order.
@@ -361,34 +380,55 @@ __device__ inline void merge_splits(const DecodeArgs& a, const MergeJob& u, floa
         __syncthreads();
     };
 
-    float mx = m_first;
-    for (int s = sm + SP; s < S; s += SP) mx = fmaxf(mx, ml0[static_cast<int64_t>(s) * 3 * GP + hm]);
+    float mx = mv[0];
+#pragma unroll
+    for (int p = 1; p < MP; ++p) mx = fmaxf(mx, mv[p]);
+    for (int s = sm + MP * SP; s < S; s += SP)
+        mx = fmaxf(mx, ml0[static_cast<int64_t>(s) * 3 * GP + hm]);
     head_reduce(mx, true, s_M);
     const float M = s_M[hm];
 
     float4 acc[SLOTS];
 #pragma unroll
     for (int j = 0; j < SLOTS; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    // The weights: all of them at once from the registers, or (more than MP
+    // passes) chunk by chunk, reloading (m, l).  Either way each thread adds
+    // its w_s l_s in ascending s.
     float lw = 0.f;
-    for (int c0 = 0; c0 < S; c0 += CH) {
-        if (c0 > 0) fetch(c0);
-        const int n = S - c0 < CH ? S - c0 : CH;
+    if (in_regs) {
 #pragma unroll
-        for (int p = 0; p < CH / SP; ++p) {
-            const int s = p * SP + sm;  // split index within the chunk
-            if (s < n) {
-                float m = m_first, l = l_first;
-                if (c0 + p > 0) {
-                    const float* q = ml0 + static_cast<int64_t>(c0 + s) * 3 * GP;
-                    m = q[hm];
-                    l = q[GP + hm];
-                }
-                const float w = merge_weight(m, M);
+        for (int p = 0; p < MP; ++p) {
+            const int s = p * SP + sm;
+            if (s < S) {
+                const float w = merge_weight(mv[p], M);
                 s_w[s][hm] = w;
-                lw += w * l;
+                lw += w * lv[p];
             }
         }
         __syncthreads();
+    }
+    for (int c0 = 0; c0 < S; c0 += CH) {
+        if (c0 > 0) fetch(c0);
+        const int n = S - c0 < CH ? S - c0 : CH;
+        if (!in_regs) {
+#pragma unroll
+            for (int p = 0; p < CH / SP; ++p) {
+                const int s = p * SP + sm;  // split index within the chunk
+                if (s < n) {
+                    float m = mv[0], l = lv[0];
+                    if (c0 + p > 0) {
+                        const float* q = ml0 + static_cast<int64_t>(c0 + s) * 3 * GP;
+                        m = q[hm];
+                        l = q[GP + hm];
+                    }
+                    const float w = merge_weight(m, M);
+                    s_w[s][hm] = w;
+                    lw += w * l;
+                }
+            }
+            __syncthreads();
+        }
+        const int wo = in_regs ? c0 : 0;  // where this chunk's weights sit in LDS
 #pragma unroll
         for (int j = 0; j < SLOTS; ++j) {
             const int h = (4 * (v0 + j * NT)) / D;
@@ -396,7 +436,7 @@ __device__ inline void merge_splits(const DecodeArgs& a, const MergeJob& u, floa
 #pragma unroll
             for (int k = 0; k < PF; ++k) {
                 const int s = gi + GROUPS * k;  // splits past S carry zeros and weight 0
-                const float w = s < n ? s_w[s][h] : 0.f;
+                const float w = s < n ? s_w[wo + s][h] : 0.f;
                 r.x += w * pre[j][k].x;
                 r.y += w * pre[j][k].y;
                 r.z += w * pre[j][k].z;
@@ -404,7 +444,7 @@ __device__ inline void merge_splits(const DecodeArgs& a, const MergeJob& u, floa
             }
             acc[j] = r;
         }
-        __syncthreads();
+        if (!in_regs) __syncthreads();  // the next chunk rewrites the weights
     }
     head_reduce(lw, false, s_L);
     if (t < G && a.alpha0_out) write_alpha0(a, u.b, u.g, t, z0, s_M[t], s_L[t]);
