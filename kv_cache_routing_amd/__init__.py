@@ -29,12 +29,21 @@ __all__ = ["record_sink", "route", "decode_attn", "route_decode", "dense_decode"
            "SR_KERNEL_AUTO", "SR_KERNEL_VALU", "SR_KERNEL_MFMA"]
 
 
+# Every call below runs these on the host before its launch, so they are kept
+# lean: the ctypes signatures convert plain ints and floats, and torch's raw
+# stream getter (where it exists) skips building a Stream object, which alone
+# cost ~3 us a call; a small layer's eager step is bound by this host time.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _ptr(t: torch.Tensor | None):
-    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+    return 0 if t is None else t.data_ptr()
 
 
 def _stream():
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if _raw_stream is not None:
+        return _raw_stream(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _need_cuda(*ts):
@@ -64,21 +73,22 @@ def _expect_q(q: torch.Tensor, k: torch.Tensor):
 
 def make_shape(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None = None) -> N.SrShape:
     """sr_shape from q [B][Hq][d] and a cache view [B][Hkv][T][d]."""
-    if k.dim() != 4:
+    ks, st, dtype = k.shape, k.stride(), k.dtype
+    if len(ks) != 4:
         raise ValueError("cache must be [B][Hkv][T][d]")
-    if v is not None and (v.shape != k.shape or v.stride() != k.stride() or v.dtype != k.dtype):
+    if v is not None and (v.shape != ks or v.stride() != st or v.dtype != dtype):
         raise ValueError("K and V caches must share shape, strides and dtype")
-    if k.stride(3) != 1:
+    if st[3] != 1:
         raise ValueError("head_dim must be contiguous")
-    if k.dtype == torch.bfloat16:
+    if dtype == torch.bfloat16:
         dt = N.SR_KV_BF16
-    elif k.dtype == torch.float32:
+    elif dtype == torch.float32:
         dt = N.SR_KV_F32
     else:
-        raise ValueError(f"unsupported cache dtype {k.dtype}")
-    B, Hkv, T, d = k.shape
+        raise ValueError(f"unsupported cache dtype {dtype}")
+    B, Hkv, T, d = ks
     Hq = q.shape[1] if q is not None else Hkv
-    return N.SrShape(B, Hq, Hkv, d, T, k.stride(0), k.stride(1), k.stride(2), dt, 0)
+    return N.SrShape(B, Hq, Hkv, d, T, st[0], st[1], st[2], dt, 0)
 
 
 def make_launch(num_splits: int = 0, kernel: int = SR_KERNEL_AUTO, wgs_per_cu: int = 0,
@@ -194,14 +204,15 @@ def route(q: torch.Tensor, k0: torch.Tensor, tau: float = 0.5, out: Routing | No
                       torch.empty((B, Hkv), dtype=torch.uint8, device=dev),
                       torch.empty((B * Hkv,), dtype=torch.int32, device=dev),
                       torch.empty((1,), dtype=torch.int32, device=dev))
-    N.check(N.lib.sr_route(ctypes.byref(shape), _ptr(q), _ptr(k0), ctypes.c_float(tau),
+    N.check(N.lib.sr_route(ctypes.byref(shape), _ptr(q), _ptr(k0), float(tau),
                            _ptr(out.scores), _ptr(out.mask), _ptr(out.work_list),
                            _ptr(out.n_active), _stream()), "sr_route")
     return out
 
 
-def _prep(q, k, v, launch, ws, out):
-    _expect_q(q, k)
+def _prep(q, k, v, launch, ws, out, q_checked=False):
+    if not q_checked:
+        _expect_q(q, k)
     if out is not None:
         _expect(out, "out", q.shape, torch.float32)
     _need_cuda(q, k, v)
@@ -221,10 +232,10 @@ def decode_attn(q, k, v, v0, work_list, n_active, sm_scale: float = 0.0,
     _expect(v0, "v0", (B, Hkv, d), torch.float32)
     _expect(work_list, "work_list", (B * Hkv,), torch.int32)
     _expect(n_active, "n_active", (1,), torch.int32)
-    shape, ws, out = _prep(q, k, v, launch, ws, out)
+    shape, ws, out = _prep(q, k, v, launch, ws, out, q_checked=True)
     N.check(N.lib.sr_decode_attn(ctypes.byref(shape), _lp(launch), _ptr(q), _ptr(k), _ptr(v),
                                  _ptr(v0), _ptr(work_list), _ptr(n_active),
-                                 ctypes.c_float(sm_scale), _ptr(ws.buf), ws.nbytes, _ptr(out),
+                                 float(sm_scale), _ptr(ws.buf), ws.nbytes, _ptr(out),
                                  _stream()), "sr_decode_attn")
     return out
 
@@ -240,7 +251,7 @@ def route_decode(q, k, v, k0, v0, tau: float = 0.5, sm_scale: float = 0.0,
     _expect(v0, "v0", (B, Hkv, d), torch.float32)
     if routing is not None:
         _expect_routing(routing, B, q.shape[1], Hkv)
-    shape, ws, out = _prep(q, k, v, launch, ws, out)
+    shape, ws, out = _prep(q, k, v, launch, ws, out, q_checked=True)
     if routing is None:
         dev = q.device
         routing = Routing(torch.empty((B, q.shape[1]), dtype=torch.float32, device=dev),
@@ -248,7 +259,7 @@ def route_decode(q, k, v, k0, v0, tau: float = 0.5, sm_scale: float = 0.0,
                           torch.empty((B * Hkv,), dtype=torch.int32, device=dev),
                           torch.empty((1,), dtype=torch.int32, device=dev))
     N.check(N.lib.sr_route_decode(ctypes.byref(shape), _lp(launch), _ptr(q), _ptr(k), _ptr(v),
-                                  _ptr(k0), _ptr(v0), ctypes.c_float(tau), ctypes.c_float(sm_scale),
+                                  _ptr(k0), _ptr(v0), float(tau), float(sm_scale),
                                   _ptr(routing.scores), _ptr(routing.mask),
                                   _ptr(routing.work_list), _ptr(routing.n_active), _ptr(ws.buf),
                                   ws.nbytes, _ptr(out), _stream()), "sr_route_decode")
@@ -274,7 +285,7 @@ def rope_route_decode(q_new, k_new, v_new, k, v, k0, v0, inv_freq, tau: float = 
         _expect(q_out, "q_out", q_new.shape, torch.float32)
     if routing is not None:
         _expect_routing(routing, B, q_new.shape[1], Hkv)
-    shape, ws, out = _prep(q_new, k, v, launch, ws, out)
+    shape, ws, out = _prep(q_new, k, v, launch, ws, out, q_checked=True)
     _need_cuda(k_new, v_new, k0, v0, inv_freq)
     dev = q_new.device
     if q_out is None:
@@ -286,8 +297,8 @@ def rope_route_decode(q_new, k_new, v_new, k, v, k0, v0, inv_freq, tau: float = 
                           torch.empty((1,), dtype=torch.int32, device=dev))
     N.check(N.lib.sr_rope_route_decode(
         ctypes.byref(shape), _lp(launch), _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(inv_freq),
-        _ptr(q_out), _ptr(k), _ptr(v), _ptr(k0), _ptr(v0), ctypes.c_float(tau),
-        ctypes.c_float(sm_scale), _ptr(routing.scores), _ptr(routing.mask),
+        _ptr(q_out), _ptr(k), _ptr(v), _ptr(k0), _ptr(v0), float(tau),
+        float(sm_scale), _ptr(routing.scores), _ptr(routing.mask),
         _ptr(routing.work_list), _ptr(routing.n_active), _ptr(ws.buf), ws.nbytes, _ptr(out),
         _stream()), "sr_rope_route_decode")
     return out, routing, q_out
@@ -299,7 +310,7 @@ def dense_decode_alpha0(q, k, v, sm_scale: float = 0.0, launch: N.SrLaunch | Non
     shape, ws, out = _prep(q, k, v, launch, ws, out)
     alpha0 = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
     N.check(N.lib.sr_dense_decode_alpha0(ctypes.byref(shape), _lp(launch), _ptr(q), _ptr(k),
-                                         _ptr(v), ctypes.c_float(sm_scale), _ptr(ws.buf),
+                                         _ptr(v), float(sm_scale), _ptr(ws.buf),
                                          ws.nbytes, _ptr(out), _ptr(alpha0), _stream()),
             "sr_dense_decode_alpha0")
     return out, alpha0
@@ -309,6 +320,6 @@ def dense_decode(q, k, v, sm_scale: float = 0.0, launch: N.SrLaunch | None = Non
                  ws: Workspace | None = None, out: torch.Tensor | None = None):
     shape, ws, out = _prep(q, k, v, launch, ws, out)
     N.check(N.lib.sr_dense_decode(ctypes.byref(shape), _lp(launch), _ptr(q), _ptr(k), _ptr(v),
-                                  ctypes.c_float(sm_scale), _ptr(ws.buf), ws.nbytes, _ptr(out),
+                                  float(sm_scale), _ptr(ws.buf), ws.nbytes, _ptr(out),
                                   _stream()), "sr_dense_decode")
     return out
