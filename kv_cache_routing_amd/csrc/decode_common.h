@@ -297,7 +297,7 @@ __device__ inline void merge_splits(const DecodeArgs& a, const MergeJob& u, floa
     constexpr int CH = PF * GROUPS;                // splits per chunk
     static_assert(CH == merge_round_splits(D, GP, NW), "the host sizes lanes by this round");
     constexpr int SP = NT / GP;                    // splits one pass over (m, l) covers
-    constexpr int MP = 4;                          // (m, l) passes held in registers
+    constexpr int MP = 2;                          // (m, l) passes held in registers
     constexpr int WS = MP * SP > CH ? MP * SP : CH;  // weights LDS holds
     static_assert(NT % GP == 0 && NV % (NV >= NT ? NT : NV) == 0, "merge layout");
     static_assert(CH % SP == 0, "a chunk is whole (m, l) passes");
