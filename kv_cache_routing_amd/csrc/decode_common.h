@@ -405,7 +405,9 @@ __device__ inline void merge_splits(const DecodeArgs& a, const MergeJob& u, floa
                 lw += w * lv[p];
             }
         }
-        __syncthreads();
+        // The sums L_h now, while the accumulators are still arriving (its
+        // barrier also publishes the weights).
+        head_reduce(lw, false, s_L);
     }
     for (int c0 = 0; c0 < S; c0 += CH) {
         if (c0 > 0) fetch(c0);
@@ -446,7 +448,7 @@ __device__ inline void merge_splits(const DecodeArgs& a, const MergeJob& u, floa
         }
         if (!in_regs) __syncthreads();  // the next chunk rewrites the weights
     }
-    head_reduce(lw, false, s_L);
+    if (!in_regs) head_reduce(lw, false, s_L);
     if (t < G && a.alpha0_out) write_alpha0(a, u.b, u.g, t, z0, s_M[t], s_L[t]);
     if constexpr (GROUPS > 1) {
         s_grp[gi][v0] = acc[0];
