@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "sinkroute.h"
@@ -275,12 +276,18 @@ inline int32_t adaptive_split_cap(int64_t seq_len, int32_t chunk, int64_t chunk_
     const int64_t chunks = (seq_len + chunk - 1) / chunk;
     const int64_t top = chunks < grid ? chunks : grid;
     if (top <= 1) return 1;
+    // The continuous optimum is near r* = sqrt(C * chunk time / (round * round
+    // time)); round counts up to about twice that cover the discrete one and
+    // keep the search short on huge grids and caches.
+    const double chunk_us = static_cast<double>(chunk_bytes) / kChunkBytesPerUs;
+    const int64_t r_max = 2 + static_cast<int64_t>(
+        2.0 * sqrt(static_cast<double>(chunks) * chunk_us / (static_cast<double>(round) * kRoundUs)));
     int64_t best_s = 1;
     double best = 0.0;
-    for (int64_t r = 1;; ++r) {
+    for (int64_t r = 1; r <= r_max; ++r) {
         const int64_t s = r * round < top ? r * round : top;
-        const double cost = static_cast<double>((chunks + s - 1) / s) * chunk_bytes /
-                                kChunkBytesPerUs + kRoundUs * static_cast<double>(r);
+        const double cost = static_cast<double>((chunks + s - 1) / s) * chunk_us +
+                            kRoundUs * static_cast<double>(r);
         if (r == 1 || cost < best) {
             best = cost;
             best_s = s;

@@ -136,6 +136,14 @@ def test_adaptive_split_cap_values():
             for T in (64, 1000, 4096, 8192, 65536, 1 << 20)]
     assert caps == sorted(caps)
     assert N.lib.sr_split_cap(ctypes.byref(shape(Hq=33)), ctypes.byref(adaptive)) == 0
+    # a huge grid and cache: the search stays short and the cap in range
+    import time
+    huge = shape(T=(1 << 31) - 1)
+    big_grid = N.SrLaunch(0, 0, 1 << 20, 0)
+    t0 = time.perf_counter()
+    cap = N.lib.sr_split_cap(ctypes.byref(huge), ctypes.byref(big_grid))
+    assert time.perf_counter() - t0 < 0.05
+    assert 1 <= cap <= N.lib.sr_grid_size(ctypes.byref(huge), ctypes.byref(big_grid))
 
 
 def test_split_policy_host_math():
