@@ -213,20 +213,23 @@ __device__ inline void partition_flags(const uint8_t* flags, int32_t n_items, in
 }
 
 // The fused prologue's decisions for a layer of at most 64 items (B*Hq
-// heads of G per item), by NT threads: returns the 64-bit mask of sink items
-// (bit j set: every head of item j has cos >= tau), the same in every wave.
-// Each head leaves its pass flag in s_pass[head] (one byte per head, so
-// nothing needs clearing first); after one barrier, lane j of every wave ANDs
-// item j's G flags (all read before the first test) and a ballot gathers
-// them.  Scores are written when `scores` is non-null.
+// heads of G per item, at most 64), by NT threads: returns the 64-bit mask of
+// sink items (bit j set: every head of item j has cos >= tau), the same in
+// every wave.  Lane group k of wave w scores heads base + 4w + k + r*GROUPS,
+// so one ballot per round gives the wave four consecutive heads' pass bits;
+// each wave keeps a 64-bit mask of its heads' passes, leaves it in
+// s_bits[wave], and after one barrier every thread ORs the NT/64 masks and
+// lane j tests item j's G bits; a ballot gathers the items.  Scores are
+// written when `scores` is non-null.
 template <int NT, int U>
 __device__ __attribute__((always_inline)) inline uint64_t fused_sink_mask(const float* __restrict__ q,
                                            const float* __restrict__ k0, float tau,
                                            int32_t n_items, int32_t G, int32_t d,
-                                           uint8_t* s_pass, float* scores) {
-    constexpr int GROUPS = NT / 16;
-    const int tid = threadIdx.x, hl = tid & 15, hg = tid >> 4, lane = tid & 63;
+                                           uint64_t* s_bits, float* scores) {
+    constexpr int GROUPS = NT / 16, NW = NT / 64;
+    const int tid = threadIdx.x, hl = tid & 15, hg = tid >> 4, lane = tid & 63, wave = tid >> 6;
     const int32_t n_heads = n_items * G;
+    uint64_t mine = 0;  // pass bits of the heads this wave scored (the same in every lane)
     // Each lane group takes heads hg, hg + GROUPS, ...; a round issues the
     // loads of only as many head slots as the round has live (1, 2, 4 or U),
     // since every slot's loads go out unconditionally.
@@ -237,10 +240,12 @@ __device__ __attribute__((always_inline)) inline uint64_t fused_sink_mask(const 
 #pragma unroll
         for (int r = 0; r < V; ++r) {
             const int32_t hh = base + hg + r * GROUPS;
-            if (hh < n_heads && hl == 0) {
-                if (scores) scores[hh] = c[r];
-                s_pass[hh] = c[r] >= tau ? 1 : 0;  // NaN fails: the head dissents
-            }
+            if (scores && hh < n_heads && hl == 0) scores[hh] = c[r];
+            // lanes 0, 16, 32, 48 hold heads first .. first + 3; NaN fails: the head dissents
+            const uint64_t b = __ballot(hl == 0 && hh < n_heads && c[r] >= tau);
+            const uint64_t nib = (b & 1u) | ((b >> 15) & 2u) | ((b >> 30) & 4u) | ((b >> 45) & 8u);
+            const int32_t first = base + 4 * wave + r * GROUPS;
+            if (first < 64) mine |= nib << first;
         }
     };
     for (int32_t base = 0; base < n_heads; base += GROUPS * U) {
@@ -250,16 +255,14 @@ __device__ __attribute__((always_inline)) inline uint64_t fused_sink_mask(const 
         else if (n_live <= 4 && U > 4) round(std::integral_constant<int, 4>{}, base, n_live);
         else round(std::integral_constant<int, U>{}, base, n_live);
     }
+    if (lane == 0) s_bits[wave] = mine;
     __syncthreads();
-    bool sink = false;
-    if (lane < n_items) {
-        uint8_t f[16];  // G <= 16
+    uint64_t heads = 0;
 #pragma unroll
-        for (int h = 0; h < 16; ++h) f[h] = s_pass[lane * G + (h < G ? h : 0)];
-        sink = true;
-#pragma unroll
-        for (int h = 0; h < 16; ++h) sink = sink & (f[h] != 0);
-    }
+    for (int w = 0; w < NW; ++w) heads |= s_bits[w];
+    const uint64_t gmask = (G >= 64 ? 0ull : (1ull << G)) - 1ull;  // G <= 16
+    const int32_t at = lane < n_items ? lane * G : 0;
+    const bool sink = lane < n_items && ((heads >> at) & gmask) == gmask;
     return __ballot(sink);
 }
 
@@ -408,7 +411,7 @@ __device__ inline bool map_work(const DecodeArgs& a, WorkRange& r) {
         // scalar registers, with no further barrier
         static_assert(kMaxFusedHeads <= 64, "one ballot covers every item");
         static_assert(kMaxFusedHeads <= 4 * (NT / 16), "one round of at most 4 heads per group");
-        __shared__ uint8_t s_pass[kMaxFusedHeads];
+        __shared__ uint64_t s_bits[NT / 64];
         const bool w0 = wg == 0;
         double *s_c = nullptr, *s_s = nullptr;
         if (a.rope) r.q = rope_queries<D, NT>(a, s_c, s_s);
@@ -418,7 +421,7 @@ __device__ inline bool map_work(const DecodeArgs& a, WorkRange& r) {
             const int lane = threadIdx.x & 63;
             sinks = __ballot(lane < n_items && a.flags_in[lane] != 0) & all;
         } else {
-            sinks = fused_sink_mask<NT, 4>(r.q, a.k0, a.tau, n_items, G, D, s_pass,
+            sinks = fused_sink_mask<NT, 4>(r.q, a.k0, a.tau, n_items, G, D, s_bits,
                                            w0 ? a.scores_out : nullptr) & all;
         }
         const uint64_t act = all & ~sinks;

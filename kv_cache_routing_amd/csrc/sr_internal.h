@@ -68,8 +68,9 @@ __host__ __device__ constexpr size_t rope_lds_bytes(int32_t q_rows, int32_t d) {
 // scores every head) only for layers of up to this many query heads; larger
 // layers run the routing kernel and then the decode, which measured faster
 // (a prologue that scores 128 heads per workgroup already costs more than
-// the extra launch).  The fused prologue keeps one flag per item in LDS and
-// partitions the items in one ballot pass, so it needs items <= heads <= 64.
+// the extra launch).  The fused prologue keeps one pass bit per head in a
+// 64-bit mask and partitions the items in one ballot pass, so it needs
+// items <= heads <= 64.
 constexpr int32_t kMaxFusedHeads = 64;
 
 // Most workgroups the routing kernel spreads its scoring over.
