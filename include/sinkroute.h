@@ -167,17 +167,20 @@ sr_status sr_rope_append(const sr_shape* shape, const float* q_new, const float*
                          void* k_cache, void* v_cache, void* stream);
 
 /* Bytes of scratch the decode calls need for this shape and launch policy:
- * partial results of up to grid + B*Hkv parts (m, l, the position-0 logit
- * and acc, fp32), one ticket per item, and, for sr_route_decode on large
- * layers, the routing kernel's ticket and room for a work list, a count and
- * one flag byte per group.
+ * a ticket region of fixed size at the start (one 32-bit ticket for each of
+ * the envelope's 32768 items, then the routing kernel's ticket: 131,328
+ * bytes with padding), partial results of up to grid + B*Hkv parts (m, l,
+ * the position-0 logit and acc, fp32), and, for sr_route_decode on large
+ * layers, room for a work list, a count and one flag byte per group.
  * Depends on the current device's CU count in adaptive mode. Returns 0 on an
  * invalid or unsupported shape. */
 size_t sr_workspace_bytes(const sr_shape* shape, const sr_launch* launch);
 
 /* Zero a new workspace once (the tickets).  Every decode call leaves the
- * tickets it used back at zero, so a workspace is reusable as is.  Two
- * calls that may run at the same time must not share a workspace. */
+ * tickets it used back at zero, and the tickets sit at the same offsets for
+ * every shape and launch policy, so a workspace is reusable as is by any
+ * later call, of any shape, whose sr_workspace_bytes it covers.  Two calls
+ * that may run at the same time must not share a workspace. */
 sr_status sr_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Routed decode (README decode-time steps; paper Eq. (1)).

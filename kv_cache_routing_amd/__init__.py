@@ -210,6 +210,23 @@ def route(q: torch.Tensor, k0: torch.Tensor, tau: float = 0.5, out: Routing | No
     return out
 
 
+# The workspaces calls use when the caller passes none: one per (device,
+# stream), replaced by a larger one when a layer needs more, so that repeated
+# calls neither allocate nor clear scratch.  Calls on one stream run in order
+# and each leaves its tickets at zero, so the next call may reuse the
+# workspace; calls on different streams get different ones.
+_default_ws: dict = {}
+
+
+def _workspace_for(shape, launch, device):
+    key = (device.index, _stream())
+    ws = _default_ws.get(key)
+    if ws is None or not ws.fits(shape, launch):
+        ws = Workspace(shape, launch, device)
+        _default_ws[key] = ws
+    return ws
+
+
 def _prep(q, k, v, launch, ws, out, q_checked=False):
     if not q_checked:
         _expect_q(q, k)
@@ -217,7 +234,9 @@ def _prep(q, k, v, launch, ws, out, q_checked=False):
         _expect(out, "out", q.shape, torch.float32)
     _need_cuda(q, k, v)
     shape = make_shape(q, k, v)
-    if ws is None or not ws.fits(shape, launch):
+    if ws is None:
+        ws = _workspace_for(shape, launch, q.device)
+    elif not ws.fits(shape, launch):
         ws = Workspace(shape, launch, q.device)
     if out is None:
         out = torch.empty_like(q)

@@ -102,17 +102,26 @@ sr_status make_plan(const sr_shape& s, const sr_launch* launch, Plan& p) {
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// A workspace (the caller's, or the library's own array for callers that
+// cannot allocate) starts with a ticket region of fixed size: one ticket per
+// item for the largest layer the envelope allows, then the routing kernel's
+// ticket.  The tickets sit at the same offsets whatever the shape and launch,
+// and nothing else is ever stored there, so every call finds them at zero
+// (zeroed once, and each call leaves the tickets it took back at zero) and a
+// workspace serves any later call whose size it covers.  The partials and the
+// routing region that follow are written before they are read.
+constexpr size_t kTicketBytes = align256((kMaxItems + 1) * sizeof(uint32_t));
+
 struct WsLayout {
-    size_t tickets, ml, acc, route, total;
+    size_t ml, acc, route, total;
 };
 
 // Where one decode call keeps its scratch: the per-item tickets and the
-// routing kernel's ticket (zero between calls: every call leaves them at zero),
-// the partials, and the routing list, count and flags of sr_route_decode's
-// two-launch form.
+// routing kernel's ticket, the partials, and the routing list, count and
+// flags of sr_route_decode's two-launch form.
 struct Scratch {
-    uint32_t* tickets;       // [B*Hkv]
-    uint32_t* route_ticket;  // [1]
+    uint32_t* tickets;       // [B*Hkv] of the region's kMaxItems
+    uint32_t* route_ticket;  // [1], after the item tickets
     float* part_ml;
     float* part_acc;
     int32_t* route_list;     // [B*Hkv + 1]: list, then n_active
@@ -122,46 +131,38 @@ struct Scratch {
 WsLayout ws_layout(const sr_shape& s, const Plan& p) {
     const size_t n_items = static_cast<size_t>(s.batch) * s.num_kv_heads;
     WsLayout w;
-    w.tickets = 0;
-    w.ml = align256(n_items * sizeof(uint32_t));
+    w.ml = kTicketBytes;
     const size_t parts = static_cast<size_t>(p.grid) + n_items;  // slots w + i, w < grid, i < n
     w.acc = w.ml + align256(parts * 3 * p.gp * sizeof(float));
-    // sr_route_decode's two-launch form: work list, n_active and ticket
-    // [n_items + 2] int32, then one flag byte per item; the routing kernel's
-    // ticket lives here, the rest serves callers that do not ask for the list,
-    // the count or the mask
+    // sr_route_decode's two-launch form: work list and n_active [n_items + 1]
+    // int32, then one flag byte per item, for callers that do not ask for the
+    // list, the count or the mask
     w.route = w.acc + align256(parts * p.gp * s.head_dim * sizeof(float));
-    w.total = w.route + align256((n_items + 2) * sizeof(int32_t) + n_items);
+    w.total = w.route + align256((n_items + 1) * sizeof(int32_t) + n_items);
     return w;
 }
 
-// The caller's workspace: tickets first, then the partials and the routing
-// region [list | n_active | routing ticket | flags].
-Scratch scratch_in_workspace(const sr_shape& s, const WsLayout& w, void* ws) {
+Scratch scratch_at(const sr_shape& s, const WsLayout& w, void* ws) {
     const size_t n_items = static_cast<size_t>(s.batch) * s.num_kv_heads;
     char* base = static_cast<char*>(ws);
     Scratch c;
-    c.tickets = reinterpret_cast<uint32_t*>(base + w.tickets);
+    c.tickets = reinterpret_cast<uint32_t*>(base);
+    c.route_ticket = c.tickets + kMaxItems;
     c.part_ml = reinterpret_cast<float*>(base + w.ml);
     c.part_acc = reinterpret_cast<float*>(base + w.acc);
     c.route_list = reinterpret_cast<int32_t*>(base + w.route);
-    c.route_ticket = reinterpret_cast<uint32_t*>(c.route_list + n_items + 1);
-    c.route_flags = reinterpret_cast<uint8_t*>(c.route_list + n_items + 2);
+    c.route_flags = reinterpret_cast<uint8_t*>(c.route_list + n_items + 1);
     return c;
 }
 
 // ---------------------------------------------------------------------------
 // Library-owned scratch of sr_route_decode_static, for callers that cannot
 // allocate.  One array per device (each GPU the library runs on holds its own
-// copy until the process ends): a ticket region sized for the largest layer
-// the envelope allows, the routing kernel's ticket, then the rest of a
-// workspace of up to SR_STATIC_SCRATCH_BYTES.  The ticket region is used for
-// nothing else, so a call of any shape finds its tickets at zero: they are
-// zeroed once at set-up and every call leaves them at zero.  Calls that
-// overlap on one device share the array and race.
-constexpr size_t kStaticTicketBytes = align256(kMaxItems * sizeof(uint32_t) + sizeof(uint32_t));
-constexpr size_t kStaticScratchBytes = kStaticTicketBytes + SR_STATIC_SCRATCH_BYTES;
-static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+// copy until the process ends) with the workspace layout, of
+// SR_STATIC_SCRATCH_BYTES: its ticket region is zeroed once at set-up and
+// every call leaves it at zero.  Calls that overlap on one device share the
+// array and race.
+static __device__ __align__(256) unsigned char scratch[SR_STATIC_SCRATCH_BYTES];
 
 std::mutex g_scratch_mu;
 std::atomic<char*> g_scratch[kMaxDevices];  // device address of `scratch`, per device
@@ -180,23 +181,10 @@ sr_status static_scratch(hipStream_t st, char*& out) {
     if (out) return SR_OK;
     void* ptr = nullptr;
     if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SR_ERR_HIP;
-    if (launch_zero(ptr, kStaticTicketBytes, st) != hipSuccess) return SR_ERR_HIP;
+    if (launch_zero(ptr, kTicketBytes, st) != hipSuccess) return SR_ERR_HIP;
     out = static_cast<char*>(ptr);
     g_scratch[dev].store(out, std::memory_order_release);
     return SR_OK;
-}
-
-Scratch scratch_in_static(const sr_shape& s, const WsLayout& w, char* base) {
-    const size_t n_items = static_cast<size_t>(s.batch) * s.num_kv_heads;
-    char* rest = base + kStaticTicketBytes;  // the workspace layout from its partials on
-    Scratch c;
-    c.tickets = reinterpret_cast<uint32_t*>(base);
-    c.route_ticket = reinterpret_cast<uint32_t*>(base) + kMaxItems;
-    c.part_ml = reinterpret_cast<float*>(rest);
-    c.part_acc = reinterpret_cast<float*>(rest + (w.acc - w.ml));
-    c.route_list = reinterpret_cast<int32_t*>(rest + (w.route - w.ml));
-    c.route_flags = reinterpret_cast<uint8_t*>(c.route_list + n_items + 2);
-    return c;
 }
 
 struct FusedRoute {
@@ -259,16 +247,14 @@ sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float
     if ((st = make_plan(s, launch, p)) != SR_OK) return st;
     const WsLayout w = ws_layout(s, p);
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    Scratch sc;
+    char* base = static_cast<char*>(ws);
     if (use_static) {
         if (w.total > SR_STATIC_SCRATCH_BYTES) return SR_ERR_UNSUPPORTED;
-        char* base = nullptr;
         if ((st = static_scratch(hs, base)) != SR_OK) return st;
-        sc = scratch_in_static(s, w, base);
-    } else {
-        if (ws_bytes < w.total) return SR_ERR_INVALID_ARG;
-        sc = scratch_in_workspace(s, w, ws);
+    } else if (ws_bytes < w.total) {
+        return SR_ERR_INVALID_ARG;
     }
+    const Scratch sc = scratch_at(s, w, base);
 
     DecodeArgs a{};
     a.q = q;

@@ -78,14 +78,16 @@ def oracle_inputs(layer):
     return as_numpy(layer.q), as_numpy(layer.k), as_numpy(layer.v)
 
 
-def ticket_region(ws, n_items: int) -> torch.Tensor:
+# A workspace starts with a ticket region of fixed size: one int32 ticket for
+# each of the envelope's 32768 items, then the routing kernel's ticket.
+MAX_ITEMS = 32768
+
+
+def ticket_region(ws, n_items: int = MAX_ITEMS + 1) -> torch.Tensor:
     return ws.buf[: 4 * n_items].view(torch.int32)
 
 
-def route_ticket(ws, n_items: int) -> int:
-    """The routing kernel's ticket in a workspace of exactly sr_workspace_bytes:
-    the last region holds the list, n_active and the ticket ([n_items + 2]
-    int32), then one flag byte per item, padded to 256 bytes."""
-    region = ((n_items + 2) * 4 + n_items + 255) // 256 * 256
-    off = ws.nbytes - region + 4 * (n_items + 1)
+def route_ticket(ws) -> int:
+    """The routing kernel's ticket, after the item tickets."""
+    off = 4 * MAX_ITEMS
     return int(ws.buf[off:off + 4].view(torch.int32).cpu()[0])

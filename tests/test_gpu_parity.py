@@ -404,6 +404,68 @@ def test_fused_route_decode_matches_two_calls_bitwise(wl, kernel):
     assert_outputs(out1.cpu().numpy(), ref, f"fused {wl.name}")
 
 
+def test_one_workspace_serves_calls_of_other_shapes():
+    # The tickets sit at fixed offsets, so partials that a call of one shape
+    # left in a workspace never land where a call of another shape keeps its
+    # tickets: each call through one shared workspace is bitwise the call
+    # through a fresh one, and the ticket region is zero after each.
+    cases = [
+        (Workload("ws-big", 2, 64, 8, 128, 40000, "bf16", seed=75, sink_plan=("count", 3)),
+         launch(splits=300)),
+        (Workload("ws-72-items", 9, 8, 8, 128, 3000, "bf16", seed=76,
+                  sink_plan=("bernoulli", 0.5)), launch()),
+        (Workload("ws-small", 1, 16, 4, 128, 3000, "bf16", seed=77, sink_plan=("count", 2)),
+         launch()),
+    ]
+    runs = []
+    for wl, lau in cases:
+        q, k, v = upload(make_layer(wl))
+        k0, v0 = sr.record_sink(k, v)
+        fresh = sr.Workspace(sr.make_shape(q, k, v), lau, q.device)
+        ref, _ = sr.route_decode(q, k, v, k0, v0, wl.tau, launch=lau, ws=fresh)
+        runs.append((wl, lau, (q, k, v, k0, v0), ref))
+    shared = max((sr.Workspace(sr.make_shape(*t[:3]), lau, t[0].device)
+                  for _, lau, t, _ in runs), key=lambda w: w.nbytes)
+    for wl, lau, t, ref in runs + runs[::-1]:
+        out, _ = sr.route_decode(*t, wl.tau, launch=lau, ws=shared)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), wl.name
+        assert int(ticket_region(shared).abs().sum()) == 0, wl.name
+
+
+def test_default_workspace_is_reused_per_stream():
+    # calls without a workspace reuse one per (device, stream): bitwise the
+    # explicit-workspace result, no new workspace on a repeat, a larger one
+    # for a longer layer, and a separate one on a side stream
+    wl = Workload("ws-default", 1, 16, 4, 128, 3000, "bf16", seed=71, sink_plan=("count", 2))
+    layer = make_layer(wl)
+    q, k, v = upload(layer)
+    k0, v0 = sr.record_sink(k, v)
+    ws = sr.Workspace(sr.make_shape(q, k, v), None, q.device)
+    ref, _ = sr.route_decode(q, k, v, k0, v0, wl.tau, ws=ws)
+    a, _ = sr.route_decode(q, k, v, k0, v0, wl.tau)
+    key = (q.device.index, sr._stream())
+    first = sr._default_ws[key]
+    b, _ = sr.route_decode(q, k, v, k0, v0, wl.tau)
+    torch.cuda.synchronize()
+    assert sr._default_ws[key] is first
+    assert torch.equal(a, ref) and torch.equal(b, ref)
+    big_wl = wl.with_(batch=2, num_q_heads=64, num_kv_heads=8, seq_len=40000, name="ws-default-big")
+    big = upload(make_layer(big_wl))
+    big_launch = launch(splits=300)
+    assert not first.fits(sr.make_shape(*big), big_launch)
+    bk0, bv0 = sr.record_sink(big[1], big[2])
+    sr.route_decode(*big, bk0, bv0, wl.tau, launch=big_launch)
+    assert sr._default_ws[key].fits(sr.make_shape(*big), big_launch)
+    assert sr._default_ws[key].nbytes > first.nbytes
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        c, _ = sr.route_decode(q, k, v, k0, v0, wl.tau)
+    torch.cuda.synchronize()
+    assert torch.equal(c, ref)
+    assert sr._default_ws[(q.device.index, side.cuda_stream)] is not sr._default_ws[key]
+
+
 def test_fused_edges_all_sinks_no_sinks_and_repeats():
     wl = Workload("f-edges", 2, 16, 4, 128, 4000, "bf16", seed=65, sink_plan=("count", 2))
     layer = make_layer(wl)
@@ -565,7 +627,7 @@ def test_routing_kernel_forms(wl):
         for name in ("scores", "mask", "work_list", "n_active"):
             assert torch.equal(getattr(rf, name), getattr(r, name)), (rep, name)
         assert torch.equal(out, sr.decode_attn(q, k, v, v0, r.work_list, r.n_active))
-        assert route_ticket(ws, n_items) == 0
+        assert route_ticket(ws) == 0
 
 
 # --- balanced work division ------------------------------------------------------
