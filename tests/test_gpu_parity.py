@@ -458,6 +458,7 @@ def test_default_workspace_is_reused_per_stream():
     sr.route_decode(*big, bk0, bv0, wl.tau, launch=big_launch)
     assert sr._default_ws[key].fits(sr.make_shape(*big), big_launch)
     assert sr._default_ws[key].nbytes > first.nbytes
+    assert any(w is first for w in sr._replaced_ws)  # kept for graphs that captured it
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
         c, _ = sr.route_decode(q, k, v, k0, v0, wl.tau)
@@ -1182,3 +1183,33 @@ def _random_rope_steps(n, seed):
 @pytest.mark.parametrize("i", range(N_RANDOM_STEPS))
 def test_randomized_rope_steps(i):
     _rope_step_check(_random_rope_steps(N_RANDOM_STEPS, FUZZ_SEED + 1)[i], planted=False)
+
+
+def test_host_arrays_are_refused_before_any_launch():
+    # Every array a call hands over is checked to be on the device (a host
+    # pointer would be read by the kernels as device memory): each refusal
+    # names the array, and nothing is launched.
+    wl = Workload("host-args", 1, 16, 4, 128, 600, "bf16", seed=81, sink_plan=("count", 1))
+    q, k, v = upload(make_layer(wl))
+    k0, v0 = sr.record_sink(k, v)
+    r = sr.route(q, k0, wl.tau)
+    cpu_routing = sr.Routing(r.scores.cpu(), r.mask, r.work_list, r.n_active)
+    with pytest.raises(ValueError, match="k0 is a host tensor"):
+        sr.route_decode(q, k, v, k0.cpu(), v0)
+    with pytest.raises(ValueError, match="v0 is a host tensor"):
+        sr.decode_attn(q, k, v, v0.cpu(), r.work_list, r.n_active)
+    with pytest.raises(ValueError, match="n_active is a host tensor"):
+        sr.decode_attn(q, k, v, v0, r.work_list, r.n_active.cpu())
+    with pytest.raises(ValueError, match="out is a host tensor"):
+        sr.dense_decode(q, k, v, out=torch.empty(q.shape))
+    with pytest.raises(ValueError, match="scores is a host tensor"):
+        sr.route(q, k0, wl.tau, out=cpu_routing)
+    with pytest.raises(ValueError, match="scores is a host tensor"):
+        sr.route_decode(q, k, v, k0, v0, routing=cpu_routing)
+    f = rope_inv_freq(128).cuda()
+    kn = torch.zeros_like(k0)
+    with pytest.raises(ValueError, match="q_out is a host tensor"):
+        sr.rope_route_decode(q, kn, kn, k, v, k0, v0, f, q_out=torch.empty(q.shape))
+    with pytest.raises(ValueError, match="inv_freq is a host tensor"):
+        sr.rope_append(q, kn, kn, k, v, 5, f.cpu())
+    torch.cuda.synchronize()
