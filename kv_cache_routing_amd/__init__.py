@@ -46,44 +46,31 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
-_several_gpus = None
+# Counting devices does not initialise the GPU.
+_SEVERAL_GPUS = torch.cuda.device_count() > 1
 
 
 def _on_device(t: torch.Tensor, name: str):
     """The library launches on the current device and its stream: every
     array must live there (a host pointer or another GPU's would be read by
     the kernels as this GPU's memory)."""
-    global _several_gpus
     dev = t.get_device()
     if dev < 0:
         raise ValueError(f"libsinkroute takes device tensors ({name} is a host tensor)")
-    if _several_gpus is None:
-        _several_gpus = torch.cuda.device_count() > 1
-    if _several_gpus and dev != torch.cuda.current_device():
+    if _SEVERAL_GPUS and dev != torch.cuda.current_device():
         raise ValueError(f"libsinkroute takes tensors on the current device: {name} is on "
                          f"cuda:{dev}, the current device is cuda:{torch.cuda.current_device()}")
 
 
-def _need_cuda(**ts):
-    """Device check of every array a call hands over (None: not given)."""
-    for name, t in ts.items():
-        if t is not None:
-            _on_device(t, name)
-
-
-def _routing_arrays(r) -> dict:
-    return {} if r is None else dict(scores=r.scores, mask=r.mask, work_list=r.work_list,
-                                     n_active=r.n_active)
-
-
 def _expect(t: torch.Tensor, name: str, shape: tuple, dtype: torch.dtype):
     """The kernels index these arrays densely from the cache shape: anything
-    else would read or write outside them.  (Kept cheap: it runs on every
-    call, and launch-bound steps pay for it.)"""
+    else would read or write outside them; and they must be on the device.
+    (Kept cheap: it runs on every call, and launch-bound steps pay for it.)"""
     if t.shape != shape or t.dtype != dtype or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}, "
                          f"got {t.dtype} {tuple(t.shape)}"
                          f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+    _on_device(t, name)
 
 
 def _expect_q(q: torch.Tensor, k: torch.Tensor):
@@ -172,8 +159,9 @@ def rope_append(q_new, k_new, v_new, k_cache, v_cache, pos: int, inv_freq,
     _expect(inv_freq, "inv_freq", (d // 2,), torch.float32)
     if q_out is not None:
         _expect(q_out, "q_out", q_new.shape, torch.float32)
-    _need_cuda(q_new=q_new, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache,
-               inv_freq=inv_freq, q_out=q_out)
+    _on_device(q_new, "q_new")
+    _on_device(k_cache, "k_cache")
+    _on_device(v_cache, "v_cache")
     shape = make_shape(q_new, k_cache, v_cache)
     if q_out is None:
         q_out = torch.empty_like(q_new)
@@ -184,7 +172,8 @@ def rope_append(q_new, k_new, v_new, k_cache, v_cache, pos: int, inv_freq,
 
 
 def record_sink(k: torch.Tensor, v: torch.Tensor, q_heads: int | None = None):
-    _need_cuda(k=k, v=v)
+    _on_device(k, "k")
+    _on_device(v, "v")
     shape = make_shape(None, k, v)
     B, Hkv, _, d = k.shape
     k0 = torch.empty((B, Hkv, d), dtype=torch.float32, device=k.device)
@@ -219,7 +208,8 @@ def route(q: torch.Tensor, k0: torch.Tensor, tau: float = 0.5, out: Routing | No
         raise ValueError("q and k0 are fp32")
     if out is not None:
         _expect_routing(out, B, Hq, Hkv)
-    _need_cuda(q=q, k0=k0, **_routing_arrays(out))
+    _on_device(q, "q")
+    _on_device(k0, "k0")
     q = q.contiguous()
     k0 = k0.contiguous()
     shape = N.SrShape(B, Hq, Hkv, d, 1, Hkv * d, d, d, N.SR_KV_F32, 0)
@@ -259,15 +249,16 @@ def _workspace_for(shape, launch, device):
     return ws
 
 
-def _prep(q, k, v, launch, ws, out, q_checked=False, **arrays):
-    """Checks common to the decode calls (arrays: the call's other device
-    arrays, after their shapes were checked), the shape, a workspace and the
+def _prep(q, k, v, launch, ws, out, q_checked=False):
+    """Checks common to the decode calls, the shape, a workspace and the
     output."""
     if not q_checked:
         _expect_q(q, k)
     if out is not None:
         _expect(out, "out", q.shape, torch.float32)
-    _need_cuda(q=q, k=k, v=v, out=out, **arrays)
+    _on_device(q, "q")
+    _on_device(k, "k")
+    _on_device(v, "v")
     shape = make_shape(q, k, v)
     if ws is None:
         ws = _workspace_for(shape, launch, q.device)
@@ -286,8 +277,7 @@ def decode_attn(q, k, v, v0, work_list, n_active, sm_scale: float = 0.0,
     _expect(v0, "v0", (B, Hkv, d), torch.float32)
     _expect(work_list, "work_list", (B * Hkv,), torch.int32)
     _expect(n_active, "n_active", (1,), torch.int32)
-    shape, ws, out = _prep(q, k, v, launch, ws, out, q_checked=True, v0=v0,
-                           work_list=work_list, n_active=n_active)
+    shape, ws, out = _prep(q, k, v, launch, ws, out, q_checked=True)
     N.check(N.lib.sr_decode_attn(ctypes.byref(shape), _lp(launch), _ptr(q), _ptr(k), _ptr(v),
                                  _ptr(v0), _ptr(work_list), _ptr(n_active),
                                  float(sm_scale), _ptr(ws.buf), ws.nbytes, _ptr(out),
@@ -306,8 +296,7 @@ def route_decode(q, k, v, k0, v0, tau: float = 0.5, sm_scale: float = 0.0,
     _expect(v0, "v0", (B, Hkv, d), torch.float32)
     if routing is not None:
         _expect_routing(routing, B, q.shape[1], Hkv)
-    shape, ws, out = _prep(q, k, v, launch, ws, out, q_checked=True, k0=k0, v0=v0,
-                           **_routing_arrays(routing))
+    shape, ws, out = _prep(q, k, v, launch, ws, out, q_checked=True)
     if routing is None:
         dev = q.device
         routing = Routing(torch.empty((B, q.shape[1]), dtype=torch.float32, device=dev),
@@ -341,9 +330,7 @@ def rope_route_decode(q_new, k_new, v_new, k, v, k0, v0, inv_freq, tau: float = 
         _expect(q_out, "q_out", q_new.shape, torch.float32)
     if routing is not None:
         _expect_routing(routing, B, q_new.shape[1], Hkv)
-    shape, ws, out = _prep(q_new, k, v, launch, ws, out, q_checked=True, k_new=k_new,
-                           v_new=v_new, k0=k0, v0=v0, inv_freq=inv_freq, q_out=q_out,
-                           **_routing_arrays(routing))
+    shape, ws, out = _prep(q_new, k, v, launch, ws, out, q_checked=True)
     dev = q_new.device
     if q_out is None:
         q_out = torch.empty_like(q_new)

@@ -1,6 +1,7 @@
 """Host-side argument checks of the Python binding (CPU tensors, no device
 work): every array the kernels index from the cache shape is checked for
-shape, dtype and contiguity before anything reaches the library."""
+shape, dtype and contiguity, and for living on the device, before anything
+reaches the library."""
 import pytest
 import torch
 
@@ -23,6 +24,15 @@ def routing(**bad):
     return sr.Routing(**parts)
 
 
+@pytest.fixture
+def shapes_only(monkeypatch):
+    """Each array's shape check is reached with host tensors in the earlier
+    arguments: the device check (which those would fail first) is switched
+    off.  Every call in these tests fails a shape check, so nothing reaches
+    the library."""
+    monkeypatch.setattr(sr, "_on_device", lambda t, name: None)
+
+
 def test_well_formed_cpu_arguments_reach_the_device_check():
     q, k, v, k0, v0 = layer()
     with pytest.raises(ValueError, match="device tensors"):
@@ -31,6 +41,15 @@ def test_well_formed_cpu_arguments_reach_the_device_check():
         sr.route_decode(q, k, v, k0, v0, routing=routing())
     with pytest.raises(ValueError, match="device tensors"):
         sr.route(q, k0, out=routing())
+    kn = torch.zeros((B, Hkv, d))
+    with pytest.raises(ValueError, match="device tensors"):
+        sr.rope_append(q, kn, kn, k, v, 0, torch.zeros(d // 2))
+    # the first host array named
+    with pytest.raises(ValueError, match="k0 is a host tensor"):
+        sr.route_decode(q, k, v, k0, v0)
+    with pytest.raises(ValueError, match="v0 is a host tensor"):
+        sr.decode_attn(q, k, v, v0, torch.zeros(B * Hkv, dtype=torch.int32),
+                       torch.zeros(1, dtype=torch.int32))
 
 
 @pytest.mark.parametrize("bad_q", [torch.zeros((B + 1, Hq, d)), torch.zeros((B, Hq, 64)),
@@ -44,7 +63,7 @@ def test_query_must_match_the_cache(bad_q):
         sr.route_decode(bad_q, k, v, k0, v0)
 
 
-def test_output_and_sink_rows_are_checked():
+def test_output_and_sink_rows_are_checked(shapes_only):
     q, k, v, k0, v0 = layer()
     wl = torch.zeros(B * Hkv, dtype=torch.int32)
     na = torch.zeros(1, dtype=torch.int32)
@@ -64,7 +83,7 @@ def test_output_and_sink_rows_are_checked():
                                        ("mask", torch.zeros((B, Hkv), dtype=torch.int32)),
                                        ("work_list", torch.zeros(B * Hkv + 1, dtype=torch.int32)),
                                        ("n_active", torch.zeros((), dtype=torch.int32))])
-def test_routing_outputs_are_checked(field, bad):
+def test_routing_outputs_are_checked(field, bad, shapes_only):
     q, k, v, k0, v0 = layer()
     with pytest.raises(ValueError, match=f"{field} "):
         sr.route(q, k0, out=routing(**{field: bad}))
@@ -80,7 +99,7 @@ def test_route_query_and_key_must_agree():
         sr.route(q[:1], k0)
 
 
-def test_rope_append_arguments_are_checked():
+def test_rope_append_arguments_are_checked(shapes_only):
     q, k, v, _, _ = layer()
     kn = torch.zeros((B, Hkv, d))
     f = torch.zeros(d // 2)
@@ -90,5 +109,3 @@ def test_rope_append_arguments_are_checked():
         sr.rope_append(q, torch.zeros((B, Hq, d)), kn, k, v, 0, f)
     with pytest.raises(ValueError, match="q_out "):
         sr.rope_append(q, kn, kn, k, v, 0, f, q_out=torch.zeros((B, Hq, d), dtype=torch.float16))
-    with pytest.raises(ValueError, match="device tensors"):
-        sr.rope_append(q, kn, kn, k, v, 0, f)
