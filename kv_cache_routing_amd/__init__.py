@@ -24,9 +24,8 @@ from ._native import (SR_KERNEL_AUTO, SR_KERNEL_MFMA, SR_KERNEL_VALU,  # noqa: F
 
 __all__ = ["record_sink", "route", "decode_attn", "route_decode", "dense_decode",
            "dense_decode_alpha0", "rope_append", "rope_route_decode", "Workspace",
-           "make_shape",
-           "make_launch", "splits_for", "split_cap", "grid_size", "plan_parts", "SinkRouteError", "Routing",
-           "SR_KERNEL_AUTO", "SR_KERNEL_VALU", "SR_KERNEL_MFMA"]
+           "make_shape", "make_launch", "splits_for", "split_cap", "grid_size", "plan_parts",
+           "SinkRouteError", "Routing", "SR_KERNEL_AUTO", "SR_KERNEL_VALU", "SR_KERNEL_MFMA"]
 
 
 # Every call below runs these on the host before its launch, so they are kept
@@ -34,10 +33,6 @@ __all__ = ["record_sink", "route", "decode_attn", "route_decode", "dense_decode"
 # stream getter (where it exists) skips building a Stream object, which alone
 # cost ~3 us a call; a small layer's eager step is bound by this host time.
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
-
-
-def _ptr(t: torch.Tensor | None):
-    return 0 if t is None else t.data_ptr()
 
 
 def _stream():
@@ -141,7 +136,7 @@ class Workspace:
         if self.nbytes == 0:
             raise SinkRouteError(N.SR_ERR_UNSUPPORTED, "sr_workspace_bytes")
         self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
-        N.check(N.lib.sr_workspace_init(_ptr(self.buf), self.nbytes, _stream()),
+        N.check(N.lib.sr_workspace_init(self.buf.data_ptr(), self.nbytes, _stream()),
                 "sr_workspace_init")
 
     def fits(self, shape, launch) -> bool:
@@ -165,9 +160,10 @@ def rope_append(q_new, k_new, v_new, k_cache, v_cache, pos: int, inv_freq,
     shape = make_shape(q_new, k_cache, v_cache)
     if q_out is None:
         q_out = torch.empty_like(q_new)
-    N.check(N.lib.sr_rope_append(ctypes.byref(shape), _ptr(q_new), _ptr(k_new), _ptr(v_new),
-                                 _ptr(inv_freq), int(pos), _ptr(q_out), _ptr(k_cache),
-                                 _ptr(v_cache), _stream()), "sr_rope_append")
+    N.check(N.lib.sr_rope_append(ctypes.byref(shape), q_new.data_ptr(), k_new.data_ptr(),
+                                 v_new.data_ptr(), inv_freq.data_ptr(), int(pos),
+                                 q_out.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                 _stream()), "sr_rope_append")
     return q_out
 
 
@@ -178,8 +174,8 @@ def record_sink(k: torch.Tensor, v: torch.Tensor, q_heads: int | None = None):
     B, Hkv, _, d = k.shape
     k0 = torch.empty((B, Hkv, d), dtype=torch.float32, device=k.device)
     v0 = torch.empty_like(k0)
-    N.check(N.lib.sr_record_sink(ctypes.byref(shape), _ptr(k), _ptr(v), _ptr(k0), _ptr(v0),
-                                 _stream()), "sr_record_sink")
+    N.check(N.lib.sr_record_sink(ctypes.byref(shape), k.data_ptr(), v.data_ptr(), k0.data_ptr(),
+                                 v0.data_ptr(), _stream()), "sr_record_sink")
     return k0, v0
 
 
@@ -219,9 +215,9 @@ def route(q: torch.Tensor, k0: torch.Tensor, tau: float = 0.5, out: Routing | No
                       torch.empty((B, Hkv), dtype=torch.uint8, device=dev),
                       torch.empty((B * Hkv,), dtype=torch.int32, device=dev),
                       torch.empty((1,), dtype=torch.int32, device=dev))
-    N.check(N.lib.sr_route(ctypes.byref(shape), _ptr(q), _ptr(k0), float(tau),
-                           _ptr(out.scores), _ptr(out.mask), _ptr(out.work_list),
-                           _ptr(out.n_active), _stream()), "sr_route")
+    N.check(N.lib.sr_route(ctypes.byref(shape), q.data_ptr(), k0.data_ptr(), float(tau),
+                           out.scores.data_ptr(), out.mask.data_ptr(), out.work_list.data_ptr(),
+                           out.n_active.data_ptr(), _stream()), "sr_route")
     return out
 
 
@@ -278,10 +274,10 @@ def decode_attn(q, k, v, v0, work_list, n_active, sm_scale: float = 0.0,
     _expect(work_list, "work_list", (B * Hkv,), torch.int32)
     _expect(n_active, "n_active", (1,), torch.int32)
     shape, ws, out = _prep(q, k, v, launch, ws, out, q_checked=True)
-    N.check(N.lib.sr_decode_attn(ctypes.byref(shape), _lp(launch), _ptr(q), _ptr(k), _ptr(v),
-                                 _ptr(v0), _ptr(work_list), _ptr(n_active),
-                                 float(sm_scale), _ptr(ws.buf), ws.nbytes, _ptr(out),
-                                 _stream()), "sr_decode_attn")
+    N.check(N.lib.sr_decode_attn(ctypes.byref(shape), _lp(launch), q.data_ptr(), k.data_ptr(),
+                                 v.data_ptr(), v0.data_ptr(), work_list.data_ptr(),
+                                 n_active.data_ptr(), float(sm_scale), ws.buf.data_ptr(),
+                                 ws.nbytes, out.data_ptr(), _stream()), "sr_decode_attn")
     return out
 
 
@@ -303,11 +299,12 @@ def route_decode(q, k, v, k0, v0, tau: float = 0.5, sm_scale: float = 0.0,
                           torch.empty((B, Hkv), dtype=torch.uint8, device=dev),
                           torch.empty((B * Hkv,), dtype=torch.int32, device=dev),
                           torch.empty((1,), dtype=torch.int32, device=dev))
-    N.check(N.lib.sr_route_decode(ctypes.byref(shape), _lp(launch), _ptr(q), _ptr(k), _ptr(v),
-                                  _ptr(k0), _ptr(v0), float(tau), float(sm_scale),
-                                  _ptr(routing.scores), _ptr(routing.mask),
-                                  _ptr(routing.work_list), _ptr(routing.n_active), _ptr(ws.buf),
-                                  ws.nbytes, _ptr(out), _stream()), "sr_route_decode")
+    N.check(N.lib.sr_route_decode(ctypes.byref(shape), _lp(launch), q.data_ptr(), k.data_ptr(),
+                                  v.data_ptr(), k0.data_ptr(), v0.data_ptr(), float(tau),
+                                  float(sm_scale), routing.scores.data_ptr(),
+                                  routing.mask.data_ptr(), routing.work_list.data_ptr(),
+                                  routing.n_active.data_ptr(), ws.buf.data_ptr(), ws.nbytes,
+                                  out.data_ptr(), _stream()), "sr_route_decode")
     return out, routing
 
 
@@ -318,9 +315,9 @@ def rope_route_decode(q_new, k_new, v_new, k, v, k0, v0, inv_freq, tau: float = 
     """One decode step in one call (one launch up to 64 query heads, two
     above; q_out carries the rotated queries between them): rotate the new
     token's query and key to position T - 1 and append its key and value
-    there, then route and attend over positions 0 .. T - 1.  k, v are cache views [B][Hkv][T][d] whose last
-    row is the new token's (their storage must hold it).  Returns (out,
-    routing outputs, rotated q)."""
+    there, then route and attend over positions 0 .. T - 1.  k, v are cache
+    views [B][Hkv][T][d] whose last row is the new token's (their storage
+    must hold it).  Returns (out, routing outputs, rotated q)."""
     _expect_q(q_new, k)
     B, Hkv, _, d = k.shape
     for t, name in ((k_new, "k_new"), (v_new, "v_new"), (k0, "k0"), (v0, "v0")):
@@ -340,11 +337,11 @@ def rope_route_decode(q_new, k_new, v_new, k, v, k0, v0, inv_freq, tau: float = 
                           torch.empty((B * Hkv,), dtype=torch.int32, device=dev),
                           torch.empty((1,), dtype=torch.int32, device=dev))
     N.check(N.lib.sr_rope_route_decode(
-        ctypes.byref(shape), _lp(launch), _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(inv_freq),
-        _ptr(q_out), _ptr(k), _ptr(v), _ptr(k0), _ptr(v0), float(tau),
-        float(sm_scale), _ptr(routing.scores), _ptr(routing.mask),
-        _ptr(routing.work_list), _ptr(routing.n_active), _ptr(ws.buf), ws.nbytes, _ptr(out),
-        _stream()), "sr_rope_route_decode")
+        ctypes.byref(shape), _lp(launch), q_new.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+        inv_freq.data_ptr(), q_out.data_ptr(), k.data_ptr(), v.data_ptr(), k0.data_ptr(),
+        v0.data_ptr(), float(tau), float(sm_scale), routing.scores.data_ptr(),
+        routing.mask.data_ptr(), routing.work_list.data_ptr(), routing.n_active.data_ptr(),
+        ws.buf.data_ptr(), ws.nbytes, out.data_ptr(), _stream()), "sr_rope_route_decode")
     return out, routing, q_out
 
 
@@ -353,9 +350,10 @@ def dense_decode_alpha0(q, k, v, sm_scale: float = 0.0, launch: N.SrLaunch | Non
     """Dense decode plus the attention weight of position 0 per head."""
     shape, ws, out = _prep(q, k, v, launch, ws, out)
     alpha0 = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
-    N.check(N.lib.sr_dense_decode_alpha0(ctypes.byref(shape), _lp(launch), _ptr(q), _ptr(k),
-                                         _ptr(v), float(sm_scale), _ptr(ws.buf),
-                                         ws.nbytes, _ptr(out), _ptr(alpha0), _stream()),
+    N.check(N.lib.sr_dense_decode_alpha0(ctypes.byref(shape), _lp(launch), q.data_ptr(),
+                                         k.data_ptr(), v.data_ptr(), float(sm_scale),
+                                         ws.buf.data_ptr(), ws.nbytes, out.data_ptr(),
+                                         alpha0.data_ptr(), _stream()),
             "sr_dense_decode_alpha0")
     return out, alpha0
 
@@ -363,7 +361,7 @@ def dense_decode_alpha0(q, k, v, sm_scale: float = 0.0, launch: N.SrLaunch | Non
 def dense_decode(q, k, v, sm_scale: float = 0.0, launch: N.SrLaunch | None = None,
                  ws: Workspace | None = None, out: torch.Tensor | None = None):
     shape, ws, out = _prep(q, k, v, launch, ws, out)
-    N.check(N.lib.sr_dense_decode(ctypes.byref(shape), _lp(launch), _ptr(q), _ptr(k), _ptr(v),
-                                  float(sm_scale), _ptr(ws.buf), ws.nbytes, _ptr(out),
-                                  _stream()), "sr_dense_decode")
+    N.check(N.lib.sr_dense_decode(ctypes.byref(shape), _lp(launch), q.data_ptr(), k.data_ptr(),
+                                  v.data_ptr(), float(sm_scale), ws.buf.data_ptr(), ws.nbytes,
+                                  out.data_ptr(), _stream()), "sr_dense_decode")
     return out
