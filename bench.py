@@ -768,12 +768,11 @@ def same_size_read(sr, torch, nbytes: int, R: int, args, stream):
     return best
 
 
-def graph_time(torch, fn, steps, loops, stream):
-    """us per step of `steps` steps captured in one HIP graph and replayed
-    (median of `loops` replays): the GPU's own time per step, without the
+def capture_graph(torch, fn, steps):
+    """`steps` steps of `fn` captured in one HIP graph (after one eager call),
+    replayed once: replaying it gives the GPU's own time per step, without the
     host's launch rate and argument checks."""
-    import statistics
-    fn(0)  # eager first
+    fn(0)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -781,16 +780,18 @@ def graph_time(torch, fn, steps, loops, stream):
             fn(i)
     g.replay()
     torch.cuda.synchronize()
-    times = []
-    for _ in range(loops):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        g.replay()
-        b.record(stream)
-        torch.cuda.synchronize()
-        times.append(a.elapsed_time(b) * 1e3 / steps)
-    del g
-    return statistics.median(times)
+    return g
+
+
+def time_graph(torch, g, steps, stream):
+    """ms per step of one replay of a graph of `steps` steps."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
 
 
 def measure(sr, torch, wl, lau, tau, args, caches, q, *, dense=True, decode=True, probe=True,
@@ -837,18 +838,25 @@ def measure(sr, torch, wl, lau, tau, args, caches, q, *, dense=True, decode=True
         forms["dense"] = dense_step
     warm = warm_up(list(forms.values()) + ([decode_only] if decode else []), args.warmup,
                    args.settle)
+    # the graph-replayed forms are timed inside the same loops as the eager
+    # ones, so that a drift of the GPU's speed during the run affects both
+    graphs = {"fused": capture_graph(torch, fused, args.steps)}
+    if dense:
+        graphs["dense"] = capture_graph(torch, dense_step, args.steps)
     runs = {name: [] for name in forms}
+    graph_runs = {name: [] for name in graphs}
     dec, dec_b2b = [], []
     for _ in range(args.loops):
         for name, fn in forms.items():
             runs[name].append(time_loop(fn, args.steps, stream) * 1e3)
+        for name, g in graphs.items():
+            graph_runs[name].append(time_graph(torch, g, args.steps, stream) * 1e3)
         if decode:
             dec.append(time_launches(decode_only, args.steps, stream) * 1e3)
             dec_b2b.append(time_loop(decode_only, args.steps, stream) * 1e3)
+    del graphs
     med = {name: statistics.median(v) for name, v in runs.items()}
-    graph = {"fused": graph_time(torch, fused, args.steps, args.loops, stream)}
-    if dense:
-        graph["dense"] = graph_time(torch, dense_step, args.steps, args.loops, stream)
+    graph = {name: statistics.median(v) for name, v in graph_runs.items()}
     step = min(med["fused"], med["two_calls"])
     alg = algorithmic_bytes(wl, n_active)
     rep = {"workload": wl.name,
