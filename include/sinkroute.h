@@ -138,6 +138,9 @@ sr_status sr_record_sink(const sr_shape* shape, const void* k_cache, const void*
  *   tau     cosine threshold; a group is a sink iff every one of its G heads
  *           has cos >= tau.  tau > 1 routes nothing (every group active).
  *   scores  out fp32 [B][Hq]: cos(q[b,h], k0[b,h/G]); 0 if either norm is 0.
+ *           A NaN or infinite element in q[b,h] or k0 makes the score NaN
+ *           (as do squared norms beyond the fp32 range), and a NaN fails the
+ *           test at every tau: that head keeps its group active.
  *   mask    out u8 [B][Hkv]: 1 = sink.
  *   work_list out i32 [B*Hkv]: active items ascending, then sinks ascending.
  *   n_active  out i32 [1]: number of active items (stays on the device).

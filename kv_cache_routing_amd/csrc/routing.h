@@ -73,7 +73,9 @@ __device__ inline void head_cosines16(const float* __restrict__ q, const float* 
         const float nq = group_allreduce_sum<16>(qq);
         const float nk = group_allreduce_sum<16>(kk);
         const float den = sqrtf(nq) * sqrtf(nk);
-        c[r] = den > 0.f ? dot / den : 0.f;
+        // a zero vector scores 0; a non-finite input leaves a NaN, which fails
+        // every threshold (the head dissents)
+        c[r] = den != 0.f ? dot / den : 0.f;
     }
 }
 
@@ -141,7 +143,7 @@ __device__ inline bool score_item16(const float* __restrict__ q, const float* __
             const float dot = group_allreduce_sum<16>(qk);
             const float nq = group_allreduce_sum<16>(qq);
             const float den = sqrtf(nq) * sk;
-            const float c = den > 0.f ? dot / den : 0.f;
+            const float c = den != 0.f ? dot / den : 0.f;  // as head_cosines16
             sink = sink && c >= tau;
             if (hl == r) mine = c;
         }

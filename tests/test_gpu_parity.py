@@ -1213,3 +1213,55 @@ def test_host_arrays_are_refused_before_any_launch():
     with pytest.raises(ValueError, match="inv_freq is a host tensor"):
         sr.rope_append(q, kn, kn, k, v, 5, f.cpu())
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("B", [2, 5], ids=["one-launch", "two-launch"])
+def test_degenerate_heads_and_keys_route_as_the_oracle(B):
+    # A NaN or infinite query element leaves that head's cosine undefined: the
+    # score is NaN and the head dissents at every tau, so its group is active
+    # even at tau = -2.  A zero position-0 key scores its group's heads 0: a
+    # sink at tau <= 0 only.  Checked in sr_route and in both forms of
+    # sr_route_decode (one launch up to 64 query heads, two above) against the
+    # oracle: scores (NaN where the oracle's are), mask, list and count exactly;
+    # sink rows exactly v0; every active row of a finite query within the
+    # tolerance (attention of a non-finite query is undefined: not compared).
+    wl = Workload(f"degenerate-b{B}", B, 16, 4, 128, 700, "bf16", seed=90 + B,
+                  sink_plan=("count", 2))
+    layer = make_layer(wl)
+    G = wl.group_size
+    q_np, k_np, v_np = oracle_inputs(layer)
+    k0_ref, _ = oracle.record_sink(k_np, v_np)
+    _, mask0, _, _ = oracle.route(q_np, k0_ref, wl.tau)
+    sinks = [tuple(int(x) for x in s) for s in zip(*np.nonzero(mask0))]
+    (b1, g1), (b2, g2), (b3, g3) = sinks[0], sinks[1], sinks[-1]
+    q = layer.q.clone()
+    k = layer.k.clone()
+    q[b1, g1 * G + 1, 5] = float("nan")
+    q[b2, g2 * G + 2, 9] = float("inf")
+    k[b3, g3, 0, :] = 0
+    q_np, k_np = as_numpy(q), as_numpy(k)
+    k0_ref, v0_ref = oracle.record_sink(k_np, v_np)
+    qd, kd, vd = q.cuda(), k.cuda(), layer.v.cuda()
+    k0, v0 = sr.record_sink(kd, vd)
+    for tau in (0.5, 0.0, -2.0):
+        scores, mask, wl_ref, n_act = oracle.route(q_np, k0_ref, tau)
+        assert mask[b1, g1] == 0 and mask[b2, g2] == 0
+        assert mask[b3, g3] == (1 if tau <= 0 else 0)
+        r = sr.route(qd, k0, tau)
+        out, rf = sr.route_decode(qd, kd, vd, k0, v0, tau)
+        torch.cuda.synchronize()
+        for got in (r, rf):
+            s = got.scores.cpu().numpy()
+            assert np.array_equal(np.isnan(s), np.isnan(scores)), tau
+            fin = ~np.isnan(scores)
+            assert np.abs(s[fin] - scores[fin]).max() <= 2e-5, tau
+            assert np.array_equal(got.mask.cpu().numpy(), mask), tau
+            assert np.array_equal(got.work_list.cpu().numpy(), wl_ref), tau
+            assert int(got.n_active.cpu()[0]) == n_act, tau
+        with np.errstate(invalid="ignore"):  # the non-finite heads' rows
+            ref = oracle.routed_decode(q_np, k_np, v_np, v0_ref, mask)
+        o = out.cpu().numpy()
+        sink_rows_exact(o, v0_ref, mask, G)
+        rows = np.isfinite(q_np).all(axis=-1)
+        assert rows.sum() == B * 16 - 2
+        assert_outputs(o[rows], ref[rows], f"{wl.name} tau={tau}")

@@ -153,6 +153,31 @@ def test_p7_zero_query_is_uniform_average_and_active():
     assert mask.sum() == 0 and n_active == 2
 
 
+def test_p7_degenerate_scores_reading():
+    # The cosine of a zero vector is read as 0 and an undefined one (a NaN or
+    # infinite element) stays NaN, which fails ">= tau" at every tau: such a
+    # head keeps its group active.  A zero k0 makes its whole group score 0,
+    # a sink exactly when tau <= 0.
+    rng = np.random.default_rng(71)
+    q = rng.standard_normal((1, 8, 16))
+    k0 = rng.standard_normal((1, 4, 16))
+    k0[0, 1] = 0.0                      # group 1: zero position-0 key
+    q[0, 4, 3] = np.nan                 # group 2, head 0: a NaN element
+    q[0, 7, 0] = np.inf                 # group 3, head 1: an infinite element
+    scores = oracle.route_scores(q, k0)
+    assert np.array_equal(scores[0, 2:4], [0.0, 0.0])
+    assert np.isnan(scores[0, 4]) and np.isnan(scores[0, 7])
+    finite = [0, 1, 5, 6]
+    np.testing.assert_allclose(scores[0, finite],
+                               [float(orc.cosine(q[0, h], k0[0, h // 2])) for h in finite],
+                               rtol=0, atol=0)
+    for tau, want in ((0.5, [0, 0, 0, 0]), (0.0, [0, 1, 0, 0]), (-2.0, [1, 1, 0, 0])):
+        _, mask, wl, n_active = oracle.route(q, k0, tau)
+        assert mask[0].tolist() == want, tau
+        assert n_active == 4 - sum(want)
+        assert set(wl[:n_active].tolist()) >= {2, 3}   # the NaN groups stay active
+
+
 # --- p8: split-K invariance ---------------------------------------------------
 @pytest.mark.parametrize("S", [1, 2, 3, 7, 64, 100, 105])
 def test_p8_split_count_invariance(S):
