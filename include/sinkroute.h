@@ -195,7 +195,7 @@ sr_status sr_workspace_init(void* ws, size_t ws_bytes, void* stream);
  *     out[b,h,:] = sum_t softmax_t(sm_scale * <q[b,h], K[b,g,t]>) V[b,g,t,:]
  *   over t = 0..T-1, fp32 accumulation, split over the context and merged in
  *   ascending split order (bitwise reproducible for a given launch policy).
- *   sm_scale <= 0 means 1/sqrt(d).
+ *   sm_scale <= 0 means 1/sqrt(d); a NaN or infinite one is SR_ERR_INVALID_ARG.
  *   For bf16 caches the MFMA kernel splits each scaled query (and, for
  *   groups of more than 4 heads, each probability) into a sum of two bf16
  *   terms; products with the stored bf16 keys and values are exact and the

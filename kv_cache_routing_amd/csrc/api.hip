@@ -239,6 +239,7 @@ sr_status run_decode(const sr_shape* shape, const sr_launch* launch, const float
     // every workgroup reads q (all of it when it routes) while others write out
     const size_t q_bytes = static_cast<size_t>(s.batch) * s.num_q_heads * s.head_dim * sizeof(float);
     if (overlaps(out, q, q_bytes)) return SR_ERR_INVALID_ARG;
+    if (!isfinite(sm_scale)) return SR_ERR_INVALID_ARG;
     if (routed && !v0) return SR_ERR_INVALID_ARG;
     if (routed && !fused && (!work_list || !n_active)) return SR_ERR_INVALID_ARG;
     if (fused && (!fused->k0 || !aligned16(fused->k0) || isnan(fused->tau)))

@@ -48,10 +48,10 @@ def p(x=FAKE):
 
 
 def decode(s, launch=None, ws_bytes=1 << 30, q=FAKE, k=FAKE, v=FAKE, out=OUT, ws=FAKE,
-           v0=FAKE, wl=FAKE, na=FAKE):
+           v0=FAKE, wl=FAKE, na=FAKE, sm_scale=0.0):
     lp = None if launch is None else ctypes.byref(launch)
-    return N.lib.sr_decode_attn(ctypes.byref(s), lp, p(q), p(k), p(v), p(v0), p(wl), p(na), 0.0,
-                                p(ws), ws_bytes, p(out), None)
+    return N.lib.sr_decode_attn(ctypes.byref(s), lp, p(q), p(k), p(v), p(v0), p(wl), p(na),
+                                sm_scale, p(ws), ws_bytes, p(out), None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -78,6 +78,15 @@ def test_stride_and_alignment_checks():
     assert decode(shape(), k=FAKE + 8) == N.SR_ERR_INVALID_ARG
     assert decode(shape(), q=FAKE + 4) == N.SR_ERR_INVALID_ARG
     assert decode(shape(), out=FAKE + 4096) == N.SR_ERR_INVALID_ARG  # out overlaps q
+
+
+@pytest.mark.parametrize("scale", [float("nan"), float("inf"), float("-inf")])
+def test_non_finite_softmax_scale(scale):
+    # NaN and infinities are refused (a NaN is not "<= 0", which selects 1/sqrt(d))
+    assert decode(shape(), sm_scale=scale) == N.SR_ERR_INVALID_ARG
+    s = shape()
+    assert N.lib.sr_dense_decode(ctypes.byref(s), None, p(), p(), p(), scale, p(), 1 << 30,
+                                 p(OUT), None) == N.SR_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("which", ["q", "k", "v", "out", "ws", "v0", "wl", "na"])
