@@ -1265,3 +1265,39 @@ def test_degenerate_heads_and_keys_route_as_the_oracle(B):
         rows = np.isfinite(q_np).all(axis=-1)
         assert rows.sum() == B * 16 - 2
         assert_outputs(o[rows], ref[rows], f"{wl.name} tau={tau}")
+
+
+# --- the longest contexts: cache offsets past 32 bits -----------------------------
+def test_context_with_offsets_past_32_bits():
+    # 36M positions of d = 64 (bf16, 9.2 GB per cache): the last rows lie 2.3e9
+    # elements (4.6e9 bytes) from the cache base, past any 32-bit element or
+    # byte index, and each item's cache spans hundreds of lanes.  One group is
+    # planted as a sink and one is active (G = 2): routing, k0/v0 and the sink
+    # rows exact, the active group against the oracle, one call bitwise equal
+    # to two calls.
+    from workloads import make_caches_device
+    wl = Workload("ctx-36m", 1, 4, 2, 64, 36_000_000, "bf16", seed=97, sink_plan=("count", 1))
+    dev = torch.device("cuda")
+    k, v = make_caches_device(wl, dev)
+    q_cpu, planted = make_queries(wl)
+    q = q_cpu.to(dev)
+    lau = launch("auto")
+    k0, v0, r, out = run_routed(q, k, v, wl.tau, lau)
+    out1, rf = sr.route_decode(q, k, v, k0, v0, wl.tau, launch=lau)
+    torch.cuda.synchronize()
+    k0_ref = as_numpy(k[:, :, 0].cpu()).astype(np.float64)
+    v0_ref = as_numpy(v[:, :, 0].cpu()).astype(np.float64)
+    assert np.array_equal(k0.cpu().numpy(), k0_ref) and np.array_equal(v0.cpu().numpy(), v0_ref)
+    q_np = as_numpy(q_cpu)
+    mask, n_active = assert_route(r, q_np, k0_ref, wl.tau)
+    assert n_active == 1 and mask.tolist() == planted.to(torch.uint8).tolist()
+    for name in ("scores", "mask", "work_list", "n_active"):
+        assert torch.equal(getattr(rf, name), getattr(r, name)), name
+    assert torch.equal(out1, out)
+    got = out.cpu().numpy()
+    sink_rows_exact(got, v0_ref, mask, 2)
+    g = int(r.work_list.cpu()[0])
+    ref = oracle.attend_group(q_np[0, 2 * g:2 * g + 2], as_numpy(k[0, g].cpu()),
+                              as_numpy(v[0, g].cpu()), 1.0 / math.sqrt(64))
+    log(f"{wl.name}: active group {g}, grid {sr.grid_size(sr.make_shape(q, k, v), None)}")
+    assert_outputs(got[0, 2 * g:2 * g + 2], ref, f"{wl.name} active group")
