@@ -1268,20 +1268,26 @@ def test_degenerate_heads_and_keys_route_as_the_oracle(B):
 
 
 # --- the longest contexts: cache offsets past 32 bits -----------------------------
-def test_context_with_offsets_past_32_bits():
-    # 36M positions of d = 64 (bf16, 9.2 GB per cache): the last rows lie 2.3e9
-    # elements (4.6e9 bytes) from the cache base, past any 32-bit element or
-    # byte index, and each item's cache spans hundreds of lanes.  One group is
-    # planted as a sink and one is active (G = 2): routing, k0/v0 and the sink
-    # rows exact, the active group against the oracle, one call bitwise equal
-    # to two calls.
+@pytest.mark.parametrize("dtype,d,T,kernel", [("bf16", 64, 36_000_000, "auto"),
+                                               ("bf16", 64, 36_000_000, "valu"),
+                                               ("f32", 128, 17_000_000, "auto")],
+                         ids=["bf16-d64-36m", "bf16-d64-36m-valu", "f32-d128-17m"])
+def test_context_with_offsets_past_32_bits(dtype, d, T, kernel):
+    # The last rows lie 2.2e9-2.3e9 elements (4.6e9-8.7e9 bytes) from the cache
+    # base, past any 32-bit element or byte index, and each item's cache spans
+    # hundreds of lanes (9.2 GB of bf16, or 17.4 GB of fp32, per cache).  One
+    # group is planted as a sink and one is active (G = 2): routing, k0/v0 and
+    # the sink rows exact, the active group against the oracle, one call
+    # bitwise equal to two calls.
     from workloads import make_caches_device
-    wl = Workload("ctx-36m", 1, 4, 2, 64, 36_000_000, "bf16", seed=97, sink_plan=("count", 1))
+    wl = Workload(f"ctx-{dtype}-{T // 1_000_000}m", 1, 4, 2, d, T, dtype, seed=97,
+                  sink_plan=("count", 1))
+    assert (T - 1) * d > 2 ** 31
     dev = torch.device("cuda")
     k, v = make_caches_device(wl, dev)
     q_cpu, planted = make_queries(wl)
     q = q_cpu.to(dev)
-    lau = launch("auto")
+    lau = launch(kernel)
     k0, v0, r, out = run_routed(q, k, v, wl.tau, lau)
     out1, rf = sr.route_decode(q, k, v, k0, v0, wl.tau, launch=lau)
     torch.cuda.synchronize()
@@ -1298,6 +1304,6 @@ def test_context_with_offsets_past_32_bits():
     sink_rows_exact(got, v0_ref, mask, 2)
     g = int(r.work_list.cpu()[0])
     ref = oracle.attend_group(q_np[0, 2 * g:2 * g + 2], as_numpy(k[0, g].cpu()),
-                              as_numpy(v[0, g].cpu()), 1.0 / math.sqrt(64))
+                              as_numpy(v[0, g].cpu()), 1.0 / math.sqrt(d))
     log(f"{wl.name}: active group {g}, grid {sr.grid_size(sr.make_shape(q, k, v), None)}")
     assert_outputs(got[0, 2 * g:2 * g + 2], ref, f"{wl.name} active group")
