@@ -1307,3 +1307,52 @@ def test_context_with_offsets_past_32_bits(dtype, d, T, kernel):
                               as_numpy(v[0, g].cpu()), 1.0 / math.sqrt(d))
     log(f"{wl.name}: active group {g}, grid {sr.grid_size(sr.make_shape(q, k, v), None)}")
     assert_outputs(got[0, 2 * g:2 * g + 2], ref, f"{wl.name} active group")
+
+
+def test_rope_step_at_a_position_past_32_bit_offsets():
+    # One whole decode step (sr_rope_route_decode) whose new token lands at
+    # position 35,999,999 of a 36M-position bf16 layer (d = 64): the rotary
+    # angles reach 3.6e7 radians and the appended rows sit 2.3e9 elements past
+    # the cache base.  Against the oracle's own rotation and append: rotated
+    # query within 1 fp32 ulp, appended key within 1 bf16 ulp, value exact;
+    # then routing (one group planted as a sink through its rotated queries)
+    # and the active group's attention over the cache holding the oracle's rows.
+    from workloads import make_caches_device
+    wl = Workload("rope-36m", 1, 4, 2, 64, 36_000_000, "bf16", seed=98, sink_plan=("none",))
+    T, d, G, pos = wl.seq_len, wl.head_dim, 2, wl.seq_len - 1
+    dev = torch.device("cuda")
+    k, v = make_caches_device(wl, dev)
+    k0d, v0d = sr.record_sink(k, v)
+    k0_ref = as_numpy(k[:, :, 0].cpu()).astype(np.float64)
+    v0_ref = as_numpy(v[:, :, 0].cpu()).astype(np.float64)
+    f = rope_inv_freq(d)
+    gen = torch.Generator().manual_seed(4242)
+    kn, vn = (torch.randn((1, 2, d), generator=gen) for _ in range(2))
+    target = torch.randn((1, 4, d), generator=gen, dtype=torch.float64)
+    u = torch.from_numpy(k0_ref[0, 0]) / float(np.linalg.norm(k0_ref[0, 0]))
+    for h in range(G):  # group 0's rotated queries lie near its k0: a sink
+        target[0, h] = 0.9 * u * target[0, h].norm() + 0.05 * target[0, h]
+    qn = torch.from_numpy(oracle.rope(target.numpy(), -pos, f.numpy())).float()
+    out, r, q_rot = sr.rope_route_decode(qn.to(dev), kn.to(dev), vn.to(dev), k, v, k0d, v0d,
+                                         f.to(dev), wl.tau)
+    torch.cuda.synchronize()
+    q_ref = oracle.rope(qn.numpy(), pos, f.numpy())
+    assert (np.abs(q_rot.cpu().numpy() - q_ref) <= np.abs(q_ref) * 2 ** -23 + 1e-30).all()
+    k_row = oracle.round_bf16(oracle.rope(kn.numpy(), pos, f.numpy()))
+    v_row = oracle.round_bf16(vn.numpy())
+    k_dev = as_numpy(k[:, :, pos].cpu()).astype(np.float64)
+    assert (np.abs(k_dev - k_row) <= _bf16_ulp(k_row) + 1e-30).all(), "appended key row"
+    assert np.array_equal(as_numpy(v[:, :, pos].cpu()).astype(np.float64), v_row)
+    scores, mask, wl_ref, n_act = oracle.route(q_ref, k0_ref, wl.tau)
+    assert mask.tolist() == [[1, 0]] and n_act == 1
+    assert np.array_equal(r.mask.cpu().numpy(), mask)
+    assert np.array_equal(r.work_list.cpu().numpy(), wl_ref)
+    assert int(r.n_active.cpu()[0]) == 1
+    assert np.abs(r.scores.cpu().numpy() - scores).max() <= 2e-5
+    got = out.cpu().numpy()
+    sink_rows_exact(got, v0_ref, mask, G)
+    ks = as_numpy(k[0, 1].cpu())
+    vs = as_numpy(v[0, 1].cpu())
+    ks[pos], vs[pos] = k_row[0, 1], v_row[0, 1]  # the oracle's own appended rows
+    ref = oracle.attend_group(q_ref[0, 2:4], ks, vs, 1.0 / math.sqrt(d))
+    assert_outputs(got[0, 2:4], ref, "rope-36m active group")
