@@ -1268,21 +1268,24 @@ def test_degenerate_heads_and_keys_route_as_the_oracle(B):
 
 
 # --- the longest contexts: cache offsets past 32 bits -----------------------------
-@pytest.mark.parametrize("dtype,d,T,kernel", [("bf16", 64, 36_000_000, "auto"),
-                                               ("bf16", 64, 36_000_000, "valu"),
-                                               ("f32", 128, 17_000_000, "auto")],
-                         ids=["bf16-d64-36m", "bf16-d64-36m-valu", "f32-d128-17m"])
-def test_context_with_offsets_past_32_bits(dtype, d, T, kernel):
-    # The last rows lie 2.2e9-2.3e9 elements (4.6e9-8.7e9 bytes) from the cache
-    # base, past any 32-bit element or byte index, and each item's cache spans
-    # hundreds of lanes (9.2 GB of bf16, or 17.4 GB of fp32, per cache).  One
-    # group is planted as a sink and one is active (G = 2): routing, k0/v0 and
-    # the sink rows exact, the active group against the oracle, one call
-    # bitwise equal to two calls.
+@pytest.mark.parametrize("dtype,d,T,B,kernel", [("bf16", 64, 36_000_000, 1, "auto"),
+                                                 ("bf16", 64, 36_000_000, 1, "valu"),
+                                                 ("f32", 128, 17_000_000, 1, "auto"),
+                                                 ("bf16", 64, 18_000_000, 2, "auto")],
+                         ids=["bf16-d64-36m", "bf16-d64-36m-valu", "f32-d128-17m",
+                              "bf16-d64-18m-b2"])
+def test_context_with_offsets_past_32_bits(dtype, d, T, B, kernel):
+    # Cache rows 2.2e9-4.6e9 elements (4.6e9-9.2e9 bytes) from the cache base,
+    # past any 32-bit element or byte index: the last rows of a 36M-position
+    # (bf16) or 17M-position (fp32, d = 128) item, or the second sequence of a
+    # batch of two 18M-position items.  Each item's cache spans hundreds of
+    # lanes.  One group per sequence is planted as a sink and one is active
+    # (G = 2): routing, k0/v0 and the sink rows exact, every active group
+    # against the oracle, one call bitwise equal to two calls.
     from workloads import make_caches_device
-    wl = Workload(f"ctx-{dtype}-{T // 1_000_000}m", 1, 4, 2, d, T, dtype, seed=97,
+    wl = Workload(f"ctx-{dtype}-{T // 1_000_000}m-b{B}", B, 4, 2, d, T, dtype, seed=97,
                   sink_plan=("count", 1))
-    assert (T - 1) * d > 2 ** 31
+    assert max((T - 1) * d, (B - 1) * 2 * T * d) > 2 ** 31
     dev = torch.device("cuda")
     k, v = make_caches_device(wl, dev)
     q_cpu, planted = make_queries(wl)
@@ -1296,17 +1299,18 @@ def test_context_with_offsets_past_32_bits(dtype, d, T, kernel):
     assert np.array_equal(k0.cpu().numpy(), k0_ref) and np.array_equal(v0.cpu().numpy(), v0_ref)
     q_np = as_numpy(q_cpu)
     mask, n_active = assert_route(r, q_np, k0_ref, wl.tau)
-    assert n_active == 1 and mask.tolist() == planted.to(torch.uint8).tolist()
+    assert n_active == B and mask.tolist() == planted.to(torch.uint8).tolist()
     for name in ("scores", "mask", "work_list", "n_active"):
         assert torch.equal(getattr(rf, name), getattr(r, name)), name
     assert torch.equal(out1, out)
     got = out.cpu().numpy()
     sink_rows_exact(got, v0_ref, mask, 2)
-    g = int(r.work_list.cpu()[0])
-    ref = oracle.attend_group(q_np[0, 2 * g:2 * g + 2], as_numpy(k[0, g].cpu()),
-                              as_numpy(v[0, g].cpu()), 1.0 / math.sqrt(d))
-    log(f"{wl.name}: active group {g}, grid {sr.grid_size(sr.make_shape(q, k, v), None)}")
-    assert_outputs(got[0, 2 * g:2 * g + 2], ref, f"{wl.name} active group")
+    log(f"{wl.name}: grid {sr.grid_size(sr.make_shape(q, k, v), None)}")
+    for j in r.work_list.cpu().numpy()[:n_active]:
+        b, g = divmod(int(j), 2)
+        ref = oracle.attend_group(q_np[b, 2 * g:2 * g + 2], as_numpy(k[b, g].cpu()),
+                                  as_numpy(v[b, g].cpu()), 1.0 / math.sqrt(d))
+        assert_outputs(got[b, 2 * g:2 * g + 2], ref, f"{wl.name} active group {b}, {g}")
 
 
 def test_rope_step_at_a_position_past_32_bit_offsets():
