@@ -1360,3 +1360,27 @@ def test_rope_step_at_a_position_past_32_bit_offsets():
     ks[pos], vs[pos] = k_row[0, 1], v_row[0, 1]  # the oracle's own appended rows
     ref = oracle.attend_group(q_ref[0, 2:4], ks, vs, 1.0 / math.sqrt(d))
     assert_outputs(got[0, 2:4], ref, "rope-36m active group")
+
+
+def test_calls_on_two_streams_at_once_match_their_sequential_results():
+    # Two layers decoded on two streams at the same time, each through the
+    # default workspace of its own stream: no state is shared between the
+    # calls, so each result is bitwise the one its layer gives alone.
+    wls = [Workload("stream-a", 1, 32, 8, 128, 200_000, "bf16", seed=201, sink_plan=("count", 4)),
+           Workload("stream-b", 2, 16, 4, 128, 150_000, "bf16", seed=202, sink_plan=("count", 1))]
+    layers = [upload(make_layer(wl)) for wl in wls]
+    sinks = [sr.record_sink(k, v) for _, k, v in layers]
+    alone = []
+    for wl, (q, k, v), (k0, v0) in zip(wls, layers, sinks):
+        out, r = sr.route_decode(q, k, v, k0, v0, wl.tau)
+        alone.append((out.clone(), r.work_list.clone()))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    results = [None, None]
+    for _ in range(3):
+        for i, (wl, (q, k, v), (k0, v0)) in enumerate(zip(wls, layers, sinks)):
+            with torch.cuda.stream(streams[i]):
+                results[i] = sr.route_decode(q, k, v, k0, v0, wl.tau)
+        torch.cuda.synchronize()
+        for (out, r), (ref, ref_list) in zip(results, alone):
+            assert torch.equal(out, ref) and torch.equal(r.work_list, ref_list)
