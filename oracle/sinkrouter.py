@@ -22,7 +22,9 @@ Sources (the method is described on these pages):
 
 Readings where the pages are silent:
   * a group is a sink only when every one of its query heads scores >= tau;
-  * a zero-norm query or key scores 0 (so the group stays active);
+  * a zero-norm query or key scores 0 (so the group stays active unless
+    tau <= 0); a NaN or infinite element leaves the cosine undefined: the
+    score is NaN, which fails ">= tau" at every tau (the head dissents);
   * query head h reads KV head h // G (the Hugging Face repeat_kv layout);
   * the softmax scale is 1/sqrt(d) unless given;
   * split s covers positions [s*L, min((s+1)*L, T)) with L = ceil(T/S), an
@@ -182,6 +184,9 @@ def dense_decode(q, k_cache, v_cache, scale: float | None = None):
 # the position-0 value without touching the cache; active groups take step 4.
 # ---------------------------------------------------------------------------
 def routed_decode(q, k_cache, v_cache, v0, mask, scale: float | None = None):
+    """The routed step (README decode-time steps): a sink group (mask 1)
+    answers every one of its heads with v0 of the group; any other group
+    attends over its whole cache as Eq. (1) states (attend_group)."""
     q = np.asarray(q)
     B, Hq, d = q.shape
     Hkv = np.asarray(k_cache).shape[1]
@@ -240,6 +245,9 @@ def merge_partials(parts):
 
 
 def split_k_decode(q, k_cache, v_cache, num_splits: int, scale: float | None = None):
+    """Every group through the split algebra above: its partials over
+    num_splits contiguous ranges, merged in ascending order.  Equal to
+    dense_decode up to rounding for any split count (the invariance pins)."""
     q = np.asarray(q)
     B, Hq, d = q.shape
     Hkv = np.asarray(k_cache).shape[1]
