@@ -266,6 +266,27 @@ def test_static_scratch_route_decode_validation():
     assert call(s, launch=lau) == N.SR_ERR_UNSUPPORTED
 
 
+def test_static_scratch_holds_8b_and_70b_layers():
+    # The no-allocation form's fixed scratch takes every Llama-3.1-8B-shaped
+    # (32 query / 8 KV heads) or 70B-shaped (64 / 8) layer of up to 64 KV
+    # groups, at any context length and cache dtype, under the adaptive policy
+    # at 1 to 8 workgroups per CU (the host sizes grids for 256 CUs when it
+    # sees no GPU, MI355X's count), and under the default launch.
+    sizes = []
+    for Hq in (32, 64):
+        for B in (1, 2, 4, 8):
+            for T in (1, 4096, 131072, 524288, 1 << 24):
+                for dt in (N.SR_KV_BF16, N.SR_KV_F32):
+                    s = shape(B=B, Hq=Hq, Hkv=8, T=T, dt=dt)
+                    for lau in [None] + [N.SrLaunch(0, 0, c, 0) for c in range(1, 9)]:
+                        lp = None if lau is None else ctypes.byref(lau)
+                        need = N.lib.sr_workspace_bytes(ctypes.byref(s), lp)
+                        assert 0 < need <= N.SR_STATIC_SCRATCH_BYTES, (Hq, B, T, dt, lau)
+                        sizes.append(need)
+    # the largest of them is close enough to the limit that the check means something
+    assert max(sizes) > N.SR_STATIC_SCRATCH_BYTES // 2
+
+
 def test_rope_route_decode_validation():
     def call(s, kn=FAKE, vn=FAKE, f=FAKE, q_out=0, q=FAKE):
         return N.lib.sr_rope_route_decode(ctypes.byref(s), None, p(q), p(kn), p(vn), p(f),
