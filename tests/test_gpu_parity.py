@@ -239,6 +239,44 @@ def test_all_sinks_and_no_sinks():
     assert_outputs(out.cpu().numpy(), oracle.dense_decode(q_np, k_np, v_np), "tau 1.5")
 
 
+@functools.lru_cache(maxsize=None)
+def _sharp_layer(dtype):
+    return make_layer(Workload(f"sharp-{dtype}", 1, 32, 8, 128, 20000, dtype, seed=77,
+                               sink_plan=("count", 4)))
+
+
+# Softmax scales above the default 1/sqrt(d) (Eq. (1) with the scale as the
+# decode call's parameter; the oracle takes the same one): the distribution
+# turns peaky, the split partials' maxima then differ by hundreds, most merge
+# weights underflow to zero, and the rounding of the logits grows with their
+# size.  Routed (one call) and dense, against the oracle at the tight bound;
+# one split per item and the adaptive split must both hold it.
+@pytest.mark.parametrize("mult", [4, 16, 64])
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sharp_softmax_scales_against_oracle(dtype, kernel, mult):
+    layer = _sharp_layer(dtype)
+    sc = mult / math.sqrt(128)
+    log(f"sharp softmax {dtype} kernel={kernel} scale={mult}/sqrt(d)")
+    q_np, k_np, v_np = oracle_inputs(layer)
+    k0_ref, v0_ref = oracle.record_sink(k_np, v_np)
+    q, k, v = upload(layer)
+    k0, v0 = sr.record_sink(k, v)
+    dense_ref = oracle.dense_decode(q_np, k_np, v_np, scale=sc)
+    for splits in (0, 1):
+        lau = launch(kernel, splits=splits)
+        out, r = sr.route_decode(q, k, v, k0, v0, 0.5, sm_scale=sc, launch=lau)
+        dense = sr.dense_decode(q, k, v, sm_scale=sc, launch=lau)
+        torch.cuda.synchronize()
+        mask = assert_route(r, q_np, k0_ref, 0.5)[0]
+        got = out.cpu().numpy()
+        sink_rows_exact(got, v0_ref, mask, 4)
+        ref = oracle.routed_decode(q_np, k_np, v_np, v0_ref, mask, scale=sc)
+        act = np.repeat(mask == 0, 4, axis=1)
+        assert_outputs(got[act], ref[act], f"routed, splits={splits}")
+        assert_outputs(dense.cpu().numpy(), dense_ref, f"dense, splits={splits}")
+
+
 @pytest.mark.parametrize("wl,kernel", [
     (Workload("strided", 2, 16, 4, 128, 3000, "bf16", seed=51, sink_plan=("count", 2)), "mfma"),
     (Workload("strided", 2, 16, 4, 128, 3000, "bf16", seed=51, sink_plan=("count", 2)), "valu"),
